@@ -32,7 +32,7 @@ def build(force: bool = True) -> str:
     """Compile liboracle.so with gcc (fp64, -O2, OpenMP)."""
     if force or not os.path.exists(_LIB):
         tmp = _LIB + ".tmp"
-        subprocess.run(["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c99",
+        subprocess.run(["gcc", "-O3", "-fopenmp", "-fPIC", "-shared", "-std=c99",
                         "-Wall", "-Wno-unknown-pragmas", _SRC, "-o", tmp, "-lm"], check=True)
         os.replace(tmp, _LIB)
     return _LIB

@@ -40,7 +40,8 @@
  * counter layout, rounding) are listed in the project's design notes; the
  * functions below state the reading they implement.
  *
- * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ * Build: gcc -O3 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ * (no fast-math: every sum keeps its written order)
  */
 #include <math.h>
 #include <stdint.h>
@@ -257,27 +258,35 @@ static void linear_fwd(int T, int in, int out, const double *X, const double *W,
         }
 }
 
-/* Linear backward: dX = dY W (overwrite, if dX), dW = dY^T X, db = sum_t dY. */
+/* Linear backward: dX = dY W (overwrite, if dX), dW = dY^T X, db = sum_t dY.
+ * Each output element is accumulated over its reduction index in ascending
+ * order; the loops are nested so that the innermost one walks rows. */
 static void linear_bwd(int T, int in, int out, const double *dY, const double *X, const double *W,
                        double *dX, double *dW, double *db)
 {
     if (dX) {
         #pragma omp parallel for schedule(static)
-        for (int t = 0; t < T; ++t)
-            for (int i = 0; i < in; ++i) {
-                double s = 0.0;
-                for (int o = 0; o < out; ++o) s += dY[(size_t)t * out + o] * W[(size_t)o * in + i];
-                dX[(size_t)t * in + i] = s;
+        for (int t = 0; t < T; ++t) {
+            double *dx = dX + (size_t)t * in;
+            for (int i = 0; i < in; ++i) dx[i] = 0.0;
+            for (int o = 0; o < out; ++o) {
+                const double a = dY[(size_t)t * out + o];
+                const double *w = W + (size_t)o * in;
+                for (int i = 0; i < in; ++i) dx[i] += a * w[i];
             }
+        }
     }
     if (dW) {
         #pragma omp parallel for schedule(static)
-        for (int o = 0; o < out; ++o)
-            for (int i = 0; i < in; ++i) {
-                double s = 0.0;
-                for (int t = 0; t < T; ++t) s += dY[(size_t)t * out + o] * X[(size_t)t * in + i];
-                dW[(size_t)o * in + i] = s;
+        for (int o = 0; o < out; ++o) {
+            double *dw = dW + (size_t)o * in;
+            for (int i = 0; i < in; ++i) dw[i] = 0.0;
+            for (int t = 0; t < T; ++t) {
+                const double a = dY[(size_t)t * out + o];
+                const double *x = X + (size_t)t * in;
+                for (int i = 0; i < in; ++i) dw[i] += a * x[i];
             }
+        }
     }
     if (db) {
         #pragma omp parallel for schedule(static)
