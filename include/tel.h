@@ -1,0 +1,183 @@
+/*
+ * tel.h -- C ABI of the fused Transformer encoder layer for AMD MI355X
+ * (gfx950).  One layer, forward and backward, Pre-LN and Post-LN.
+ *
+ * What the layer computes (per sequence b of length S, hidden H, N heads of
+ * width d = H/N, FFN width F):
+ *   Pre-LN   x1 = x + Drop1(Attn(LN1(x)) W_o^T + b_o)
+ *            y  = x1 + Drop2(GELU(LN2(x1) W_1^T + b_1) W_2^T + b_2)
+ *   Post-LN  x1 = LN1(x + Drop1(Attn(x) W_o^T + b_o))
+ *            y  = LN2(x1 + Drop2(GELU(x1 W_1^T + b_1) W_2^T + b_2))
+ *   Attn(a): [Q|K|V] = a W_qkv^T + b_qkv (fused projection, rows of W_qkv
+ *            stacked Q,K,V; head h = columns h*d..h*d+d-1 of each),
+ *            P = softmax(Q K^T / sqrt(d)) over the valid keys j < len[b]
+ *            (padded keys weigh exactly 0), context = Drop0(P) V, heads
+ *            merged back to [token, H].
+ * Sources: the op order of an encoder layer and the fusion of linear+bias+
+ * activation are from "Forward computation-graph optimisation in the
+ * Transformer" (sections 2 and 4); the config fields, Pre-/Post-LN switch,
+ * LayerNorm epsilon, FFN default width and the three memory-saving switches
+ * are from the DeepSpeed Transformer Kernel guide ("Step 2: configuration
+ * parameters", "Step 3: memory-saving switches"); the fused QKV projection,
+ * head split, 1/sqrt(d) scale, exact GELU and inverted dropout are from the
+ * AI-infra blog (sections 2.1, 2.3 and 5.1); attention itself from the
+ * deployment article's pseudo-code ("1. matrix-operation restructuring").
+ *
+ * Dropout (inverted: kept value * 1/(1-p)) draws its bits from
+ * Philox4x32-10 (Salmon et al., SC'11): key = (seed mod 2^32, layer_id),
+ * counter = (floor(e/4) low, floor(e/4) high, site, step mod 2^32), word
+ * e mod 4; an element is dropped iff its word < floor(p * 2^32) with p the
+ * fp32 value in tel_config.  Sites: 0 attention probabilities, element
+ * e = ((b*N + h)*S + i)*S + j; 1 attention-branch output, 2 FFN-branch
+ * output, element e = t*H + c with token t = b*S + s; 3 the progressive
+ * layer-drop gate (element 0).  Masks are a pure function of
+ * (seed, layer_id, site, step, e): nothing is stored between forward and
+ * backward, so every switch setting regenerates identical masks.
+ *
+ * Data layout: row-major, token-major activations [B*S, H] with t = b*S+s;
+ * weights in nn.Linear layout W[out, in].  Params, activations and grads
+ * all have dtype cfg.dtype; accumulation, softmax and LayerNorm statistics
+ * are fp32.  Every pointer must be 16-byte aligned.
+ *
+ * Ownership: the caller owns every device buffer (x, y, params, grads,
+ * saved, scratch, key_lengths); the library owns only the opaque host handle
+ * and never allocates device memory.  No device pointer is retained across
+ * calls.  All work is enqueued on the caller's stream; no call blocks the
+ * host or synchronises the device.
+ *
+ * Errors: every argument is validated on the host before any HIP call, so
+ * invalid input returns TEL_ERR_INVALID_ARG / TEL_ERR_UNSUPPORTED without
+ * touching the GPU.  A failed kernel launch returns TEL_ERR_HIP.  The message
+ * for the last non-OK status of the calling thread is tel_last_error().
+ * Nothing aborts or throws across this interface.
+ */
+#ifndef TEL_H
+#define TEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* tel_stream_t; /* hipStream_t; NULL = default stream */
+
+typedef enum { TEL_F32 = 0, TEL_F16 = 1, TEL_BF16 = 2 } tel_dtype;
+
+typedef enum {
+    TEL_OK = 0,
+    TEL_ERR_INVALID_ARG = -1, /* bad shape, probability, pointer or alignment */
+    TEL_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. head width) */
+    TEL_ERR_STATE = -3,       /* backward without a forward that saved state */
+    TEL_ERR_HIP = -4          /* a HIP call or kernel launch failed */
+} tel_status;
+
+/* Layer configuration; shapes are fixed at creation (DeepSpeed Transformer
+ * Kernel guide, "Step 2": batch_size is the per-GPU micro-batch,
+ * max_seq_length the sequence length). */
+typedef struct {
+    int32_t batch, seq, hidden, heads;
+    int32_t ffn;                   /* <= 0 selects 4*hidden */
+    float attn_dropout;            /* site 0 probability, in [0,1) */
+    float hidden_dropout;          /* sites 1 and 2 probability, in [0,1) */
+    int32_t pre_ln;                /* 1 Pre-LN, 0 Post-LN */
+    uint64_t seed;                 /* dropout key word 0 (low 32 bits used) */
+    int32_t layer_id;              /* dropout key word 1 */
+    int32_t dtype;                 /* tel_dtype */
+    float ln_eps;                  /* LayerNorm epsilon (the guide's default 1e-12) */
+    int32_t attn_dropout_checkpoint; /* masks are never stored: accepted, no effect on memory */
+    int32_t normalize_invertible;  /* LN backward from the LN output; drops the LN inputs */
+    int32_t gelu_checkpoint;       /* keep the GELU input only; recompute GELU in backward */
+} tel_config;
+
+/* The twelve parameters, nn.Linear layout, dtype cfg.dtype, device memory:
+ * w_qkv [3H,H], b_qkv [3H], w_o [H,H], b_o [H], ln1_g/ln1_b [H],
+ * w_1 [F,H], b_1 [F], w_2 [H,F], b_2 [H], ln2_g/ln2_b [H]. */
+typedef struct {
+    const void *w_qkv, *b_qkv, *w_o, *b_o, *ln1_g, *ln1_b;
+    const void *w_1, *b_1, *w_2, *b_2, *ln2_g, *ln2_b;
+} tel_params;
+
+/* Gradients, same shapes and dtype; OVERWRITTEN (not accumulated). */
+typedef struct {
+    void *w_qkv, *b_qkv, *w_o, *b_o, *ln1_g, *ln1_b;
+    void *w_1, *b_1, *w_2, *b_2, *ln2_g, *ln2_b;
+} tel_grads;
+
+typedef struct tel_layer tel_layer;
+
+/* Validate cfg and create a handle (host memory only).  Supported: dims
+ * multiples of 16, head width d in {16,32,64,128}, H % N == 0, dtype f32,
+ * f16 or bf16.  *out is set to NULL on failure. */
+tel_status tel_layer_create(const tel_config* cfg, tel_layer** out);
+
+/* Bytes of the two caller-provided device workspaces:
+ *   saved   -- activations written by forward and read by the matching
+ *              backward; must stay unmodified in between;
+ *   scratch -- temporaries of one call; may be reused by any later call on
+ *              the same stream (shared by all layers of a stack). */
+tel_status tel_layer_workspace_bytes(const tel_layer* layer, size_t* saved_bytes, size_t* scratch_bytes);
+
+/* Forward.  x [B*S,H] in, y [B*S,H] out (may not alias x).  key_lengths:
+ * device int32 [B], valid length of each sequence in [1,S] (NULL: all S).
+ * training = 0 disables dropout.  step is the dropout counter word.
+ * saved may be NULL (inference): the activations then live in scratch,
+ * which must hold saved_bytes + scratch_bytes (rounded up to 256), and no
+ * backward may follow.  scratch is always required. */
+tel_status tel_layer_forward(tel_layer* layer, const tel_params* params, const void* x,
+                             const int32_t* key_lengths, int training, uint64_t step, void* y,
+                             void* saved, void* scratch, tel_stream_t stream);
+
+/* Backward of the most recent forward that had a saved buffer.  x,
+ * key_lengths, training and step must equal the forward's (x may be NULL
+ * for Pre-LN with normalize_invertible, where it is not read).  dy [B*S,H]
+ * in; dx [B*S,H] and all twelve grads out.  Returns TEL_ERR_STATE if no
+ * forward with saved state preceded it. */
+tel_status tel_layer_backward(tel_layer* layer, const tel_params* params, const void* x,
+                              const int32_t* key_lengths, int training, uint64_t step, const void* dy,
+                              const void* saved, void* scratch, void* dx, const tel_grads* grads,
+                              tel_stream_t stream);
+
+/* Free the handle.  NULL is accepted. */
+tel_status tel_layer_destroy(tel_layer* layer);
+
+/* Thread-local message describing the last non-OK status ("" if none). */
+const char* tel_last_error(void);
+
+/* Test hook: write the keep bits (1 keep, 0 drop) of dropout site 0, 1 or 2
+ * for the whole layer at this step into out_dev (device uint8; B*N*S*S
+ * bytes for site 0, B*S*H bytes for sites 1 and 2), computed by the same
+ * device generator the kernels use. */
+tel_status tel_debug_dropout_mask(const tel_layer* layer, int site, uint64_t step, uint8_t* out_dev,
+                                  tel_stream_t stream);
+
+/* Kernel ids of one layer's launches, for tel_debug_kernel_events. */
+enum {
+    TEL_K_LN1_FWD = 0, TEL_K_QKV_FWD = 1, TEL_K_ATTN_FWD = 2, TEL_K_OUT_FWD = 3, TEL_K_LN2_FWD = 4,
+    TEL_K_FFN1_FWD = 5, TEL_K_FFN2_FWD = 6,
+    TEL_K_FFN2_DGRAD = 10, TEL_K_FFN2_WGRAD = 11, TEL_K_FFN1_DGRAD = 12, TEL_K_FFN1_WGRAD = 13,
+    TEL_K_LN2_BWD = 14, TEL_K_OUT_DGRAD = 15, TEL_K_OUT_WGRAD = 16, TEL_K_ATTN_BWD = 17,
+    TEL_K_QKV_DGRAD = 18, TEL_K_QKV_WGRAD = 19, TEL_K_LN1_BWD = 20
+};
+
+/* Benchmark hook: from now on, every launch of kernel kernel_id (a TEL_K_*
+ * id) by this layer is bracketed on its stream by hipEventRecord of
+ * start_events[i % count] and stop_events[i % count] (hipEvent_t handles the
+ * caller created), i counting the launches since this call.  The arrays are
+ * borrowed until the hook is disabled with kernel_id < 0.  Results are
+ * unchanged. */
+tel_status tel_debug_kernel_events(tel_layer* layer, int kernel_id, void** start_events, void** stop_events,
+                                   int count);
+
+/* Progressive layer dropping (PLD page, "core mechanism": theta(t) =
+ * (1 - theta_bar) exp(-gamma t) + theta_bar).  Host-only, pure functions.
+ * tel_pld_keep returns 1 iff layer layer_id runs at this step: the site-3
+ * Philox word for element 0 is < floor(theta * 2^32). */
+double tel_pld_theta(double t, double theta_bar, double gamma);
+int32_t tel_pld_keep(uint64_t seed, int32_t layer_id, uint64_t step, double theta);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TEL_H */

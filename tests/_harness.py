@@ -1,0 +1,142 @@
+"""Shared helpers of the parity tests: run one layer through the C ABI on the
+GPU and through the fp64 oracle on the CPU, from the same seeded buffers."""
+from __future__ import annotations
+
+import numpy as np
+
+import oracle
+from transformer_encoder_layer_amd import synthetic as syn
+
+NAMES = syn.PARAM_NAMES
+
+
+def rounded(a, dtype):
+    """fp64 array -> (storage tensor on CPU, the fp64 values it holds)."""
+    t = syn.to_storage(a, dtype)
+    return t, t.double().numpy()
+
+
+def prepare(w: syn.Workload, layer=0, random_affine=False, weight_scale=1.0):
+    """Seeded inputs for workload w, rounded to its storage dtype."""
+    p64 = syn.layer_params(w, layer, random_affine=random_affine)
+    if weight_scale != 1.0:
+        for k in ("w_qkv", "w_o", "w_1", "w_2"):
+            p64[k] = p64[k] * weight_scale
+    params_t, params_r = {}, {}
+    for n in NAMES:
+        params_t[n], params_r[n] = rounded(p64[n], w.dtype)
+    x_t, x_r = rounded(syn.layer_input(w), w.dtype)
+    dy_t, dy_r = rounded(syn.upstream_grad(w), w.dtype)
+    lengths = syn.seq_lengths(w)
+    return dict(params_t=params_t, params_r=params_r, x_t=x_t, x_r=x_r, dy_t=dy_t, dy_r=dy_r, lengths=lengths)
+
+
+def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=None, switches=None,
+              device="cuda", backward=True, use_lengths=True):
+    """Run forward (+ backward) through the C ABI.  dy_rows: optional boolean
+    mask over sequences; dy is zeroed for the others.  Returns fp64 numpy."""
+    import torch
+    from transformer_encoder_layer_amd import binding as B
+    from transformer_encoder_layer_amd.layer import LayerConfig
+
+    sw = dict(switches or {})
+    cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, float(np.float32(w.attn_p)),
+                      float(np.float32(w.hidden_p)), w.pre_ln, w.seed, layer_id, syn.torch_dtype(w.dtype),
+                      1e-12, bool(sw.get("attn_dropout_checkpoint", w.attn_dropout_checkpoint)),
+                      bool(sw.get("normalize_invertible", w.normalize_invertible)),
+                      bool(sw.get("gelu_checkpoint", w.gelu_checkpoint)))
+    h = B.tel_layer_create(cfg.to_c())
+    try:
+        saved_b, scratch_b = B.tel_layer_workspace_bytes(h)
+        dev = torch.device(device)
+        P = {n: data["params_t"][n].to(dev) for n in NAMES}
+        x = data["x_t"].to(dev)
+        dy = data["dy_t"].clone()
+        if dy_rows is not None:
+            m = np.repeat(np.asarray(dy_rows, dtype=bool), w.seq)
+            dy[torch.from_numpy(~m)] = 0
+        dy = dy.to(dev)
+        lens = torch.from_numpy(data["lengths"]).to(dev) if (use_lengths and w.lengths is not None) else None
+        y = torch.empty_like(x)
+        saved = torch.empty(max(saved_b, 1), dtype=torch.uint8, device=dev)
+        scratch = torch.empty(max(scratch_b, 1), dtype=torch.uint8, device=dev)
+        B.tel_layer_forward(h, B.make_params(P), x, lens, training, step, y, saved, scratch)
+        out = {"y": y}
+        if backward:
+            dx = torch.empty_like(x)
+            G = {n: torch.empty_like(P[n]) for n in NAMES}
+            B.tel_layer_backward(h, B.make_params(P), x, lens, training, step, dy, saved, scratch, dx,
+                                 B.make_grads(G))
+            out["dx"] = dx
+            out.update({"g_" + n: G[n] for n in NAMES})
+        torch.cuda.synchronize()
+        return {k: v.double().cpu().numpy() for k, v in out.items()}
+    finally:
+        B.tel_layer_destroy(h)
+
+
+def oracle_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, batches=None, dy_rows=None,
+                 invertible=False, backward=True):
+    """Oracle forward (+ backward) on the sequences in `batches` (global indices),
+    one sequence at a time so that RNG element indices are global.  Weight
+    gradients are summed over the listed sequences."""
+    S, H = w.seq, w.hidden
+    batches = list(range(w.batch)) if batches is None else list(batches)
+    res = {"y": {}, "dx": {}}
+    gsum = None
+    for b in batches:
+        cfg = oracle.LayerCfg(1, S, H, w.heads, w.ffn, pre_ln=w.pre_ln, training=training,
+                              attn_p=float(np.float32(w.attn_p)), hidden_p=float(np.float32(w.hidden_p)),
+                              seed=w.seed, step=step, layer_id=layer_id, batch_offset=b)
+        xb = data["x_r"][b * S:(b + 1) * S]
+        lb = data["lengths"][b:b + 1]
+        y, _ = oracle.layer_forward(cfg, data["params_r"], xb, lb)
+        res["y"][b] = y
+        if backward:
+            dyb = data["dy_r"][b * S:(b + 1) * S]
+            if dy_rows is not None and not dy_rows[b]:
+                dyb = np.zeros_like(dyb)
+            dx, g = oracle.layer_backward(cfg, data["params_r"], xb, lb, dyb, ln_invertible=invertible)
+            res["dx"][b] = dx
+            gsum = g if gsum is None else {n: gsum[n] + g[n] for n in NAMES}
+    res["grads"] = gsum
+    return res
+
+
+def max_abs(a, b):
+    return float(np.abs(np.asarray(a) - np.asarray(b)).max())
+
+
+def rel_norm(a, b):
+    b = np.asarray(b)
+    den = np.linalg.norm(b.ravel())
+    return float(np.linalg.norm((np.asarray(a) - b).ravel()) / max(den, 1e-30))
+
+
+def compare(w: syn.Workload, g, o, batches, tol=None, check_grads=True):
+    """Assert the tolerances: fp32 max-abs 1e-5 everywhere; fp16/bf16 max-abs
+    2e-2 on y and relative-norm 5e-2 on dx and each parameter gradient."""
+    S = w.seq
+    report = {}
+    lowp = w.dtype != "f32"
+    ytol = 2e-2 if lowp else 1e-5
+    for b in batches:
+        report[f"y[{b}]"] = max_abs(g["y"][b * S:(b + 1) * S], o["y"][b])
+        assert report[f"y[{b}]"] <= ytol, report
+    if not check_grads:
+        return report
+    gx = np.concatenate([g["dx"][b * S:(b + 1) * S] for b in batches])
+    ox = np.concatenate([o["dx"][b] for b in batches])
+    if lowp:
+        report["dx"] = rel_norm(gx, ox)
+        assert report["dx"] <= 5e-2, report
+        for n in NAMES:
+            report[n] = rel_norm(g["g_" + n], o["grads"][n])
+            assert report[n] <= 5e-2, report
+    else:
+        report["dx"] = max_abs(gx, ox)
+        assert report["dx"] <= 1e-5, report
+        for n in NAMES:
+            report[n] = max_abs(g["g_" + n], o["grads"][n])
+            assert report[n] <= 1e-5, report
+    return report

@@ -1,0 +1,152 @@
+"""CPU-only checks of the C ABI: the library loads, exports every entry point
+include/tel.h declares, validates its arguments before touching the GPU,
+and its host-side PLD gate agrees bit for bit with the oracle's."""
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+from transformer_encoder_layer_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "tel.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+char\s*\*|tel_status|double|int32_t)\s+(tel_\w+)\s*\(", txt,
+                                 flags=re.M)))
+
+
+def test_header_matches_binding():
+    assert header_functions() == sorted(B.EXPORTS)
+
+
+def test_library_exports_every_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for f in header_functions():
+        assert f in syms, f
+    L = B.lib()
+    for f in header_functions():
+        assert hasattr(L, f)
+
+
+def cfg(**kw):
+    base = dict(batch=2, seq=16, hidden=64, heads=4, ffn=256, attn_dropout=0.0, hidden_dropout=0.0, pre_ln=1,
+                seed=1234, layer_id=0, dtype=B.TEL_F32, ln_eps=1e-12, attn_dropout_checkpoint=0,
+                normalize_invertible=0, gelu_checkpoint=0)
+    base.update(kw)
+    return B.tel_config(*[base[f] for f, _ in B.tel_config._fields_])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(hidden=60), B.TEL_ERR_INVALID_ARG),        # not a multiple of 16 / heads
+    (dict(heads=3), B.TEL_ERR_INVALID_ARG),          # H % N != 0
+    (dict(hidden=64, heads=8), B.TEL_ERR_UNSUPPORTED),  # d = 8
+    (dict(hidden=1024, heads=4), B.TEL_ERR_UNSUPPORTED),  # d = 256
+    (dict(seq=20), B.TEL_ERR_INVALID_ARG),
+    (dict(batch=0), B.TEL_ERR_INVALID_ARG),
+    (dict(attn_dropout=1.0), B.TEL_ERR_INVALID_ARG),
+    (dict(hidden_dropout=-0.1), B.TEL_ERR_INVALID_ARG),
+    (dict(dtype=7), B.TEL_ERR_INVALID_ARG),
+    (dict(ln_eps=-1.0), B.TEL_ERR_INVALID_ARG),
+    (dict(ffn=24), B.TEL_ERR_INVALID_ARG),
+])
+def test_create_rejects(kw, status):
+    with pytest.raises(B.TelError) as e:
+        B.tel_layer_create(cfg(**kw))
+    assert e.value.status == status
+    assert B.tel_last_error()
+
+
+def test_create_null_args():
+    import ctypes
+    h = ctypes.c_void_p(123)
+    assert B.lib().tel_layer_create(None, ctypes.byref(h)) == B.TEL_ERR_INVALID_ARG
+    assert h.value is None
+    c = cfg()
+    assert B.lib().tel_layer_create(ctypes.byref(c), None) == B.TEL_ERR_INVALID_ARG
+
+
+def test_ffn_default_and_workspace():
+    h = B.tel_layer_create(cfg(ffn=0))
+    s0, c0 = B.tel_layer_workspace_bytes(h)
+    B.tel_layer_destroy(h)
+    h = B.tel_layer_create(cfg(ffn=256))
+    s1, c1 = B.tel_layer_workspace_bytes(h)
+    B.tel_layer_destroy(h)
+    assert (s0, c0) == (s1, c1)  # ffn <= 0 selects 4H = 256
+    B.tel_layer_destroy(None)
+
+
+@pytest.mark.parametrize("pre_ln", [1, 0])
+def test_memory_switches_shrink_saved(pre_ln):
+    sizes = {}
+    for name, kw in {"base": {}, "gelu": dict(gelu_checkpoint=1), "inv": dict(normalize_invertible=1),
+                     "attn": dict(attn_dropout_checkpoint=1)}.items():
+        h = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=4, seq=128, hidden=256, heads=4, ffn=1024,
+                                   pre_ln=pre_ln, **kw))
+        sizes[name] = B.tel_layer_workspace_bytes(h)[0]
+        B.tel_layer_destroy(h)
+    T, F, H = 512, 1024, 256
+    assert sizes["base"] - sizes["gelu"] >= T * F * 2          # GELU output [T,F] fp16 not kept
+    if pre_ln:
+        assert sizes["base"] - sizes["inv"] >= T * H * 4       # fp32 LN2 input not kept
+    else:
+        assert sizes["inv"] < sizes["base"]
+    assert sizes["attn"] == sizes["base"]                      # masks are never stored
+
+
+def test_forward_validation_before_gpu():
+    h = B.tel_layer_create(cfg())
+    P = B.tel_params(*([4096] * 12))
+    G = B.tel_grads(*([4096] * 12))
+    try:
+        with pytest.raises(B.TelError) as e:   # NULL x
+            B.tel_layer_forward(h, P, None, None, 1, 0, 4096, 4096, 4096, 0)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        with pytest.raises(B.TelError) as e:   # misaligned y
+            B.tel_layer_forward(h, P, 4096, None, 1, 0, 4100, 4096, 8192, 0)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        with pytest.raises(B.TelError) as e:   # y aliases x
+            B.tel_layer_forward(h, P, 4096, None, 1, 0, 4096, 8192, 8192, 0)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        with pytest.raises(B.TelError) as e:   # NULL parameter
+            B.tel_layer_forward(h, B.tel_params(*([4096] * 11 + [0])), 4096, None, 1, 0, 8192, 4096, 4096, 0)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        with pytest.raises(B.TelError) as e:   # backward with no forward
+            B.tel_layer_backward(h, P, 4096, None, 1, 0, 4096, 4096, 4096, 4096, G, 0)
+        assert e.value.status == B.TEL_ERR_STATE
+        with pytest.raises(B.TelError) as e:   # NULL gradient
+            B.tel_layer_backward(h, P, 4096, None, 1, 0, 4096, 4096, 4096, 4096,
+                                 B.tel_grads(*([0] + [4096] * 11)), 0)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        with pytest.raises(B.TelError) as e:   # bad mask site
+            B.tel_debug_dropout_mask(h, 3, 0, 4096, 0)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+    finally:
+        B.tel_layer_destroy(h)
+
+
+def test_pld_host_gate_matches_oracle():
+    for tb in (0.0, 0.1, 0.5, 0.9, 1.0):
+        for t in (0, 1, 100, 5000, 123456):
+            assert B.tel_pld_theta(t, tb, 0.001) == oracle.pld_theta(t, tb, 0.001)
+    theta = oracle.pld_theta(5000, 0.5, 0.001)
+    for seed in (7, 1234):
+        for layer in range(24):
+            for step in (0, 1, 4999, 5000, 2 ** 33 + 5):
+                for th in (theta, 0.0, 1.0, 0.25):
+                    assert B.tel_pld_keep(seed, layer, step, th) == oracle.pld_keep(seed, layer, step, th)
+
+
+def test_pld_memsave_stack_gates():
+    # the memory-saving stack at t = 5000: theta = 0.50337, seed 7, 24 layers
+    theta = B.tel_pld_theta(5000, 0.5, 0.001)
+    gates = [B.tel_pld_keep(7, l, 5000, theta) for l in range(24)]
+    assert gates == [oracle.pld_keep(7, l, 5000, theta) for l in range(24)]
+    assert 0 < sum(gates) < 24

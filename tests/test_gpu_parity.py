@@ -1,0 +1,175 @@
+"""GPU parity of the fused layer (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 max-abs 1e-5 on y, dx and every gradient; fp16/bf16
+max-abs 2e-2 on y and relative-norm 5e-2 on dx and each gradient; dropout
+masks bit-exact.  Small cases run every sequence through the oracle; the
+full-size workloads run the GPU at their real shape and compare sampled
+sequences (dy is zero on the others, so every weight gradient is exactly
+the sum over the sampled sequences, which the oracle computes)."""
+import numpy as np
+import pytest
+
+import oracle
+from _harness import NAMES, compare, gpu_layer, oracle_layer, prepare
+from transformer_encoder_layer_amd import synthetic as syn
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(w, batches=None, dy_rows=None, step=0, layer_id=0, switches=None, random_affine=True,
+         weight_scale=1.0, invertible=None):
+    data = prepare(w, layer=layer_id, random_affine=random_affine, weight_scale=weight_scale)
+    g = gpu_layer(w, data, step=step, layer_id=layer_id, dy_rows=dy_rows, switches=switches)
+    inv = w.normalize_invertible if invertible is None else invertible
+    o = oracle_layer(w, data, step=step, layer_id=layer_id, batches=batches, dy_rows=dy_rows, invertible=inv)
+    bs = list(range(w.batch)) if batches is None else batches
+    rep = compare(w, g, o, bs)
+    print(w.name, {k: f"{v:.3g}" for k, v in rep.items()})
+    return g, o
+
+
+# ------------------------------------------------------------------ tiny fp32
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_tiny_fp32(pre_ln):
+    w = syn.WORKLOADS["tiny"].with_(pre_ln=pre_ln)
+    _run(w, weight_scale=4.0)
+
+
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_tiny_fp32_dropout(pre_ln):
+    w = syn.WORKLOADS["tiny"].with_(pre_ln=pre_ln, attn_p=0.1, hidden_p=0.1)
+    _run(w, step=3, layer_id=2, weight_scale=4.0)
+
+
+# ------------------------------------------------------------------ MFMA paths, small shapes
+SMALL = dict(batch=4, seq=128, hidden=256, heads=4, ffn=1024)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_small_lowp(dtype, pre_ln):
+    w = syn.Workload("small", **SMALL, pre_ln=pre_ln, dtype=dtype, attn_p=0.1, hidden_p=0.1, seed=11,
+                     lengths=(1, 128))
+    _run(w, step=7, layer_id=1)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_small_lowp_ragged_seq(dtype):
+    # S = 192: attention has a partial 128-query block; lengths hit block edges
+    w = syn.Workload("ragged", 2, 192, 128, 2, 512, True, dtype, 0.1, 0.1, 5, lengths=(63, 65))
+    _run(w)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_small_lowp_d32_simt_attention(dtype):
+    # head width 32 takes the generic attention kernel
+    w = syn.Workload("d32", 2, 64, 128, 4, 512, False, dtype, 0.1, 0.1, 9, lengths=(5, 64))
+    _run(w)
+
+
+# ------------------------------------------------------------------ masks
+@pytest.mark.parametrize("site", [0, 1, 2])
+def test_dropout_masks_bitexact(site):
+    import torch
+    from transformer_encoder_layer_amd import binding as B
+    from transformer_encoder_layer_amd.layer import LayerConfig
+    cfg = LayerConfig(3, 64, 128, 2, 512, 0.1, 0.25, True, 99, 5, torch.float16)
+    h = B.tel_layer_create(cfg.to_c())
+    try:
+        n = 3 * 2 * 64 * 64 if site == 0 else 3 * 64 * 128
+        out = torch.empty(n, dtype=torch.uint8, device="cuda")
+        B.tel_debug_dropout_mask(h, site, 77, out)
+        got = out.cpu().numpy()
+    finally:
+        B.tel_layer_destroy(h)
+    p = float(np.float32(0.1 if site == 0 else 0.25))
+    want = oracle.dropout_mask(99, 5, site, 77, p, 0, n)
+    assert np.array_equal(got, want)
+
+
+# ------------------------------------------------------------------ memory switches
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_checkpoint_switches_bitwise(pre_ln):
+    w = syn.Workload("sw", **SMALL, pre_ln=pre_ln, dtype="f16", attn_p=0.1, hidden_p=0.1, seed=3,
+                     lengths=(30, 128))
+    data = prepare(w, random_affine=True)
+    base = gpu_layer(w, data, step=1)
+    for sw in (dict(gelu_checkpoint=True), dict(attn_dropout_checkpoint=True),
+               dict(gelu_checkpoint=True, attn_dropout_checkpoint=True)):
+        other = gpu_layer(w, data, step=1, switches=sw)
+        for k in base:
+            assert np.array_equal(base[k], other[k]), (sw, k)
+
+
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_invertible_layernorm(pre_ln):
+    w = syn.Workload("inv", **SMALL, pre_ln=pre_ln, dtype="f16", attn_p=0.1, hidden_p=0.1, seed=4,
+                     lengths=(30, 128), normalize_invertible=True)
+    _run(w, step=2)
+
+
+def test_run_to_run_deterministic():
+    w = syn.Workload("det", **SMALL, pre_ln=True, dtype="bf16", attn_p=0.1, hidden_p=0.1, seed=8)
+    data = prepare(w, random_affine=True)
+    a = gpu_layer(w, data, step=4)
+    b = gpu_layer(w, data, step=4)
+    for k in a:
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_inference_forward_no_saved():
+    import torch
+    from transformer_encoder_layer_amd import binding as B
+    from transformer_encoder_layer_amd.layer import LayerConfig
+    w = syn.Workload("inf", **SMALL, pre_ln=True, dtype="f16", attn_p=0.1, hidden_p=0.1, seed=6)
+    data = prepare(w, random_affine=True)
+    ref = gpu_layer(w, data, training=False, backward=False)
+    o = oracle_layer(w, data, training=False, backward=False)
+    compare(w, ref, o, list(range(w.batch)), check_grads=False)
+    cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, 0.1, 0.1, True, 6, 0, torch.float16)
+    h = B.tel_layer_create(cfg.to_c())
+    try:
+        sv, sc = B.tel_layer_workspace_bytes(h)
+        P = {n: data["params_t"][n].cuda() for n in NAMES}
+        x = data["x_t"].cuda()
+        y = torch.empty_like(x)
+        scratch = torch.empty((sc + 255) // 256 * 256 + sv, dtype=torch.uint8, device="cuda")
+        B.tel_layer_forward(h, B.make_params(P), x, None, 0, 0, y, None, scratch)
+        torch.cuda.synchronize()
+        assert np.array_equal(y.double().cpu().numpy(), ref["y"])
+        with pytest.raises(B.TelError):
+            B.tel_layer_backward(h, B.make_params(P), x, None, 0, 0, x, scratch, scratch, y,
+                                 B.make_grads(P))
+    finally:
+        B.tel_layer_destroy(h)
+
+
+# ------------------------------------------------------------------ full-size workloads, sampled
+def _sampled(name, batches, **over):
+    w = syn.WORKLOADS[name].with_(**over)
+    rows = np.zeros(w.batch, dtype=bool)
+    rows[batches] = True
+    return _run(w, batches=batches, dy_rows=rows, random_affine=False)
+
+
+def test_full_bert_large_layer():
+    _sampled("bert_large", [0, 63])
+
+
+def test_full_bert_large_layer23():
+    w = syn.WORKLOADS["bert_large"]
+    rows = np.zeros(w.batch, dtype=bool)
+    rows[[17]] = True
+    _run(w, batches=[17], dy_rows=rows, layer_id=23, step=5, random_affine=False)
+
+
+def test_full_bert_base_postln():
+    _sampled("bert_base_postln", [0, 31])
+
+
+def test_full_long_seq():
+    _sampled("long_seq", [7])
+
+
+def test_full_memsave_layer():
+    _sampled("memsave_stack", [0, 127])

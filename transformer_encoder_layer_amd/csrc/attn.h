@@ -1,0 +1,27 @@
+// attn.h -- tiled attention forward/backward (online softmax; the S x S
+// score matrix is never written to memory).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "tel_common.h"
+
+namespace tel {
+
+struct AttnArgs {
+    int dtype;          // tel_dtype
+    int B, S, NH, d;    // H = NH * d
+    const void* qkvh;   // [3][B][NH][S][d]
+    const int32_t* len; // [B] valid key counts, or nullptr
+    Drop drop;          // site 0; thr == 0: no dropout
+    // forward
+    void* ctx;          // [B*S][H] head-merged output
+    float* lse;         // [B][NH][S] log2-sum-exp2 of the scaled scores
+    // backward
+    const void* dout;   // [B][NH][S][d] gradient of ctx, head-split
+    float* dvec;        // [B][NH][S] rowsum(dO * O) (written by the dq kernel)
+    void* dqkv;         // [B*S][3H] token-major gradient of the fused projection
+};
+
+hipError_t attn_forward(const AttnArgs& a, hipStream_t st, bool force_simt = false);
+hipError_t attn_backward(const AttnArgs& a, hipStream_t st, bool force_simt = false);
+
+}  // namespace tel

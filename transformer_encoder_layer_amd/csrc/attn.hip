@@ -1,0 +1,613 @@
+// attn.hip -- scaled, key-masked softmax attention with dropout on the
+// probabilities, forward and backward, for gfx950.
+//
+// Definition (deployment article, attention pseudo-code; AI-infra blog
+// section 5.1 for the 1/sqrt(d) scale and inverted dropout):
+//   s_ij = q_i . k_j / sqrt(d) for keys j < len[b], -inf otherwise
+//   P_ij = softmax_j(s_ij);  O_i = sum_j P_ij * keep_ij / (1-p) * v_j
+// The softmax normaliser runs over all valid keys before dropout.
+//
+// MFMA path (d = 64, S % 64 == 0): one workgroup = 4 waves x 32 queries
+// of one (batch, head); keys stream through LDS in blocks of 64 with an
+// online (running max / running sum) softmax, so only the per-row
+// log-sum-exp is written -- never the S x S matrix.  Scores are produced
+// transposed (keys x queries) so that each lane owns one query and four
+// consecutive keys: the row max/sum needs one cross-lane exchange, and one
+// Philox call yields the dropout bits of those four keys.  The probability
+// tile feeds the P.V product straight from registers; V is read with the
+// transposing LDS load using the same key permutation.
+//
+// Backward: a query-parallel kernel computes D_i = rowsum(dO_i * O_i) and
+// dQ; a key-parallel kernel computes dK and dV (no atomics: every output
+// row is owned by one wave).  Both recompute P from Q, K and the saved
+// log-sum-exp and regenerate the dropout bits from the counter-based RNG.
+//
+// SIMT path: one thread per row, any S and d in {16, 32, 64, 128}.
+#include "attn.h"
+#include "mfma_common.h"
+
+namespace tel {
+
+static constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ bool keep1(const Rng& r, uint64_t e, uint32_t thr) {
+    return (keep4(r, e >> 2, thr) >> (e & 3)) & 1u;
+}
+
+// ------------------------------------------------------------------ MFMA fwd
+template <typename T>
+__global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
+    constexpr int D = 64, KB = 64, VLD = D + 16;
+    typedef typename MfmaOp<T>::v8 v8;
+    __shared__ __align__(16) T Ks[KB * D];
+    __shared__ __align__(16) T Vs[KB * VLD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int S = a.S, NH = a.NH, B = a.B;
+    const int q0 = blockIdx.x * 128 + wave * 32;
+    const bool active = q0 < S;
+    const int L = a.len ? a.len[b] : S;
+    const int nkb = (L + KB - 1) / KB;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const float c = kLog2e * 0.125f;  // log2(e) / sqrt(64)
+    const int ql = q0 + (lane & 31);
+
+    v8 qf[4];
+    if (active) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)ql * D + ks * 16 + (lane >> 5) * 8);
+    }
+    float m_run = -INFINITY, l_run = 0.0f;
+    f32x16 o[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ct][r] = 0.0f;
+    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + ql) * (uint64_t)S;
+
+    for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+            const uint4 kv = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row) * D + ch * 8);
+            const uint4 vv = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row) * D + ch * 8);
+            *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = kv;
+            *reinterpret_cast<uint4*>(Vs + row * VLD + ch * 8) = vv;
+        }
+        __syncthreads();
+        if (active) {
+            f32x16 s[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks, kt * 32, ks, lane), qf[ks], s[kt]);
+            }
+            // s[kt][r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
+            float mloc = -INFINITY;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = kb * KB + kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const float v = key < L ? s[kt][r] * c : -INFINITY;
+                    s[kt][r] = v;
+                    mloc = fmaxf(mloc, v);
+                }
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+            const float m_new = fmaxf(m_run, mloc);
+            const float alpha = exp2f(m_run - m_new);
+            m_run = m_new;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const float p = exp2f(s[kt][r] - m_new);
+                    s[kt][r] = p;
+                    lsum += p;
+                }
+            l_run = l_run * alpha + lsum;
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+            if (a.drop.thr) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
+                        const uint32_t kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
+                    }
+            }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 4; ++ks2) {
+                const int kt = ks2 >> 1, half = ks2 & 1;
+                v8 pf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[i] = from_f<T>(s[kt][(2 * half) * 4 + i]);
+                    pf[4 + i] = from_f<T>(s[kt][(2 * half + 1) * 4 + i]);
+                }
+                const int kb0 = kt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    o[ct] = MfmaOp<T>::mma(frag_tr<T>(Vs, VLD, ct * 32, kb0, kb0 + 8, lane), pf, o[ct]);
+            }
+        }
+        __syncthreads();
+    }
+    if (active) {
+        const float l = l_run + __shfl_xor(l_run, 32, 64);
+        const float inv = a.drop.scale / l;
+        T* out = (T*)a.ctx + (size_t)(b * S + ql) * (NH * D) + h * D;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
+                Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+            }
+        if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = m_run + log2f(l);
+    }
+}
+
+// ------------------------------------------------------------------ MFMA bwd: D and dQ
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
+    constexpr int D = 64, KB = 64;
+    typedef typename MfmaOp<T>::v8 v8;
+    __shared__ __align__(16) T Ks[KB * D];
+    __shared__ __align__(16) T Vs[KB * D];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
+    const int q0 = blockIdx.x * 128 + wave * 32;
+    const bool active = q0 < S;
+    const int L = a.len ? a.len[b] : S;
+    const int nkb = (L + KB - 1) / KB;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const T* dO = (const T*)a.dout + ((size_t)b * NH + h) * head;
+    const float c = kLog2e * 0.125f;
+    const int ql = q0 + (lane & 31);
+
+    v8 qf[4], df[4];
+    float Dq = 0.0f, lse2 = 0.0f;
+    if (active) {
+        const T* O = (const T*)a.ctx + (size_t)(b * S + ql) * H + h * D;
+        float part = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int off = ks * 16 + (lane >> 5) * 8;
+            qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)ql * D + off);
+            df[ks] = *reinterpret_cast<const v8*>(dO + (size_t)ql * D + off);
+            const v8 ov = *reinterpret_cast<const v8*>(O + off);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) part += to_f(df[ks][i]) * to_f(ov[i]);
+        }
+        Dq = part + __shfl_xor(part, 32, 64);
+        lse2 = a.lse[(size_t)(b * NH + h) * S + ql];
+        if (lane < 32) a.dvec[(size_t)(b * NH + h) * S + ql] = Dq;
+    }
+    f32x16 dq[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dq[ct][r] = 0.0f;
+    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + ql) * (uint64_t)S;
+
+    for (int kb = 0; kb < nkb; ++kb) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+            const uint4 kv = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row) * D + ch * 8);
+            const uint4 vv = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row) * D + ch * 8);
+            *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = kv;
+            *reinterpret_cast<uint4*>(Vs + kmaj_off(row, ch * 8)) = vv;
+        }
+        __syncthreads();
+        if (active) {
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { s[kt][r] = 0.0f; dp[kt][r] = 0.0f; }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks, kt * 32, ks, lane), qf[ks], s[kt]);
+                    dp[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Vs, kt * 32, ks, lane), df[ks], dp[kt]);
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
+                    uint32_t kbits = 0xFu;
+                    if (a.drop.thr) kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = g * 4 + i;
+                        const float p = (key4 + i < L) ? exp2f(s[kt][r] * c - lse2) : 0.0f;
+                        const float f = ((kbits >> i) & 1u) ? a.drop.scale : 0.0f;
+                        s[kt][r] = p * (dp[kt][r] * f - Dq);
+                    }
+                }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 4; ++ks2) {
+                const int kt = ks2 >> 1, half = ks2 & 1;
+                v8 pf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[i] = from_f<T>(s[kt][(2 * half) * 4 + i]);
+                    pf[4 + i] = from_f<T>(s[kt][(2 * half + 1) * 4 + i]);
+                }
+                const int kb0 = kt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    dq[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Ks, ct * 32, kb0, kb0 + 8, lane), pf, dq[ct]);
+            }
+        }
+        __syncthreads();
+    }
+    if (active) {
+        T* out = (T*)a.dqkv + (size_t)(b * S + ql) * (3 * H) + h * D;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = dq[ct][g * 4 + i] * 0.125f;
+                Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+            }
+    }
+}
+
+// ------------------------------------------------------------------ MFMA bwd: dK, dV
+template <typename T>
+__global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
+    constexpr int D = 64, QB = 64;
+    typedef typename MfmaOp<T>::v8 v8;
+    __shared__ __align__(16) T Qs[QB * D];
+    __shared__ __align__(16) T Os[QB * D];
+    __shared__ float lse_s[QB], D_s[QB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
+    const int key0 = blockIdx.x * 128 + wave * 32;
+    const bool active = key0 < S;
+    const int L = a.len ? a.len[b] : S;
+    const bool live = active && key0 < L;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const T* dO = (const T*)a.dout + ((size_t)b * NH + h) * head;
+    const float* lse = a.lse + (size_t)(b * NH + h) * S;
+    const float* Dv = a.dvec + (size_t)(b * NH + h) * S;
+    const float c = kLog2e * 0.125f;
+    const int kl = key0 + (lane & 31);
+    const uint64_t bhbase = (uint64_t)(b * NH + h) * S;
+
+    v8 kf[4], vf[4];
+    if (live) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int off = ks * 16 + (lane >> 5) * 8;
+            kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)kl * D + off);
+            vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)kl * D + off);
+        }
+    }
+    f32x16 dk[2], dv[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dk[ct][r] = 0.0f; dv[ct][r] = 0.0f; }
+
+    const int nqb = S / QB;
+    for (int qb = 0; qb < nqb; ++qb) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+            const uint4 qv = *reinterpret_cast<const uint4*>(Q + (size_t)(qb * QB + row) * D + ch * 8);
+            const uint4 ov = *reinterpret_cast<const uint4*>(dO + (size_t)(qb * QB + row) * D + ch * 8);
+            *reinterpret_cast<uint4*>(Qs + kmaj_off(row, ch * 8)) = qv;
+            *reinterpret_cast<uint4*>(Os + kmaj_off(row, ch * 8)) = ov;
+        }
+        if (tid < QB) lse_s[tid] = lse[qb * QB + tid];
+        else if (tid < 2 * QB) D_s[tid - QB] = Dv[qb * QB + tid - QB];
+        __syncthreads();
+        if (live) {
+            f32x16 s[2], dp[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { s[qt][r] = 0.0f; dp[qt][r] = 0.0f; }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    s[qt] = MfmaOp<T>::mma(frag_kmaj<T>(Qs, qt * 32, ks, lane), kf[ks], s[qt]);
+                    dp[qt] = MfmaOp<T>::mma(frag_kmaj<T>(Os, qt * 32, ks, lane), vf[ks], dp[qt]);
+                }
+            }
+            // s[qt][r]: query qb*64 + qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl
+            f32x16 ds[2];
+#pragma unroll
+            for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = qt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const int q = qb * QB + qi;
+                    const float p = kl < L ? exp2f(s[qt][r] * c - lse_s[qi]) : 0.0f;
+                    float f = 1.0f;
+                    if (a.drop.thr) f = keep1(a.drop.rng, (bhbase + q) * S + kl, a.drop.thr) ? a.drop.scale : 0.0f;
+                    ds[qt][r] = p * (dp[qt][r] * f - D_s[qi]);
+                    s[qt][r] = p * f;
+                }
+#pragma unroll
+            for (int ks2 = 0; ks2 < 4; ++ks2) {
+                const int qt = ks2 >> 1, half = ks2 & 1;
+                v8 pf, sf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[i] = from_f<T>(s[qt][(2 * half) * 4 + i]);
+                    pf[4 + i] = from_f<T>(s[qt][(2 * half + 1) * 4 + i]);
+                    sf[i] = from_f<T>(ds[qt][(2 * half) * 4 + i]);
+                    sf[4 + i] = from_f<T>(ds[qt][(2 * half + 1) * 4 + i]);
+                }
+                const int qb0 = qt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) {
+                    dv[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Os, ct * 32, qb0, qb0 + 8, lane), pf, dv[ct]);
+                    dk[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Qs, ct * 32, qb0, qb0 + 8, lane), sf, dk[ct]);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    if (active) {
+        T* outk = (T*)a.dqkv + (size_t)(b * S + kl) * (3 * H) + H + h * D;
+        T* outv = outk + H;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float vk[4], vv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vk[i] = dk[ct][g * 4 + i] * 0.125f;
+                    vv[i] = dv[ct][g * 4 + i];
+                }
+                const int col = ct * 32 + g * 8 + (lane >> 5) * 4;
+                Vec4<T>::store(outk + col, vk);
+                Vec4<T>::store(outv + col, vv);
+            }
+    }
+}
+
+// ------------------------------------------------------------------ SIMT
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_fwd_simt(AttnArgs a) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
+    if (idx >= B * NH * S) return;
+    const int q = idx % S, bh = idx / S, b = bh / NH, h = bh % NH;
+    const int L = a.len ? a.len[b] : S;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const float c = kLog2e / sqrtf((float)D);
+    float qv[D], o[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) { qv[i] = to_f(Q[(size_t)q * D + i]); o[i] = 0.0f; }
+    float m = -INFINITY, l = 0.0f;
+    const uint64_t rowbase = ((uint64_t)bh * S + q) * (uint64_t)S;
+    for (int j = 0; j < L; ++j) {
+        float s = 0.0f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) s += qv[i] * to_f(K[(size_t)j * D + i]);
+        s *= c;
+        const float mn = fmaxf(m, s);
+        const float alpha = exp2f(m - mn), p = exp2f(s - mn);
+        l = l * alpha + p;
+        m = mn;
+        const float pk = (a.drop.thr && !keep1(a.drop.rng, rowbase + j, a.drop.thr)) ? 0.0f : p;
+#pragma unroll
+        for (int i = 0; i < D; ++i) o[i] = o[i] * alpha + pk * to_f(V[(size_t)j * D + i]);
+    }
+    T* out = (T*)a.ctx + (size_t)(b * S + q) * H + h * D;
+    const float inv = a.drop.scale / l;
+#pragma unroll
+    for (int i = 0; i < D; ++i) out[i] = from_f<T>(o[i] * inv);
+    a.lse[idx] = m + log2f(l);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_bwd_dq_simt(AttnArgs a) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
+    if (idx >= B * NH * S) return;
+    const int q = idx % S, bh = idx / S, b = bh / NH, h = bh % NH;
+    const int L = a.len ? a.len[b] : S;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const T* dO = (const T*)a.dout + (size_t)bh * head;
+    const T* O = (const T*)a.ctx + (size_t)(b * S + q) * H + h * D;
+    const float c = kLog2e / sqrtf((float)D);
+    float qv[D], dov[D], dq[D];
+    float Dq = 0.0f;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        qv[i] = to_f(Q[(size_t)q * D + i]);
+        dov[i] = to_f(dO[(size_t)q * D + i]);
+        Dq += dov[i] * to_f(O[i]);
+        dq[i] = 0.0f;
+    }
+    a.dvec[idx] = Dq;
+    const float lse2 = a.lse[idx];
+    const uint64_t rowbase = ((uint64_t)bh * S + q) * (uint64_t)S;
+    for (int j = 0; j < L; ++j) {
+        float s = 0.0f, dp = 0.0f;
+#pragma unroll
+        for (int i = 0; i < D; ++i) {
+            s += qv[i] * to_f(K[(size_t)j * D + i]);
+            dp += dov[i] * to_f(V[(size_t)j * D + i]);
+        }
+        const float p = exp2f(s * c - lse2);
+        float f = 1.0f;
+        if (a.drop.thr) f = keep1(a.drop.rng, rowbase + j, a.drop.thr) ? a.drop.scale : 0.0f;
+        const float ds = p * (dp * f - Dq);
+#pragma unroll
+        for (int i = 0; i < D; ++i) dq[i] += ds * to_f(K[(size_t)j * D + i]);
+    }
+    const float sc = 1.0f / sqrtf((float)D);
+    T* out = (T*)a.dqkv + (size_t)(b * S + q) * (3 * H) + h * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) out[i] = from_f<T>(dq[i] * sc);
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(128) void attn_bwd_dkdv_simt(AttnArgs a) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
+    if (idx >= B * NH * S) return;
+    const int j = idx % S, bh = idx / S, b = bh / NH, h = bh % NH;
+    const int L = a.len ? a.len[b] : S;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const T* dO = (const T*)a.dout + (size_t)bh * head;
+    const float* lse = a.lse + (size_t)bh * S;
+    const float* Dv = a.dvec + (size_t)bh * S;
+    const float c = kLog2e / sqrtf((float)D);
+    float kv[D], vv[D], dk[D], dv[D];
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        kv[i] = to_f(K[(size_t)j * D + i]);
+        vv[i] = to_f(V[(size_t)j * D + i]);
+        dk[i] = 0.0f;
+        dv[i] = 0.0f;
+    }
+    if (j < L) {
+        for (int q = 0; q < S; ++q) {
+            float s = 0.0f, dp = 0.0f;
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                s += to_f(Q[(size_t)q * D + i]) * kv[i];
+                dp += to_f(dO[(size_t)q * D + i]) * vv[i];
+            }
+            const float p = exp2f(s * c - lse[q]);
+            float f = 1.0f;
+            if (a.drop.thr) f = keep1(a.drop.rng, ((uint64_t)bh * S + q) * S + j, a.drop.thr) ? a.drop.scale : 0.0f;
+            const float ds = p * (dp * f - Dv[q]);
+#pragma unroll
+            for (int i = 0; i < D; ++i) {
+                dv[i] += p * f * to_f(dO[(size_t)q * D + i]);
+                dk[i] += ds * to_f(Q[(size_t)q * D + i]);
+            }
+        }
+    }
+    const float sc = 1.0f / sqrtf((float)D);
+    T* outk = (T*)a.dqkv + (size_t)(b * S + j) * (3 * H) + H + h * D;
+    T* outv = outk + H;
+#pragma unroll
+    for (int i = 0; i < D; ++i) {
+        outk[i] = from_f<T>(dk[i] * sc);
+        outv[i] = from_f<T>(dv[i]);
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+static bool mfma_attn_ok(const AttnArgs& a) { return a.dtype != 0 && a.d == 64 && a.S % 64 == 0; }
+
+template <typename T, int D>
+static hipError_t simt_fwd(const AttnArgs& a, hipStream_t st) {
+    const int n = a.B * a.NH * a.S;
+    hipLaunchKernelGGL((attn_fwd_simt<T, D>), dim3((n + 127) / 128), dim3(128), 0, st, a);
+    return hipGetLastError();
+}
+template <typename T, int D>
+static hipError_t simt_bwd(const AttnArgs& a, hipStream_t st) {
+    const int n = a.B * a.NH * a.S;
+    hipLaunchKernelGGL((attn_bwd_dq_simt<T, D>), dim3((n + 127) / 128), dim3(128), 0, st, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((attn_bwd_dkdv_simt<T, D>), dim3((n + 127) / 128), dim3(128), 0, st, a);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t fwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
+    if constexpr (!std::is_same<T, float>::value) {
+        if (!force_simt && mfma_attn_ok(a)) {
+            dim3 grid((a.S + 127) / 128, a.NH, a.B);
+            hipLaunchKernelGGL(attn_fwd_mfma<T>, grid, dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    switch (a.d) {
+        case 16: return simt_fwd<T, 16>(a, st);
+        case 32: return simt_fwd<T, 32>(a, st);
+        case 64: return simt_fwd<T, 64>(a, st);
+        case 128: return simt_fwd<T, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T>
+static hipError_t bwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
+    if constexpr (!std::is_same<T, float>::value) {
+        if (!force_simt && mfma_attn_ok(a)) {
+            dim3 grid((a.S + 127) / 128, a.NH, a.B);
+            hipLaunchKernelGGL(attn_bwd_dq_mfma<T>, grid, dim3(256), 0, st, a);
+            hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+            hipLaunchKernelGGL(attn_bwd_dkdv_mfma<T>, grid, dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
+    }
+    switch (a.d) {
+        case 16: return simt_bwd<T, 16>(a, st);
+        case 32: return simt_bwd<T, 32>(a, st);
+        case 64: return simt_bwd<T, 64>(a, st);
+        case 128: return simt_bwd<T, 128>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t attn_forward(const AttnArgs& a, hipStream_t st, bool force_simt) {
+    switch (a.dtype) {
+        case 0: return fwd_t<float>(a, st, true);
+        case 1: return fwd_t<f16>(a, st, force_simt);
+        case 2: return fwd_t<bf16>(a, st, force_simt);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t attn_backward(const AttnArgs& a, hipStream_t st, bool force_simt) {
+    switch (a.dtype) {
+        case 0: return bwd_t<float>(a, st, true);
+        case 1: return bwd_t<f16>(a, st, force_simt);
+        case 2: return bwd_t<bf16>(a, st, force_simt);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace tel

@@ -1,0 +1,62 @@
+// gemm.h -- host-side description of one GEMM with a fused epilogue.
+//   C[m][n] = sum_k A(m,k) * B(n,k),  0 <= m < M, 0 <= n < N, 0 <= k < K
+//   A(m,k) = a_kmajor ? A[m*lda + k] : A[k*lda + m]
+//   B(n,k) = b_kmajor ? B[n*ldb + k] : B[k*ldb + n]
+// Forward projections (Y = X W^T) are (A k-major, B k-major); input
+// gradients (dX = dY W) are (A k-major, B n-major); weight gradients
+// (dW = dY^T X) are (A m-major, B n-major).
+#pragma once
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime.h>
+#include "tel_common.h"
+
+namespace tel {
+
+enum EpiKind {
+    EPI_STORE = 0,         // out = v                               (T, or f32 if out_f32)
+    EPI_QKV = 1,           // v + bias, scattered to [3][B][N][S][d]
+    EPI_BIAS_DROP_RES = 2, // out = res + drop(v + bias)            (res T|f32, out T|f32)
+    EPI_BIAS_GELU = 3,     // u = v + bias -> out; GELU(u) -> out2 (if non-null)
+    EPI_GELU_BWD = 4,      // out = v * GELU'(aux)
+    EPI_HEADSPLIT = 5,     // v scattered to [B][N][S][d]
+    EPI_ADD_RES = 6,       // out = v + res(f32)
+};
+
+struct EpiArgs {
+    void* out = nullptr;
+    int ldo = 0;
+    int out_f32 = 0;
+    const void* bias = nullptr;
+    const void* res = nullptr;
+    int res_f32 = 0;
+    void* out2 = nullptr;
+    const void* aux = nullptr;
+    int B = 0, S = 0, H = 0, NH = 0, d = 0;  // head-split geometry
+    Drop drop{};                              // thr == 0: no dropout
+};
+
+struct GemmDesc {
+    int dtype = 0;  // tel_dtype
+    int M = 0, N = 0, K = 0;
+    const void* A = nullptr;
+    int lda = 0;
+    bool a_kmajor = true;
+    const void* B = nullptr;
+    int ldb = 0;
+    bool b_kmajor = true;
+    bool b_gelu = false;  // B elements pass through GELU on load
+    int epi = EPI_STORE;
+    EpiArgs ea;
+    float* splitk_ws = nullptr;  // fp32 [splits][M][N] partials (weight gradients)
+    size_t splitk_ws_elems = 0;
+};
+
+// Launch; returns hipSuccess or the launch error.  force_simt selects the
+// generic SIMT kernel regardless of shape (used by tests).
+hipError_t gemm_launch(const GemmDesc& g, hipStream_t stream, bool force_simt = false);
+
+// Elements of split-K workspace the dispatcher will use for this GEMM (0 if none).
+size_t gemm_splitk_elems(const GemmDesc& g);
+
+}  // namespace tel

@@ -1,0 +1,506 @@
+// gemm.hip -- GEMMs of the encoder layer on gfx950 with fused epilogues.
+//
+// Fast path: fp16/bf16 MFMA (v_mfma_f32_32x32x16_{f16,bf16}, fp32
+// accumulation) with LDS double buffering.  A k-major operand tile is kept
+// in LDS as [rows][64 k] with 16-byte chunks XOR-swizzled by row and read
+// with 128-bit LDS loads; an m/n-major operand tile is kept as
+// [64 k][rows + pad] exactly as in global memory and read with the gfx950
+// transposing LDS load (ds_read_b64_tr_b16), so no layout needs a separate
+// transpose pass.  The MFMA "A" operand is the B tile and the "B" operand
+// the A tile, so each lane ends with four consecutive output columns of one
+// row: epilogues (bias, GELU, dropout, residual, head split) work on
+// 4-wide vectors and store 8 or 16 bytes.
+//
+// Generic path: a SIMT fp32-FMA tiled GEMM with bounds checks for every
+// shape and dtype (the fp32 configuration and shapes the MFMA tiles do not
+// divide).  Both paths share the epilogue code.
+#include "gemm.h"
+#include "mfma_common.h"
+#include <type_traits>
+
+namespace tel {
+
+// ------------------------------------------------------------------ epilogue
+template <typename T, int EPI>
+__device__ __forceinline__ void epilogue4(const EpiArgs& e, int m, int n, float v[4]) {
+    if constexpr (EPI == EPI_STORE) {
+        if (e.out_f32) Vec4<float>::store((float*)e.out + (size_t)m * e.ldo + n, v);
+        else Vec4<T>::store((T*)e.out + (size_t)m * e.ldo + n, v);
+    } else if constexpr (EPI == EPI_QKV) {
+        float b[4];
+        Vec4<T>::load((const T*)e.bias + n, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += b[i];
+        const int which = n / e.H, rem = n - which * e.H, h = rem / e.d, c = rem - h * e.d;
+        const int bb = m / e.S, s = m - bb * e.S;
+        const size_t off = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
+        Vec4<T>::store((T*)e.out + off, v);
+    } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
+        float b[4], r[4];
+        Vec4<T>::load((const T*)e.bias + n, b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += b[i];
+        if (e.drop.thr) {
+            const uint64_t el = (uint64_t)m * e.ldo + n;  // token * H + column, n % 4 == 0
+            const uint32_t k = keep4(e.drop.rng, el >> 2, e.drop.thr);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * e.drop.scale : 0.0f;
+        }
+        const size_t off = (size_t)m * e.ldo + n;
+        if (e.res_f32) Vec4<float>::load((const float*)e.res + off, r);
+        else Vec4<T>::load((const T*)e.res + off, r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += r[i];
+        if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
+        else Vec4<T>::store((T*)e.out + off, v);
+    } else if constexpr (EPI == EPI_BIAS_GELU) {
+        float b[4];
+        Vec4<T>::load((const T*)e.bias + n, b);
+        const size_t off = (size_t)m * e.ldo + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += b[i];
+        Vec4<T>::store((T*)e.out + off, v);
+        if (e.out2) {
+            float g[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) g[i] = gelu_f(round_through<T>(v[i]));
+            Vec4<T>::store((T*)e.out2 + off, g);
+        }
+    } else if constexpr (EPI == EPI_GELU_BWD) {
+        float u[4];
+        const size_t off = (size_t)m * e.ldo + n;
+        Vec4<T>::load((const T*)e.aux + off, u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= gelu_grad_f(u[i]);
+        Vec4<T>::store((T*)e.out + off, v);
+    } else if constexpr (EPI == EPI_HEADSPLIT) {
+        const int bb = m / e.S, s = m - bb * e.S, h = n / e.d, c = n - h * e.d;
+        const size_t off = (((size_t)bb * e.NH + h) * e.S + s) * e.d + c;
+        Vec4<T>::store((T*)e.out + off, v);
+    } else if constexpr (EPI == EPI_ADD_RES) {
+        float r[4];
+        const size_t off = (size_t)m * e.ldo + n;
+        Vec4<float>::load((const float*)e.res + off, r);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += r[i];
+        Vec4<T>::store((T*)e.out + off, v);
+    }
+}
+
+struct GemmParams {
+    const void* A;
+    const void* B;
+    int lda, ldb;
+    int M, N, K;
+    int k_per_split;  // multiple of the k tile
+    EpiArgs ea;
+    float* ws;        // split-K partials, [splits][M][N]
+};
+
+// ------------------------------------------------------------------ MFMA path
+constexpr int KT = 64;        // k tile (elements)
+constexpr int MN_PAD = 16;    // padding (elements) of m/n-major LDS rows
+
+template <bool KMAJ, int R>
+struct TileGeom {
+    static constexpr int ELEMS = KMAJ ? R * KT : KT * (R + MN_PAD);
+    static constexpr int CHUNKS = R * KT / 8;  // 16-byte chunks per tile
+};
+
+// Fragment for a 32x32x16 MFMA operand: lane l gets rows rb + (l & 31),
+// k = ks*16 + 8*(l >> 5) .. +7.
+template <typename T, bool KMAJ, int R>
+__device__ __forceinline__ typename MfmaOp<T>::v8 frag_load(const T* lds, int rb, int ks, int lane) {
+    if constexpr (KMAJ) {
+        return frag_kmaj<T>(lds, rb, ks, lane);
+    } else {
+        const int kb = ks * 16 + (lane >> 5) * 8;
+        return frag_tr<T>(lds, R + MN_PAD, rb, kb, kb + 4, lane);
+    }
+}
+
+// Load one operand tile (R rows of the m or n dimension, KT of k) from global
+// into registers: CPT chunks of 8 elements per thread.
+template <typename T, bool KMAJ, int R, int NT>
+__device__ __forceinline__ void tile_load(uint4* reg, const T* base, int ld,
+                                          int row0, int k0, int tid) {
+    constexpr int CPT = TileGeom<KMAJ, R>::CHUNKS / NT;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        if constexpr (KMAJ) {
+            const int row = c >> 3, ch = c & 7;
+            reg[i] = *reinterpret_cast<const uint4*>(base + (size_t)(row0 + row) * ld + k0 + ch * 8);
+        } else {
+            constexpr int CPR = R / 8;  // chunks per k row
+            const int kr = c / CPR, ch = c - kr * CPR;
+            reg[i] = *reinterpret_cast<const uint4*>(base + (size_t)(k0 + kr) * ld + row0 + ch * 8);
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ uint4 gelu_chunk(uint4 u) {
+    typedef T v8 __attribute__((ext_vector_type(8)));
+    v8 x = *reinterpret_cast<v8*>(&u);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = from_f<T>(gelu_f(to_f(x[i])));
+    return *reinterpret_cast<uint4*>(&x);
+}
+
+template <typename T, bool KMAJ, int R, int NT, bool GELU>
+__device__ __forceinline__ void tile_store(T* lds, const uint4* reg, int tid) {
+    constexpr int CPT = TileGeom<KMAJ, R>::CHUNKS / NT;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        uint4 val = reg[i];
+        if constexpr (GELU) val = gelu_chunk<T>(val);
+        if constexpr (KMAJ) {
+            const int row = c >> 3, ch = c & 7;
+            *reinterpret_cast<uint4*>(lds + kmaj_off(row, ch * 8)) = val;
+        } else {
+            constexpr int CPR = R / 8;
+            const int kr = c / CPR, ch = c - kr * CPR;
+            *reinterpret_cast<uint4*>(lds + kr * (R + MN_PAD) + ch * 8) = val;
+        }
+    }
+}
+
+// Map the linear workgroup id to an output tile.  Consecutive ids are
+// dispatched round-robin over the 8 XCDs; the remap gives each XCD one
+// contiguous range of tiles, walked in groups of GM tile rows so that the
+// tiles resident on one XCD share A rows and B columns in its L2.
+__device__ __forceinline__ void tile_of(int pid, int tm, int tn, int& im, int& in_) {
+    const int total = tm * tn;
+    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    constexpr int GM = 8;
+    const int group = pid / (GM * tn);
+    const int first = group * GM;
+    const int gm = min(tm - first, GM);
+    const int r = pid - group * GM * tn;
+    im = first + r % gm;
+    in_ = r / gm;
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
+__global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) {
+    constexpr int NT = WGM * WGN * 64;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int MI = WM / 32, NI = WN / 32;
+    typedef TileGeom<AK, BM> GA;
+    typedef TileGeom<BKM, BN> GB;
+    constexpr int STAGE = GA::ELEMS + GB::ELEMS;
+    static_assert(GA::CHUNKS % NT == 0 && GB::CHUNKS % NT == 0, "tile/thread mismatch");
+    typedef typename MfmaOp<T>::v8 v8;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* smem = reinterpret_cast<T*>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int tm = p.M / BM, tn = p.N / BN;
+    int im, in_;
+    tile_of(blockIdx.x, tm, tn, im, in_);
+    const int m0 = im * BM, n0 = in_ * BN;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nk = (kend - kbeg) / KT;
+
+    const T* A = (const T*)p.A;
+    const T* B = (const T*)p.B;
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    uint4 ra[GA::CHUNKS / NT], rb[GB::CHUNKS / NT];
+    tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg, tid);
+    tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg, tid);
+    tile_store<T, AK, BM, NT, false>(smem, ra, tid);
+    tile_store<T, BKM, BN, NT, BGELU>(smem + GA::ELEMS, rb, tid);
+    __syncthreads();
+
+    for (int kt = 0; kt < nk; ++kt) {
+        const T* sa = smem + (kt & 1) * STAGE;
+        const T* sb = sa + GA::ELEMS;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg + (kt + 1) * KT, tid);
+            tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg + (kt + 1) * KT, tid);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KT / 16; ++ks) {
+            v8 fa[MI], fb[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) fa[i] = frag_load<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) fb[j] = frag_load<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
+        }
+        if (more) {
+            T* da = smem + ((kt + 1) & 1) * STAGE;
+            tile_store<T, AK, BM, NT, false>(da, ra, tid);
+            tile_store<T, BKM, BN, NT, BGELU>(da + GA::ELEMS, rb, tid);
+        }
+        __syncthreads();
+    }
+
+    // acc[i][j][g*4 + r]: row m = m0 + wm*WM + i*32 + (lane & 31),
+    // columns n .. n+3 with n = n0 + wn*WN + j*32 + g*8 + (lane >> 5)*4.
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int m = m0 + wm * WM + i * 32 + (lane & 31);
+                const int n = n0 + wn * WN + j * 32 + g * 8 + (lane >> 5) * 4;
+                float v[4] = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                              acc[i][j][g * 4 + 3]};
+                if (gridDim.z > 1) {
+                    Vec4<float>::store(p.ws + ((size_t)blockIdx.z * p.M + m) * p.N + n, v);
+                } else {
+                    epilogue4<T, EPI>(p.ea, m, n, v);
+                }
+            }
+}
+
+// Deterministic split-K reduction: out[m][n] = sum_z ws[z][m][n] in z order.
+template <typename T>
+__global__ void splitk_reduce_kernel(const float* ws, int splits, int M, int N, EpiArgs ea) {
+    const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+    const size_t MN = (size_t)M * N;
+    if (i4 >= MN) return;
+    float v[4] = {0, 0, 0, 0};
+    for (int z = 0; z < splits; ++z) {
+        float t[4];
+        Vec4<float>::load(ws + z * MN + i4, t);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += t[i];
+    }
+    const int m = (int)(i4 / N), n = (int)(i4 - (size_t)m * N);
+    epilogue4<T, EPI_STORE>(ea, m, n, v);
+}
+
+// ------------------------------------------------------------------ SIMT path
+template <typename T, int EPI, bool BGELU>
+__global__ __launch_bounds__(256) void gemm_simt_kernel(GemmParams p, int a_kmajor, int b_kmajor) {
+    constexpr int TB = 64, TK = 16;
+    __shared__ float As[TK][TB + 1];
+    __shared__ float Bs[TK][TB + 1];
+    const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+    const int m0 = blockIdx.y * TB, n0 = blockIdx.x * TB;
+    const T* A = (const T*)p.A;
+    const T* B = (const T*)p.B;
+    float acc[4][4] = {};
+    for (int k0 = 0; k0 < p.K; k0 += TK) {
+        for (int e = tid; e < TB * TK; e += 256) {
+            const int r = e / TK, kk = e % TK;  // r: row in tile, kk: k in tile
+            const int m = m0 + r, n = n0 + r, k = k0 + kk;
+            float av = 0.f, bv = 0.f;
+            if (m < p.M && k < p.K) av = to_f(a_kmajor ? A[(size_t)m * p.lda + k] : A[(size_t)k * p.lda + m]);
+            if (n < p.N && k < p.K) {
+                bv = to_f(b_kmajor ? B[(size_t)n * p.ldb + k] : B[(size_t)k * p.ldb + n]);
+                if constexpr (BGELU) bv = to_f(from_f<T>(gelu_f(bv)));
+            }
+            As[kk][r] = av;
+            Bs[kk][r] = bv;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < TK; ++kk) {
+            float a[4], b[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = As[kk][ty + 16 * i];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+    const int n = n0 + tx * 4;
+    if (n >= p.N) return;  // N % 4 == 0: a 4-group is wholly in or out
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int m = m0 + ty + 16 * i;
+        if (m < p.M) epilogue4<T, EPI>(p.ea, m, n, acc[i]);
+    }
+}
+
+// ------------------------------------------------------------------ dispatch
+struct TileCfg {
+    int BM, BN;
+};
+
+static bool mfma_ok(const GemmDesc& g, int BM, int BN) {
+    return g.M % BM == 0 && g.N % BN == 0 && g.K % KT == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
+}
+
+// Split-K count for a weight-gradient GEMM whose tile grid is too small to
+// fill 256 CUs; 1 otherwise.
+static int splitk_for(const GemmDesc& g, int BM, int BN) {
+    if (g.epi != EPI_STORE || g.splitk_ws == nullptr) return 1;
+    const int tiles = (g.M / BM) * (g.N / BN);
+    const int ksteps = g.K / KT;
+    int s = 1;
+    while (tiles * s < 256 && s * 2 <= ksteps / 8 && ksteps % (s * 2) == 0) s *= 2;
+    if ((size_t)s * g.M * g.N > g.splitk_ws_elems) s = 1;
+    return s;
+}
+
+static TileCfg pick_tiles(const GemmDesc& g) {
+    // largest tile whose grid still yields >= 256 workgroups, else 128x128
+    const TileCfg cands[] = {{256, 256}, {256, 128}, {128, 128}};
+    for (const TileCfg& c : cands) {
+        if (!mfma_ok(g, c.BM, c.BN)) continue;
+        const int tiles = (g.M / c.BM) * (g.N / c.BN);
+        if (tiles >= 256 || (c.BM == 128 && c.BN == 128)) return c;
+    }
+    return {0, 0};
+}
+
+template <typename Kern>
+static hipError_t set_lds(Kern k, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(k), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
+static hipError_t launch_mfma(const GemmDesc& g, hipStream_t st, int splits) {
+    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws};
+    auto kern = gemm_mfma_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI, BGELU>;
+    const size_t lds = 2 * (TileGeom<AK, BM>::ELEMS + TileGeom<BKM, BN>::ELEMS) * sizeof(T);
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = set_lds(kern, lds);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    dim3 grid((g.M / BM) * (g.N / BN), 1, splits);
+    hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const size_t n4 = (size_t)g.M * g.N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea);
+    return hipGetLastError();
+}
+
+template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
+static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
+    if (c.BM == 256 && c.BN == 256) {
+        int s = splitk_for(g, 256, 256);
+        return launch_mfma<T, 256, 256, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
+    }
+    if (c.BM == 256 && c.BN == 128) {
+        int s = splitk_for(g, 256, 128);
+        return launch_mfma<T, 256, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
+    }
+    int s = splitk_for(g, 128, 128);
+    return launch_mfma<T, 128, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
+}
+
+// Operand layouts the layer uses with each epilogue: projections (A, B
+// k-major) end in QKV / bias+dropout+residual / bias+GELU; input gradients
+// (B n-major) in GELU' / store / head split / residual add; weight gradients
+// (A m-major, B n-major) in store.  Other combinations take the SIMT path.
+template <int EPI, bool AK, bool BKM>
+constexpr bool mfma_combo() {
+    if (AK && BKM) return EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES || EPI == EPI_BIAS_GELU || EPI == EPI_STORE;
+    if (AK && !BKM) return EPI == EPI_GELU_BWD || EPI == EPI_STORE || EPI == EPI_HEADSPLIT || EPI == EPI_ADD_RES;
+    if (!AK && !BKM) return EPI == EPI_STORE;
+    return false;
+}
+
+template <typename T, int EPI, bool BGELU>
+static hipError_t dispatch_mfma(const GemmDesc& g, hipStream_t st, TileCfg c) {
+    if (g.a_kmajor && g.b_kmajor) {
+        if constexpr (mfma_combo<EPI, true, true>() && !BGELU) return dispatch_tiles<T, EPI, BGELU, true, true>(g, st, c);
+    } else if (g.a_kmajor && !g.b_kmajor) {
+        if constexpr (mfma_combo<EPI, true, false>() && !BGELU) return dispatch_tiles<T, EPI, BGELU, true, false>(g, st, c);
+    } else if (!g.a_kmajor && !g.b_kmajor) {
+        if constexpr (mfma_combo<EPI, false, false>()) return dispatch_tiles<T, EPI, BGELU, false, false>(g, st, c);
+    }
+    return hipErrorNotSupported;
+}
+
+template <typename T, int EPI, bool BGELU>
+static hipError_t launch_simt(const GemmDesc& g, hipStream_t st) {
+    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K, g.ea, nullptr};
+    dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
+    hipLaunchKernelGGL((gemm_simt_kernel<T, EPI, BGELU>), grid, dim3(256), 0, st, p, (int)g.a_kmajor,
+                       (int)g.b_kmajor);
+    return hipGetLastError();
+}
+
+template <typename T, int EPI>
+static hipError_t dispatch_epi(const GemmDesc& g, hipStream_t st, bool force_simt) {
+    constexpr bool lowp = !std::is_same<T, float>::value;
+    if constexpr (lowp) {
+        if (!force_simt) {
+            TileCfg c = pick_tiles(g);
+            if (c.BM) {
+                hipError_t e = hipErrorNotSupported;
+                if (g.b_gelu) {
+                    if constexpr (EPI == EPI_STORE) e = dispatch_mfma<T, EPI, true>(g, st, c);
+                } else {
+                    e = dispatch_mfma<T, EPI, false>(g, st, c);
+                }
+                if (e != hipErrorNotSupported) return e;
+            }
+        }
+    }
+    if (g.b_gelu) {
+        if constexpr (EPI == EPI_STORE) return launch_simt<T, EPI, true>(g, st);
+        return hipErrorInvalidValue;
+    }
+    return launch_simt<T, EPI, false>(g, st);
+}
+
+template <typename T>
+static hipError_t dispatch_type(const GemmDesc& g, hipStream_t st, bool force_simt) {
+    switch (g.epi) {
+        case EPI_STORE: return dispatch_epi<T, EPI_STORE>(g, st, force_simt);
+        case EPI_QKV: return dispatch_epi<T, EPI_QKV>(g, st, force_simt);
+        case EPI_BIAS_DROP_RES: return dispatch_epi<T, EPI_BIAS_DROP_RES>(g, st, force_simt);
+        case EPI_BIAS_GELU: return dispatch_epi<T, EPI_BIAS_GELU>(g, st, force_simt);
+        case EPI_GELU_BWD: return dispatch_epi<T, EPI_GELU_BWD>(g, st, force_simt);
+        case EPI_HEADSPLIT: return dispatch_epi<T, EPI_HEADSPLIT>(g, st, force_simt);
+        case EPI_ADD_RES: return dispatch_epi<T, EPI_ADD_RES>(g, st, force_simt);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t gemm_launch(const GemmDesc& g, hipStream_t st, bool force_simt) {
+    if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+    switch (g.dtype) {
+        case 0: return dispatch_type<float>(g, st, true);
+        case 1: return dispatch_type<f16>(g, st, force_simt);
+        case 2: return dispatch_type<bf16>(g, st, force_simt);
+    }
+    return hipErrorInvalidValue;
+}
+
+size_t gemm_splitk_elems(const GemmDesc& g) {
+    if (g.dtype == 0) return 0;
+    TileCfg c = pick_tiles(g);
+    if (!c.BM) return 0;
+    GemmDesc h = g;
+    h.splitk_ws = reinterpret_cast<float*>(16);
+    h.splitk_ws_elems = (size_t)-1;
+    const int s = splitk_for(h, c.BM, c.BN);
+    return s > 1 ? (size_t)s * g.M * g.N : 0;
+}
+
+}  // namespace tel

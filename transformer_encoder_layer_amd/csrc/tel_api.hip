@@ -1,0 +1,609 @@
+// tel_api.hip -- the C ABI of the fused encoder layer: argument validation,
+// workspace planning and the launch sequence of one forward / backward.
+//
+// Launch sequence (per call, all on the caller's stream, no host sync):
+//   Pre-LN forward : LN1 -> QKV GEMM (+bias, head split) -> attention ->
+//                    out-proj GEMM (+bias, dropout 1, +x) -> LN2 ->
+//                    FFN1 GEMM (+bias, GELU) -> FFN2 GEMM (+bias, dropout 2, +x1)
+//   Post-LN forward: QKV GEMM -> attention -> out-proj GEMM (+x) -> LN1 ->
+//                    FFN1 -> FFN2 (+x1) -> LN2
+//   backward       : the chain rule in reverse; each GEMM is split into an
+//                    input-gradient GEMM (with the GELU' / head-split / residual
+//                    epilogue) and a weight-gradient GEMM; bias, gamma and beta
+//                    gradients are deterministic two-stage column sums.
+// The residual stream (x1, and z1/z2 for Post-LN) is kept in fp32 so that
+// the output carries a single rounding to the storage dtype.
+#include <math.h>
+#include <stdarg.h>
+#include <new>
+#include <stdio.h>
+#include <string.h>
+#include <string>
+
+#include "../../include/tel.h"
+#include "attn.h"
+#include "gemm.h"
+#include "rowops.h"
+
+using namespace tel;
+
+static thread_local std::string g_err;
+
+static tel_status fail(tel_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+static tel_status fail(tel_status s, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return s;
+}
+
+#define HIP_TRY(expr)                                                                         \
+    do {                                                                                      \
+        hipError_t e_ = (expr);                                                               \
+        if (e_ != hipSuccess) return fail(TEL_ERR_HIP, "%s: %s", #expr, hipGetErrorString(e_)); \
+    } while (0)
+
+namespace {
+
+// ------------------------------------------------------------------ workspace plan
+struct Buf {
+    size_t off = 0, bytes = 0;
+    bool in_saved = false;
+    bool used = false;
+};
+
+struct Plan {
+    // saved (forward -> backward)
+    Buf ln1_out, mu1, rs1, qkvh, ctx, lse, mu2, rs2, ln2_out, u, g;
+    Buf res1;     // Pre-LN x1 (fp32) | Post-LN z1 (fp32)
+    Buf x1e;      // Post-LN LN1 output, dtype
+    Buf x1f;      // Post-LN LN1 output, fp32 (residual of the FFN branch)
+    Buf res2;     // Post-LN z2 (fp32)
+    Buf ycopy;    // Post-LN output copy (invertible LN2 backward)
+    // scratch (backward)
+    Buf df, du, dgemm, dres, dz, dout, dvec, dqkv, dres2;
+    Buf part_ln, part_col, splitk;
+    size_t saved_bytes = 0, scratch_bytes = 0;
+};
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+}  // namespace
+
+struct tel_layer {
+    tel_config cfg;
+    int B, S, H, NH, d, F, T;
+    size_t esz;
+    Plan plan;
+    long pending_fwd;  // forwards with saved state not yet consumed by a backward
+    // optional benchmark hook: events recorded around one kernel's launches
+    int prof_kernel = -1;
+    hipEvent_t* prof_start = nullptr;
+    hipEvent_t* prof_stop = nullptr;
+    int prof_count = 0;
+    long prof_calls = 0;
+};
+
+// Run one launch; if it is the profiled kernel, bracket it with the next
+// pair of the caller's events (same stream, so the pair spans exactly it).
+#define TIMED(kid, expr)                                                                  \
+    do {                                                                                  \
+        const bool prof_ = L->prof_kernel == (kid) && L->prof_count > 0;                  \
+        const int pi_ = prof_ ? (int)(L->prof_calls % L->prof_count) : 0;                 \
+        if (prof_) HIP_TRY(hipEventRecord(L->prof_start[pi_], st));                       \
+        HIP_TRY(expr);                                                                    \
+        if (prof_) {                                                                      \
+            HIP_TRY(hipEventRecord(L->prof_stop[pi_], st));                               \
+            L->prof_calls++;                                                              \
+        }                                                                                 \
+    } while (0)
+
+static void place(Buf& b, size_t bytes, bool saved, size_t& sv, size_t& sc) {
+    b.bytes = bytes;
+    b.used = true;
+    b.in_saved = saved;
+    size_t& top = saved ? sv : sc;
+    b.off = top;
+    top = align_up(top + bytes);
+}
+
+static void make_plan(tel_layer* L) {
+    Plan& p = L->plan;
+    p = Plan();
+    const size_t T = L->T, H = L->H, F = L->F, e = L->esz, f4 = 4;
+    const size_t BNS = (size_t)L->B * L->NH * L->S;
+    const bool inv = L->cfg.normalize_invertible != 0;
+    const bool gck = L->cfg.gelu_checkpoint != 0;
+    size_t sv = 0, sc = 0;
+    if (L->cfg.pre_ln) {
+        place(p.ln1_out, T * H * e, true, sv, sc);
+        place(p.mu1, T * f4, true, sv, sc);
+        place(p.rs1, T * f4, true, sv, sc);
+        place(p.qkvh, 3 * T * H * e, true, sv, sc);
+        place(p.ctx, T * H * e, true, sv, sc);
+        place(p.lse, BNS * f4, true, sv, sc);
+        place(p.res1, T * H * f4, !inv, sv, sc);
+        place(p.mu2, T * f4, true, sv, sc);
+        place(p.rs2, T * f4, true, sv, sc);
+        place(p.ln2_out, T * H * e, true, sv, sc);
+        place(p.u, T * F * e, true, sv, sc);
+        place(p.g, T * F * e, !gck, sv, sc);
+    } else {
+        place(p.qkvh, 3 * T * H * e, true, sv, sc);
+        place(p.ctx, T * H * e, true, sv, sc);
+        place(p.lse, BNS * f4, true, sv, sc);
+        place(p.res1, T * H * f4, !inv, sv, sc);
+        place(p.mu1, T * f4, true, sv, sc);
+        place(p.rs1, T * f4, true, sv, sc);
+        place(p.x1e, T * H * e, true, sv, sc);
+        place(p.x1f, T * H * f4, inv, sv, sc);
+        place(p.u, T * F * e, true, sv, sc);
+        place(p.g, T * F * e, !gck, sv, sc);
+        place(p.res2, T * H * f4, !inv, sv, sc);
+        place(p.mu2, T * f4, true, sv, sc);
+        place(p.rs2, T * f4, true, sv, sc);
+        if (inv) place(p.ycopy, T * H * e, true, sv, sc);
+    }
+    const size_t fwd_scratch = sc;
+    // backward scratch starts again at 0: forward temporaries are dead by then
+    sc = 0;
+    place(p.df, T * H * e, false, sv, sc);
+    place(p.du, T * F * e, false, sv, sc);
+    place(p.dgemm, T * H * e, false, sv, sc);
+    place(p.dres, T * H * f4, false, sv, sc);
+    place(p.dres2, T * H * f4, false, sv, sc);
+    place(p.dz, T * H * e, false, sv, sc);
+    place(p.dout, T * H * e, false, sv, sc);
+    place(p.dvec, BNS * f4, false, sv, sc);
+    place(p.dqkv, 3 * T * H * e, false, sv, sc);
+    const size_t maxN = 3 * H > F ? 3 * H : F;
+    place(p.part_ln, 2 * (size_t)ln_backward_parts(L->T) * H * f4, false, sv, sc);
+    place(p.part_col, (size_t)colsum_parts(L->T) * maxN * f4, false, sv, sc);
+    // split-K partials of the four weight-gradient GEMMs
+    size_t sk = 0;
+    const int wg[4][2] = {{3 * L->H, L->H}, {L->H, L->H}, {L->F, L->H}, {L->H, L->F}};
+    for (auto& s : wg) {
+        GemmDesc gd;
+        gd.dtype = L->cfg.dtype;
+        gd.M = s[0]; gd.N = s[1]; gd.K = L->T;
+        gd.lda = s[0]; gd.ldb = s[1];
+        gd.a_kmajor = false; gd.b_kmajor = false;
+        gd.epi = EPI_STORE;
+        size_t n = gemm_splitk_elems(gd);
+        if (n > sk) sk = n;
+    }
+    if (sk) place(p.splitk, sk * f4, false, sv, sc);
+    p.saved_bytes = sv;
+    p.scratch_bytes = sc > fwd_scratch ? sc : fwd_scratch;
+}
+
+static tel_status validate_cfg(const tel_config* c) {
+    if (!c) return fail(TEL_ERR_INVALID_ARG, "config is NULL");
+    if (c->batch <= 0 || c->seq <= 0 || c->hidden <= 0 || c->heads <= 0)
+        return fail(TEL_ERR_INVALID_ARG, "batch, seq, hidden and heads must be positive");
+    const int F = c->ffn <= 0 ? 4 * c->hidden : c->ffn;
+    if (c->hidden % c->heads) return fail(TEL_ERR_INVALID_ARG, "hidden %d not divisible by heads %d", c->hidden, c->heads);
+    if (c->seq % 16 || c->hidden % 16 || F % 16)
+        return fail(TEL_ERR_INVALID_ARG, "seq, hidden and ffn must be multiples of 16");
+    const int d = c->hidden / c->heads;
+    if (d != 16 && d != 32 && d != 64 && d != 128) return fail(TEL_ERR_UNSUPPORTED, "head width %d not in {16,32,64,128}", d);
+    if (c->hidden > 4096) return fail(TEL_ERR_UNSUPPORTED, "hidden %d > 4096", c->hidden);
+    if (!(c->attn_dropout >= 0.0f && c->attn_dropout < 1.0f) || !(c->hidden_dropout >= 0.0f && c->hidden_dropout < 1.0f))
+        return fail(TEL_ERR_INVALID_ARG, "dropout probabilities must lie in [0,1)");
+    if (c->dtype != TEL_F32 && c->dtype != TEL_F16 && c->dtype != TEL_BF16)
+        return fail(TEL_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+    if (!(c->ln_eps >= 0.0f)) return fail(TEL_ERR_INVALID_ARG, "ln_eps must be >= 0");
+    const double T = (double)c->batch * c->seq;
+    if (T * (double)(3 * c->hidden > F ? 3 * c->hidden : F) >= 2147483647.0 ||
+        (double)c->batch * c->heads * c->seq * (double)c->seq >= 9.0e18)
+        return fail(TEL_ERR_UNSUPPORTED, "problem too large for 32-bit row indexing");
+    return TEL_OK;
+}
+
+static bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static Drop make_drop(const tel_layer* L, float p, uint32_t site, uint64_t step, int training) {
+    Drop d;
+    d.rng.key0 = (uint32_t)L->cfg.seed;
+    d.rng.key1 = (uint32_t)L->cfg.layer_id;
+    d.rng.site = site;
+    d.rng.step = (uint32_t)step;
+    d.thr = 0;
+    d.scale = 1.0f;
+    if (training && p > 0.0f) {
+        const double t = floor((double)p * 4294967296.0);
+        d.thr = (uint32_t)t;
+        d.scale = (float)(1.0 / (1.0 - (double)p));
+    }
+    return d;
+}
+
+extern "C" {
+
+const char* tel_last_error(void) { return g_err.c_str(); }
+
+tel_status tel_layer_create(const tel_config* cfg, tel_layer** out) {
+    if (!out) return fail(TEL_ERR_INVALID_ARG, "out is NULL");
+    *out = nullptr;
+    tel_status s = validate_cfg(cfg);
+    if (s != TEL_OK) return s;
+    tel_layer* L = new (std::nothrow) tel_layer();
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "out of host memory");
+    L->cfg = *cfg;
+    L->B = cfg->batch; L->S = cfg->seq; L->H = cfg->hidden; L->NH = cfg->heads;
+    L->d = cfg->hidden / cfg->heads;
+    L->F = cfg->ffn <= 0 ? 4 * cfg->hidden : cfg->ffn;
+    L->cfg.ffn = L->F;
+    L->T = L->B * L->S;
+    L->esz = cfg->dtype == TEL_F32 ? 4 : 2;
+    L->pending_fwd = 0;
+    make_plan(L);
+    *out = L;
+    g_err.clear();
+    return TEL_OK;
+}
+
+tel_status tel_layer_workspace_bytes(const tel_layer* L, size_t* saved_bytes, size_t* scratch_bytes) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    if (saved_bytes) *saved_bytes = L->plan.saved_bytes;
+    if (scratch_bytes) *scratch_bytes = L->plan.scratch_bytes;
+    return TEL_OK;
+}
+
+tel_status tel_layer_destroy(tel_layer* L) {
+    delete L;
+    return TEL_OK;
+}
+
+static tel_status check_params(const tel_params* p) {
+    if (!p) return fail(TEL_ERR_INVALID_ARG, "params is NULL");
+    const void* ptrs[12] = {p->w_qkv, p->b_qkv, p->w_o, p->b_o, p->ln1_g, p->ln1_b,
+                            p->w_1, p->b_1, p->w_2, p->b_2, p->ln2_g, p->ln2_b};
+    for (int i = 0; i < 12; ++i) {
+        if (!ptrs[i]) return fail(TEL_ERR_INVALID_ARG, "parameter %d is NULL", i);
+        if (!aligned(ptrs[i])) return fail(TEL_ERR_INVALID_ARG, "parameter %d not 16-byte aligned", i);
+    }
+    return TEL_OK;
+}
+
+static tel_status check_grads(const tel_grads* g) {
+    if (!g) return fail(TEL_ERR_INVALID_ARG, "grads is NULL");
+    void* ptrs[12] = {g->w_qkv, g->b_qkv, g->w_o, g->b_o, g->ln1_g, g->ln1_b,
+                      g->w_1, g->b_1, g->w_2, g->b_2, g->ln2_g, g->ln2_b};
+    for (int i = 0; i < 12; ++i) {
+        if (!ptrs[i]) return fail(TEL_ERR_INVALID_ARG, "gradient %d is NULL", i);
+        if (!aligned(ptrs[i])) return fail(TEL_ERR_INVALID_ARG, "gradient %d not 16-byte aligned", i);
+    }
+    return TEL_OK;
+}
+
+struct Bases {
+    void* saved;
+    void* scratch;
+    void* of(const Buf& b) const { return (char*)(b.in_saved ? saved : scratch) + b.off; }
+};
+
+tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
+                             int training, uint64_t step, void* y, void* saved, void* scratch,
+                             tel_stream_t stream) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    tel_status s = check_params(P);
+    if (s != TEL_OK) return s;
+    if (!x || !y || !scratch) return fail(TEL_ERR_INVALID_ARG, "x, y and scratch must be non-NULL");
+    if (!aligned(x) || !aligned(y) || !aligned(scratch) || (saved && !aligned(saved)) ||
+        (key_lengths && !aligned(key_lengths)))
+        return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+    if (x == y) return fail(TEL_ERR_INVALID_ARG, "y must not alias x");
+    hipStream_t st = (hipStream_t)stream;
+    const tel_config& c = L->cfg;
+    const Plan& p = L->plan;
+    const int T = L->T, H = L->H, F = L->F, dt = c.dtype;
+    // without a saved buffer every "saved" tensor lives in a private region of scratch
+    // placed after the scratch plan: callers that pass saved = NULL must size scratch
+    // as saved_bytes + scratch_bytes.
+    void* sv = saved ? saved : (char*)scratch + align_up(p.scratch_bytes);
+    Bases bs{sv, scratch};
+    const Drop d0 = make_drop(L, c.attn_dropout, 0, step, training);
+    const Drop d1 = make_drop(L, c.hidden_dropout, 1, step, training);
+    const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
+
+    AttnArgs aa{};
+    aa.dtype = dt; aa.B = L->B; aa.S = L->S; aa.NH = L->NH; aa.d = L->d;
+    aa.qkvh = bs.of(p.qkvh); aa.len = key_lengths; aa.drop = d0;
+    aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
+
+    auto proj = [&](const void* A, const void* W, int N, int K, int epi) {
+        GemmDesc g;
+        g.dtype = dt; g.M = T; g.N = N; g.K = K;
+        g.A = A; g.lda = K; g.a_kmajor = true;
+        g.B = W; g.ldb = K; g.b_kmajor = true;
+        g.epi = epi;
+        return g;
+    };
+
+    if (c.pre_ln) {
+        LnFwdArgs l1{dt, T, H, c.ln_eps, x, 0, P->ln1_g, P->ln1_b, bs.of(p.ln1_out), nullptr, nullptr,
+                     (float*)bs.of(p.mu1), (float*)bs.of(p.rs1)};
+        TIMED(TEL_K_LN1_FWD, ln_forward(l1, st));
+        GemmDesc g = proj(bs.of(p.ln1_out), P->w_qkv, 3 * H, H, EPI_QKV);
+        g.ea.out = bs.of(p.qkvh); g.ea.bias = P->b_qkv;
+        g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
+        TIMED(TEL_K_QKV_FWD, gemm_launch(g, st));
+        TIMED(TEL_K_ATTN_FWD, attn_forward(aa, st));
+        g = proj(bs.of(p.ctx), P->w_o, H, H, EPI_BIAS_DROP_RES);
+        g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_o;
+        g.ea.res = x; g.ea.res_f32 = 0; g.ea.drop = d1;
+        TIMED(TEL_K_OUT_FWD, gemm_launch(g, st));
+        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res1), 1, P->ln2_g, P->ln2_b, bs.of(p.ln2_out), nullptr, nullptr,
+                     (float*)bs.of(p.mu2), (float*)bs.of(p.rs2)};
+        TIMED(TEL_K_LN2_FWD, ln_forward(l2, st));
+        g = proj(bs.of(p.ln2_out), P->w_1, F, H, EPI_BIAS_GELU);
+        g.ea.out = bs.of(p.u); g.ea.ldo = F; g.ea.bias = P->b_1; g.ea.out2 = bs.of(p.g);
+        TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
+        g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
+        g.ea.out = y; g.ea.ldo = H; g.ea.out_f32 = 0; g.ea.bias = P->b_2;
+        g.ea.res = bs.of(p.res1); g.ea.res_f32 = 1; g.ea.drop = d2;
+        TIMED(TEL_K_FFN2_FWD, gemm_launch(g, st));
+    } else {
+        GemmDesc g = proj(x, P->w_qkv, 3 * H, H, EPI_QKV);
+        g.ea.out = bs.of(p.qkvh); g.ea.bias = P->b_qkv;
+        g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
+        TIMED(TEL_K_QKV_FWD, gemm_launch(g, st));
+        TIMED(TEL_K_ATTN_FWD, attn_forward(aa, st));
+        g = proj(bs.of(p.ctx), P->w_o, H, H, EPI_BIAS_DROP_RES);
+        g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_o;
+        g.ea.res = x; g.ea.res_f32 = 0; g.ea.drop = d1;
+        TIMED(TEL_K_OUT_FWD, gemm_launch(g, st));
+        LnFwdArgs l1{dt, T, H, c.ln_eps, bs.of(p.res1), 1, P->ln1_g, P->ln1_b, bs.of(p.x1e),
+                     (float*)bs.of(p.x1f), nullptr, (float*)bs.of(p.mu1), (float*)bs.of(p.rs1)};
+        TIMED(TEL_K_LN1_FWD, ln_forward(l1, st));
+        g = proj(bs.of(p.x1e), P->w_1, F, H, EPI_BIAS_GELU);
+        g.ea.out = bs.of(p.u); g.ea.ldo = F; g.ea.bias = P->b_1; g.ea.out2 = bs.of(p.g);
+        TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
+        g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
+        g.ea.out = bs.of(p.res2); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_2;
+        g.ea.res = bs.of(p.x1f); g.ea.res_f32 = 1; g.ea.drop = d2;
+        TIMED(TEL_K_FFN2_FWD, gemm_launch(g, st));
+        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res2), 1, P->ln2_g, P->ln2_b, y, nullptr,
+                     p.ycopy.used ? bs.of(p.ycopy) : nullptr, (float*)bs.of(p.mu2), (float*)bs.of(p.rs2)};
+        TIMED(TEL_K_LN2_FWD, ln_forward(l2, st));
+    }
+    if (saved) L->pending_fwd++;
+    g_err.clear();
+    return TEL_OK;
+}
+
+tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
+                              int training, uint64_t step, const void* dy, const void* saved, void* scratch,
+                              void* dx, const tel_grads* G, tel_stream_t stream) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    tel_status s = check_params(P);
+    if (s != TEL_OK) return s;
+    s = check_grads(G);
+    if (s != TEL_OK) return s;
+    const tel_config& c = L->cfg;
+    const bool need_x = !(c.pre_ln && c.normalize_invertible);
+    if (!dy || !saved || !scratch || !dx || (need_x && !x))
+        return fail(TEL_ERR_INVALID_ARG, "dy, saved, scratch, dx (and x unless Pre-LN invertible) must be non-NULL");
+    if (!aligned(dy) || !aligned(saved) || !aligned(scratch) || !aligned(dx) || (x && !aligned(x)) ||
+        (key_lengths && !aligned(key_lengths)))
+        return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+    if (L->pending_fwd <= 0) return fail(TEL_ERR_STATE, "backward called without a preceding forward with saved state");
+    hipStream_t st = (hipStream_t)stream;
+    const Plan& p = L->plan;
+    const int T = L->T, H = L->H, F = L->F, dt = c.dtype;
+    Bases bs{const_cast<void*>(saved), scratch};
+    const Drop d0 = make_drop(L, c.attn_dropout, 0, step, training);
+    const Drop d1 = make_drop(L, c.hidden_dropout, 1, step, training);
+    const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
+    const bool inv = c.normalize_invertible != 0;
+    const bool gck = c.gelu_checkpoint != 0;
+    float* part_ln_g = (float*)bs.of(p.part_ln);
+    const int lnP = ln_backward_parts(T);
+    float* part_ln_b = part_ln_g + (size_t)lnP * H;
+    float* part_col = (float*)bs.of(p.part_col);
+    const int colP = colsum_parts(T);
+    float* skws = p.splitk.used ? (float*)bs.of(p.splitk) : nullptr;
+    const size_t skn = p.splitk.used ? p.splitk.bytes / 4 : 0;
+
+    // dX[T][in] = dY[T][out] . W[out][in]
+    auto dgrad = [&](const void* dY, const void* W, int out, int in, int epi) {
+        GemmDesc g;
+        g.dtype = dt; g.M = T; g.N = in; g.K = out;
+        g.A = dY; g.lda = out; g.a_kmajor = true;
+        g.B = W; g.ldb = in; g.b_kmajor = false;
+        g.epi = epi;
+        return g;
+    };
+    // dW[out][in] = dY^T . X, written to the caller's gradient (dtype)
+    auto wgrad = [&](const void* dY, const void* X, int out, int in, void* dW, bool gelu) {
+        GemmDesc g;
+        g.dtype = dt; g.M = out; g.N = in; g.K = T;
+        g.A = dY; g.lda = out; g.a_kmajor = false;
+        g.B = X; g.ldb = in; g.b_kmajor = false;
+        g.b_gelu = gelu;
+        g.epi = EPI_STORE;
+        g.ea.out = dW; g.ea.ldo = in;
+        g.splitk_ws = skws; g.splitk_ws_elems = skn;
+        return gemm_launch(g, st);
+    };
+    auto bias_grad = [&](const void* dY, int N, void* out) -> hipError_t {
+        hipError_t e = colsum_partial(dt, dY, T, N, part_col, st);
+        if (e != hipSuccess) return e;
+        return colsum_finalize(dt, part_col, colP, N, out, st);
+    };
+    auto ln_grads = [&](void* gg, void* gb) -> hipError_t {
+        hipError_t e = colsum_finalize(dt, part_ln_g, lnP, H, gg, st);
+        if (e != hipSuccess) return e;
+        return colsum_finalize(dt, part_ln_b, lnP, H, gb, st);
+    };
+
+    AttnArgs aa{};
+    aa.dtype = dt; aa.B = L->B; aa.S = L->S; aa.NH = L->NH; aa.d = L->d;
+    aa.qkvh = bs.of(p.qkvh); aa.len = key_lengths; aa.drop = d0;
+    aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
+    aa.dout = bs.of(p.dout); aa.dvec = (float*)bs.of(p.dvec); aa.dqkv = bs.of(p.dqkv);
+
+    const void* g_src = gck ? bs.of(p.u) : bs.of(p.g);  // FFN2 input (or GELU input to recompute it from)
+
+    if (c.pre_ln) {
+        // y = x1 + drop2(g W2^T + b2)
+        HIP_TRY(dropout_apply(dt, dy, bs.of(p.df), (size_t)T * H, d2, st));
+        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, EPI_GELU_BWD);
+        g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
+        TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck));
+        HIP_TRY(bias_grad(bs.of(p.df), H, G->b_2));
+        g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
+        g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
+        TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_FFN1_WGRAD, wgrad(bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, false));
+        HIP_TRY(bias_grad(bs.of(p.du), F, G->b_1));
+        // x1 -> LN2: dx1 = dy + LN2'(da2); dz = drop1(dx1)
+        LnBwdArgs lb{};
+        lb.dtype = dt; lb.T = T; lb.H = H;
+        lb.dout = bs.of(p.dgemm);
+        lb.src = inv ? bs.of(p.ln2_out) : bs.of(p.res1); lb.src_f32 = inv ? 0 : 1; lb.from_output = inv;
+        lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
+        lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
+        lb.res = dy; lb.res_f32 = 0;
+        lb.out = bs.of(p.dres); lb.out_f32 = 1;
+        lb.drop_out = bs.of(p.dz); lb.drop = d1;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
+        HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
+        // out-projection
+        g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
+        g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
+        TIMED(TEL_K_OUT_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false));
+        HIP_TRY(bias_grad(bs.of(p.dz), H, G->b_o));
+        TIMED(TEL_K_ATTN_BWD, attn_backward(aa, st));
+        // QKV projection
+        g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_STORE);
+        g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
+        TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, false));
+        HIP_TRY(bias_grad(bs.of(p.dqkv), 3 * H, G->b_qkv));
+        // x -> LN1: dx = dx1 + LN1'(da1)
+        lb = LnBwdArgs{};
+        lb.dtype = dt; lb.T = T; lb.H = H;
+        lb.dout = bs.of(p.dgemm);
+        lb.src = inv ? bs.of(p.ln1_out) : x; lb.src_f32 = 0; lb.from_output = inv;
+        lb.mu = (const float*)bs.of(p.mu1); lb.rstd = (const float*)bs.of(p.rs1);
+        lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
+        lb.res = bs.of(p.dres); lb.res_f32 = 1;
+        lb.out = dx; lb.out_f32 = 0;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
+        HIP_TRY(ln_grads(G->ln1_g, G->ln1_b));
+    } else {
+        // y = LN2(z2): dz2 = LN2'(dy); df = drop2(dz2)
+        LnBwdArgs lb{};
+        lb.dtype = dt; lb.T = T; lb.H = H;
+        lb.dout = dy;
+        lb.src = inv ? bs.of(p.ycopy) : bs.of(p.res2); lb.src_f32 = inv ? 0 : 1; lb.from_output = inv;
+        lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
+        lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
+        lb.out = bs.of(p.dres2); lb.out_f32 = 1;
+        lb.drop_out = bs.of(p.df); lb.drop = d2;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
+        HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
+        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, EPI_GELU_BWD);
+        g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
+        TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck));
+        HIP_TRY(bias_grad(bs.of(p.df), H, G->b_2));
+        g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
+        g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
+        TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_FFN1_WGRAD, wgrad(bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, false));
+        HIP_TRY(bias_grad(bs.of(p.du), F, G->b_1));
+        // x1 = LN1(z1): dz1 = LN1'(dgemm + dz2); dz = drop1(dz1)
+        lb = LnBwdArgs{};
+        lb.dtype = dt; lb.T = T; lb.H = H;
+        lb.dout = bs.of(p.dgemm); lb.dout_add = (const float*)bs.of(p.dres2);
+        lb.src = inv ? bs.of(p.x1f) : bs.of(p.res1); lb.src_f32 = 1; lb.from_output = inv;
+        lb.mu = (const float*)bs.of(p.mu1); lb.rstd = (const float*)bs.of(p.rs1);
+        lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
+        lb.out = bs.of(p.dres); lb.out_f32 = 1;
+        lb.drop_out = bs.of(p.dz); lb.drop = d1;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
+        HIP_TRY(ln_grads(G->ln1_g, G->ln1_b));
+        g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
+        g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
+        TIMED(TEL_K_OUT_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false));
+        HIP_TRY(bias_grad(bs.of(p.dz), H, G->b_o));
+        TIMED(TEL_K_ATTN_BWD, attn_backward(aa, st));
+        // dx = dz1 + dqkv W_qkv
+        g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_ADD_RES);
+        g.ea.out = dx; g.ea.ldo = H; g.ea.res = bs.of(p.dres);
+        TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
+        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), x, 3 * H, H, G->w_qkv, false));
+        HIP_TRY(bias_grad(bs.of(p.dqkv), 3 * H, G->b_qkv));
+    }
+    L->pending_fwd--;
+    g_err.clear();
+    return TEL_OK;
+}
+
+tel_status tel_debug_kernel_events(tel_layer* L, int kernel_id, void** start_events, void** stop_events,
+                                   int count) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    if (kernel_id < 0 || count <= 0) {
+        L->prof_kernel = -1;
+        L->prof_count = 0;
+        return TEL_OK;
+    }
+    if (!start_events || !stop_events) return fail(TEL_ERR_INVALID_ARG, "event arrays are NULL");
+    L->prof_kernel = kernel_id;
+    L->prof_start = reinterpret_cast<hipEvent_t*>(start_events);
+    L->prof_stop = reinterpret_cast<hipEvent_t*>(stop_events);
+    L->prof_count = count;
+    L->prof_calls = 0;
+    return TEL_OK;
+}
+
+tel_status tel_debug_dropout_mask(const tel_layer* L, int site, uint64_t step, uint8_t* out_dev, tel_stream_t stream) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    if (!out_dev) return fail(TEL_ERR_INVALID_ARG, "out is NULL");
+    if (site < 0 || site > 2) return fail(TEL_ERR_INVALID_ARG, "site must be 0, 1 or 2");
+    const float pr = site == 0 ? L->cfg.attn_dropout : L->cfg.hidden_dropout;
+    const Drop d = make_drop(L, pr, (uint32_t)site, step, 1);
+    const size_t n = site == 0 ? (size_t)L->B * L->NH * L->S * L->S : (size_t)L->T * L->H;
+    HIP_TRY(dropout_mask_dump(d, out_dev, n, (hipStream_t)stream));
+    return TEL_OK;
+}
+
+double tel_pld_theta(double t, double theta_bar, double gamma) {
+    return (1.0 - theta_bar) * exp(-gamma * t) + theta_bar;
+}
+
+int32_t tel_pld_keep(uint64_t seed, int32_t layer_id, uint64_t step, double theta) {
+    // Philox4x32-10 on the host, site 3, element 0
+    uint32_t c0 = 0, c1 = 0, c2 = 3u, c3 = (uint32_t)step;
+    uint32_t k0 = (uint32_t)seed, k1 = (uint32_t)layer_id;
+    for (int r = 0; r < 10; ++r) {
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p2 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t n0 = (uint32_t)(p2 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p2;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    const double thr = floor(theta * 4294967296.0);
+    return (double)c0 < thr ? 1 : 0;
+}
+
+}  // extern "C"

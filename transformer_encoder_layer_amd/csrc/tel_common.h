@@ -1,0 +1,129 @@
+// tel_common.h -- device-side helpers shared by the gfx950 kernels of the
+// fused encoder layer: storage types, conversions, vector access, the
+// counter-based dropout generator and the exact GELU.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tel {
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- types
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(f16 x) { return (float)x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+
+template <typename T> __device__ __forceinline__ T from_f(float x);
+template <> __device__ __forceinline__ float from_f<float>(float x) { return x; }
+template <> __device__ __forceinline__ f16 from_f<f16>(float x) { return (f16)x; }
+template <> __device__ __forceinline__ bf16 from_f<bf16>(float x) { return (bf16)x; }
+
+// round a float through storage type T and back (value the stored tensor holds)
+template <typename T> __device__ __forceinline__ float round_through(float x) { return to_f(from_f<T>(x)); }
+
+// 4 consecutive elements: load as float4, store from float4.
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+    static __device__ __forceinline__ void load(const float* p, float v[4]) {
+        float4 q = *reinterpret_cast<const float4*>(p);
+        v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+    }
+    static __device__ __forceinline__ void store(float* p, const float v[4]) {
+        *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+template <> struct Vec4<f16> {
+    static __device__ __forceinline__ void load(const f16* p, float v[4]) {
+        f16x4 q = *reinterpret_cast<const f16x4*>(p);
+        v[0] = (float)q[0]; v[1] = (float)q[1]; v[2] = (float)q[2]; v[3] = (float)q[3];
+    }
+    static __device__ __forceinline__ void store(f16* p, const float v[4]) {
+        f16x4 q = {(f16)v[0], (f16)v[1], (f16)v[2], (f16)v[3]};
+        *reinterpret_cast<f16x4*>(p) = q;
+    }
+};
+template <> struct Vec4<bf16> {
+    static __device__ __forceinline__ void load(const bf16* p, float v[4]) {
+        bf16x4 q = *reinterpret_cast<const bf16x4*>(p);
+        v[0] = (float)q[0]; v[1] = (float)q[1]; v[2] = (float)q[2]; v[3] = (float)q[3];
+    }
+    static __device__ __forceinline__ void store(bf16* p, const float v[4]) {
+        bf16x4 q = {(bf16)v[0], (bf16)v[1], (bf16)v[2], (bf16)v[3]};
+        *reinterpret_cast<bf16x4*>(p) = q;
+    }
+};
+
+// ---------------------------------------------------------------- RNG
+// Philox4x32 with 10 rounds (Salmon et al., SC'11): per round the counter
+// words 0 and 2 are multiplied by two odd constants; the high halves are
+// mixed with the other two words and the key, and the key advances by two
+// Weyl increments between rounds.
+struct Rng {
+    uint32_t key0, key1;  // seed mod 2^32, layer id
+    uint32_t site, step;  // counter words 2 and 3
+};
+
+__device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int round = 0; round < 10; ++round) {
+        const uint32_t a0 = 0xD2511F53u * c0;
+        const uint32_t b0 = __umulhi(0xD2511F53u, c0);
+        const uint32_t a2 = 0xCD9E8D57u * c2;
+        const uint32_t b2 = __umulhi(0xCD9E8D57u, c2);
+        const uint32_t n0 = b2 ^ c1 ^ k0;
+        const uint32_t n2 = b0 ^ c3 ^ k1;
+        c0 = n0; c1 = a2; c2 = n2; c3 = a0;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+    return make_uint4(c0, c1, c2, c3);
+}
+
+// Keep bits of the four elements 4g .. 4g+3 of one dropout site: bit i set
+// iff element 4g+i is kept, i.e. its 32-bit word >= thr.
+__device__ __forceinline__ uint32_t keep4(const Rng& r, uint64_t g, uint32_t thr) {
+    const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), r.site, r.step, r.key0, r.key1);
+    return (uint32_t)(w.x >= thr) | ((uint32_t)(w.y >= thr) << 1) | ((uint32_t)(w.z >= thr) << 2) |
+           ((uint32_t)(w.w >= thr) << 3);
+}
+
+// Dropout description passed to kernels: thr == 0 means "no dropout".
+struct Drop {
+    Rng rng;
+    uint32_t thr;
+    float scale;  // 1/(1-p) rounded to fp32
+};
+
+// ---------------------------------------------------------------- GELU
+// Exact GELU u*Phi(u) and its derivative Phi(u) + u*phi(u), evaluated with
+// explicit roundings so that every kernel that recomputes them produces the
+// same bits.
+__device__ __forceinline__ float gelu_f(float u) {
+    const float cdf = __fmul_rn(0.5f, __fadd_rn(1.0f, erff(__fmul_rn(u, 0.70710678118654752f))));
+    return __fmul_rn(u, cdf);
+}
+__device__ __forceinline__ float gelu_grad_f(float u) {
+    const float cdf = __fmul_rn(0.5f, __fadd_rn(1.0f, erff(__fmul_rn(u, 0.70710678118654752f))));
+    const float pdf = __fmul_rn(0.39894228040143268f, __expf(__fmul_rn(-0.5f, __fmul_rn(u, u))));
+    return __fadd_rn(cdf, __fmul_rn(u, pdf));
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+}  // namespace tel

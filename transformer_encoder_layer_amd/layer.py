@@ -1,0 +1,161 @@
+"""torch.nn front end of the fused encoder layer.
+
+``EncoderLayer`` holds the twelve parameters (nn.Linear layout) and calls the
+C ABI through ``binding``: forward and backward each run entirely in the HIP
+library on the current torch stream.  torch provides device memory (the
+per-forward ``saved`` buffer, a ``scratch`` buffer shared by all layers on a
+device) and the stream; nothing of the layer is computed in torch.
+
+``EncoderStack`` stacks layers with distinct layer ids (as the DeepSpeed
+guide's deepcopy of one layer spec does) and implements progressive layer
+dropping: at step t every layer is kept with probability
+theta(t) = (1 - theta_bar) exp(-gamma t) + theta_bar (PLD page, "core
+mechanism"); the keep decision is the counter-based gate of tel_pld_keep, so
+every process derives the same gates without communication.  A dropped layer
+is the identity in forward and backward.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+from . import binding as B
+
+_DTYPES = {torch.float32: B.TEL_F32, torch.float16: B.TEL_F16, torch.bfloat16: B.TEL_BF16}
+
+
+@dataclass
+class LayerConfig:
+    batch: int
+    seq: int
+    hidden: int
+    heads: int
+    ffn: int = 0
+    attn_dropout: float = 0.1
+    hidden_dropout: float = 0.1
+    pre_ln: bool = True
+    seed: int = 1234
+    layer_id: int = 0
+    dtype: torch.dtype = torch.float16
+    ln_eps: float = 1e-12
+    attn_dropout_checkpoint: bool = False
+    normalize_invertible: bool = False
+    gelu_checkpoint: bool = False
+
+    def to_c(self) -> B.tel_config:
+        return B.tel_config(self.batch, self.seq, self.hidden, self.heads, self.ffn, self.attn_dropout,
+                            self.hidden_dropout, int(self.pre_ln), self.seed, self.layer_id,
+                            _DTYPES[self.dtype], self.ln_eps, int(self.attn_dropout_checkpoint),
+                            int(self.normalize_invertible), int(self.gelu_checkpoint))
+
+
+_scratch = {}
+
+
+def scratch_buffer(device: torch.device, nbytes: int) -> torch.Tensor:
+    """A uint8 device buffer of at least nbytes, shared by every layer on the device."""
+    key = (device.type, device.index)
+    buf = _scratch.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _scratch[key] = buf
+    return buf
+
+
+def _round256(n: int) -> int:
+    return (n + 255) // 256 * 256
+
+
+class _LayerFn(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, x, lengths, step, layer, *params):
+        dev = x.device
+        need_grad = torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in params))
+        x = x.contiguous()
+        y = torch.empty_like(x)
+        saved = torch.empty(layer.saved_bytes, dtype=torch.uint8, device=dev) if need_grad else None
+        scratch = scratch_buffer(dev, layer.scratch_bytes if need_grad
+                                 else _round256(layer.scratch_bytes) + layer.saved_bytes)
+        P = B.make_params(dict(zip(B.PARAM_NAMES, params)))
+        training = int(layer.training)
+        B.tel_layer_forward(layer.handle, P, x, lengths, training, step, y, saved, scratch)
+        ctx.layer = layer
+        ctx.step = step
+        ctx.training_flag = training
+        ctx.saved_buf = saved
+        ctx.save_for_backward(x, *params)
+        ctx.lengths = lengths
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        layer = ctx.layer
+        x, *params = ctx.saved_tensors
+        dy = dy.contiguous()
+        dx = torch.empty_like(x)
+        grads = [torch.empty_like(p) for p in params]
+        scratch = scratch_buffer(x.device, layer.scratch_bytes)
+        B.tel_layer_backward(layer.handle, B.make_params(dict(zip(B.PARAM_NAMES, params))), x, ctx.lengths,
+                             ctx.training_flag, ctx.step, dy, ctx.saved_buf, scratch, dx,
+                             B.make_grads(dict(zip(B.PARAM_NAMES, grads))))
+        ctx.saved_buf = None
+        return (dx, None, None, None, *grads)
+
+
+class EncoderLayer(torch.nn.Module):
+    def __init__(self, cfg: LayerConfig, device="cuda"):
+        super().__init__()
+        self.cfg = cfg
+        H = cfg.hidden
+        F = cfg.ffn if cfg.ffn > 0 else 4 * H
+        self.ffn = F
+        self.handle = B.tel_layer_create(cfg.to_c())
+        self.saved_bytes, self.scratch_bytes = B.tel_layer_workspace_bytes(self.handle)
+        shapes = {"w_qkv": (3 * H, H), "b_qkv": (3 * H,), "w_o": (H, H), "b_o": (H,), "ln1_g": (H,),
+                  "ln1_b": (H,), "w_1": (F, H), "b_1": (F,), "w_2": (H, F), "b_2": (H,), "ln2_g": (H,),
+                  "ln2_b": (H,)}
+        for n in B.PARAM_NAMES:
+            init = torch.ones if n.endswith("_g") else torch.zeros
+            self.register_parameter(n, torch.nn.Parameter(init(shapes[n], dtype=cfg.dtype, device=device)))
+
+    def params(self):
+        return [getattr(self, n) for n in B.PARAM_NAMES]
+
+    def forward(self, x: torch.Tensor, key_lengths: Optional[torch.Tensor] = None, step: int = 0):
+        return _LayerFn.apply(x, key_lengths, int(step), self, *self.params())
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h:
+            try:
+                B.tel_layer_destroy(h)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def pld_theta(step: int, theta_bar: float = 0.5, gamma: float = 0.001) -> float:
+    return B.tel_pld_theta(step, theta_bar, gamma)
+
+
+class EncoderStack(torch.nn.Module):
+    def __init__(self, cfg: LayerConfig, layers: int, device="cuda", pld: Optional[tuple] = None):
+        super().__init__()
+        self.layers = torch.nn.ModuleList(
+            [EncoderLayer(LayerConfig(**{**cfg.__dict__, "layer_id": i}), device) for i in range(layers)])
+        self.pld = pld  # (theta_bar, gamma) or None
+        self.seed = cfg.seed
+
+    def gates(self, step: int):
+        if self.pld is None or not self.training:
+            return [True] * len(self.layers)
+        theta = pld_theta(step, *self.pld)
+        return [B.tel_pld_keep(self.seed, i, step, theta) for i in range(len(self.layers))]
+
+    def forward(self, x, key_lengths=None, step: int = 0):
+        for layer, keep in zip(self.layers, self.gates(step)):
+            if keep:
+                x = layer(x, key_lengths, step)
+        return x
