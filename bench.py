@@ -1,0 +1,253 @@
+"""Throughput of the fused encoder layer, forward + backward, on one MI355X.
+
+Default workload: the BERT-Large layer (batch 64, sequence 128, hidden 1024,
+16 heads, FFN 4096, fp16 storage / fp32 accumulation, Pre-LN, dropout 0.1)
+as a stack of 24 layers with distinct layer ids.  One step = forward through
+all 24 layers, then backward through all 24, every kernel in libtel.so;
+inputs, weights and workspaces are resident in HBM before timing starts.
+
+Reported: value = tokens/s of one layer's forward+backward (stack tokens/s
+times the number of layers run), model TFLOP/s and its fraction of the dense
+fp16 MFMA peak, the roofline of the dominant kernel (timed live with HIP
+events around each of its launches inside the timed steps), and the fp64
+CPU oracle's throughput on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_TFLOPS = {"f16": 2500.0, "bf16": 2500.0, "f32": 157.3}  # MI355X dense, published
+PEAK_HBM_GBS = 8000.0
+
+
+def model_flops(w) -> float:
+    """fwd = 2T(4H^2 + 2HF) + 4 B S^2 H; fwd+bwd = 3 x fwd (recompute not counted)."""
+    T, H, F = w.batch * w.seq, w.hidden, w.ffn
+    fwd = 2.0 * T * (4 * H * H + 2 * H * F) + 4.0 * w.batch * w.seq * w.seq * H
+    return 3.0 * fwd
+
+
+class Hip:
+    """The few HIP runtime calls the benchmark needs for events."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self) -> int:
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def destroy(self, e):
+        self.h.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(w, n_seq: int):
+    """Oracle forward + backward of n_seq sequences of the workload (fp64, host cores)."""
+    import oracle
+    from transformer_encoder_layer_amd import synthetic as syn
+    sub = w.with_(batch=n_seq)
+    p = syn.layer_params(w, 0)
+    x = syn.layer_input(w)[: n_seq * w.seq]
+    dy = syn.upstream_grad(w)[: n_seq * w.seq]
+    lengths = syn.seq_lengths(w)[:n_seq]
+    cfg = oracle.LayerCfg(n_seq, w.seq, w.hidden, w.heads, w.ffn, pre_ln=w.pre_ln, training=True,
+                          attn_p=float(np.float32(w.attn_p)), hidden_p=float(np.float32(w.hidden_p)),
+                          seed=w.seed, step=0, layer_id=0)
+    oracle.lib()
+    t0 = time.perf_counter()
+    oracle.layer_forward(cfg, p, x, lengths)
+    oracle.layer_backward(cfg, p, x, lengths, dy, ln_invertible=w.normalize_invertible)
+    dt = time.perf_counter() - t0
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": n_seq * w.seq / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_seq} of {w.batch} sequences ({n_seq * w.seq} tokens), one layer forward+backward, "
+                      f"fp64, {dt:.2f} s", "seconds": dt,
+            "model_gflops": model_flops(sub) / dt / 1e9}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="bert_large")
+    ap.add_argument("--layers", type=int, default=0, help="override the stack depth")
+    ap.add_argument("--kernel", default="ffn1_fwd", help="kernel timed for the roofline")
+    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer's data-parallel sharding is described in DESIGN.md, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from transformer_encoder_layer_amd import binding as B
+    from transformer_encoder_layer_amd import synthetic as syn
+    from transformer_encoder_layer_amd.layer import LayerConfig
+
+    w = syn.WORKLOADS[args.workload]
+    n_layers = args.layers or w.layers
+    dev = torch.device("cuda:0")
+    dt = syn.torch_dtype(w.dtype)
+    T, H = w.tokens, w.hidden
+
+    # ---- layers (distinct ids, weights from the seeded generator)
+    handles, params, grads, saved = [], [], [], []
+    for l in range(n_layers):
+        cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, float(np.float32(w.attn_p)),
+                          float(np.float32(w.hidden_p)), w.pre_ln, w.seed, l, dt, 1e-12,
+                          w.attn_dropout_checkpoint, w.normalize_invertible, w.gelu_checkpoint)
+        h = B.tel_layer_create(cfg.to_c())
+        handles.append(h)
+        p64 = syn.layer_params(w, l)
+        P = {n: syn.to_storage(p64[n], w.dtype).to(dev) for n in B.PARAM_NAMES}
+        params.append(P)
+        grads.append({n: torch.empty_like(P[n]) for n in B.PARAM_NAMES})
+        sv, sc = B.tel_layer_workspace_bytes(h)
+        saved.append(torch.empty(sv, dtype=torch.uint8, device=dev))
+    scratch = torch.empty(max(B.tel_layer_workspace_bytes(h)[1] for h in handles), dtype=torch.uint8,
+                          device=dev)
+    cparams = [B.make_params(P) for P in params]
+    cgrads = [B.make_grads(G) for G in grads]
+    x0 = syn.to_storage(syn.layer_input(w), w.dtype).to(dev)
+    dy_top = syn.to_storage(syn.upstream_grad(w), w.dtype).to(dev)
+    lengths = torch.from_numpy(syn.seq_lengths(w)).to(dev) if w.lengths is not None else None
+    acts = [x0] + [torch.empty_like(x0) for _ in range(n_layers)]
+    dgrads = [torch.empty_like(x0) for _ in range(n_layers)] + [dy_top]
+
+    # progressive layer dropping: gates of this step (memory-saving stack)
+    step_id = w.pld[2] if w.pld else 0
+    if w.pld:
+        theta = B.tel_pld_theta(step_id, w.pld[0], w.pld[1])
+        gates = [B.tel_pld_keep(w.seed, l, step_id, theta) for l in range(n_layers)]
+    else:
+        theta, gates = 1.0, [True] * n_layers
+    run = [l for l in range(n_layers) if gates[l]]
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def step():
+        # skipped layers are the identity: their input buffer is passed on unchanged
+        cur = x0
+        inputs = {}
+        for l in run:
+            inputs[l] = cur
+            B.tel_layer_forward(handles[l], cparams[l], cur, lengths, 1, step_id, acts[l + 1], saved[l], scratch,
+                                stream)
+            cur = acts[l + 1]
+        g = dy_top
+        for l in reversed(run):
+            B.tel_layer_backward(handles[l], cparams[l], inputs[l], lengths, 1, step_id, g, saved[l], scratch,
+                                 dgrads[l], cgrads[l], stream)
+            g = dgrads[l]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # live per-kernel timing of the dominant kernel during the timed steps
+    hip = Hip()
+    kid = B.KERNELS[args.kernel]
+    ev = {l: ([hip.event() for _ in range(args.steps)], [hip.event() for _ in range(args.steps)]) for l in run}
+    keep_alive = [B.tel_debug_kernel_events(handles[l], kid, ev[l][0], ev[l][1]) for l in run]
+    t_start, t_stop = hip.event(), hip.event()
+
+    torch.cuda.synchronize()
+    hip.h.hipEventRecord(ctypes.c_void_p(t_start), ctypes.c_void_p(stream))
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    hip.h.hipEventRecord(ctypes.c_void_p(t_stop), ctypes.c_void_p(stream))
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = hip.elapsed_ms(t_start, t_stop)
+    for l in run:
+        B.tel_debug_kernel_events(handles[l], -1, None, None)
+    del keep_alive
+    kern_ms = [hip.elapsed_ms(a, b) for l in run for a, b in zip(*ev[l])]
+    kern_avg_ms = float(np.mean(kern_ms))
+
+    ms_per_step = total_ms / args.steps
+    n_run = len(run)
+    layer_tokens_per_s = T * n_run / (ms_per_step / 1e3)
+    tflops = model_flops(w) * n_run / (ms_per_step / 1e3) / 1e12
+    peak = PEAK_MFMA_TFLOPS[w.dtype]
+
+    # roofline of the timed kernel (algorithmic work per launch)
+    F = w.ffn
+    gemm_flops = {"qkv_fwd": 2.0 * T * H * 3 * H, "out_fwd": 2.0 * T * H * H, "ffn1_fwd": 2.0 * T * H * F,
+                  "ffn2_fwd": 2.0 * T * F * H, "ffn2_dgrad": 2.0 * T * H * F, "ffn2_wgrad": 2.0 * T * H * F,
+                  "ffn1_dgrad": 2.0 * T * F * H, "ffn1_wgrad": 2.0 * T * F * H, "out_dgrad": 2.0 * T * H * H,
+                  "out_wgrad": 2.0 * T * H * H, "qkv_dgrad": 2.0 * T * 3 * H * H, "qkv_wgrad": 2.0 * T * 3 * H * H}
+    if args.kernel in gemm_flops:
+        ach = gemm_flops[args.kernel] / (kern_avg_ms / 1e3) / 1e12
+        roof = {"kernel": args.kernel, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(ach / peak, 4), "traffic": None, "avg_launch_us": round(kern_avg_ms * 1e3, 2),
+                "launches": len(kern_ms), "algorithmic_per_launch": gemm_flops[args.kernel]}
+    else:
+        e = 2 if w.dtype != "f32" else 4
+        ln_bytes = {"ln1_fwd": 2 * T * H * e + 8 * T, "ln2_fwd": T * H * (4 + e) + 8 * T}
+        byts = ln_bytes.get(args.kernel, float("nan"))
+        ach = byts / (kern_avg_ms / 1e3) / 1e9
+        roof = {"kernel": args.kernel, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
+                "avg_launch_us": round(kern_avg_ms * 1e3, 2), "launches": len(kern_ms),
+                "algorithmic_per_launch": byts}
+
+    out = {
+        "metric": "fwd+bwd tokens/sec and TFLOP/s (% MFMA peak), BERT-Large layer B64 S128 fp16",
+        "value": round(layer_tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: batch {w.batch}, seq {w.seq}, hidden {w.hidden}, heads {w.heads}, "
+                               f"ffn {w.ffn}, {'Pre' if w.pre_ln else 'Post'}-LN, {w.dtype}, dropout "
+                               f"{w.attn_p}/{w.hidden_p}, {n_layers}-layer stack"
+                               + (f", PLD theta={theta:.5f} keeps {n_run}" if w.pld else ""),
+                   "batch": w.batch, "seq_len": w.seq, "hidden": w.hidden, "heads": w.heads, "ffn": w.ffn,
+                   "layers": n_layers, "layers_run": n_run, "parallelism": "single GPU"},
+        "tflops": round(tflops, 1),
+        "pct_mfma_peak": round(100 * tflops / peak, 2),
+        "stack_tokens_per_s": round(T / (ms_per_step / 1e3), 1),
+        "ms_per_layer_fwd_bwd": round(ms_per_step / n_run, 4),
+        "wall_s_timed": round(wall, 3),
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_seqs, w.batch))
+    for e in [t_start, t_stop] + [x for l in run for x in ev[l][0] + ev[l][1]]:
+        hip.destroy(e)
+    for h in handles:
+        B.tel_layer_destroy(h)
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -37,7 +37,7 @@ __device__ __forceinline__ bool keep1(const Rng& r, uint64_t e, uint32_t thr) {
 // ------------------------------------------------------------------ MFMA fwd
 template <typename T>
 __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
-    constexpr int D = 64, KB = 64, VLD = D + 16;
+    constexpr int D = 64, KB = 64, VLD = D + 32;  // V rows 192 B apart: conflict-free transposing reads
     typedef typename MfmaOp<T>::v8 v8;
     __shared__ __align__(16) T Ks[KB * D];
     __shared__ __align__(16) T Vs[KB * VLD];

@@ -21,70 +21,88 @@
 namespace tel {
 
 // ------------------------------------------------------------------ epilogue
+// Each epilogue works on 4 consecutive columns n..n+3 of row m.  It is split
+// into loads (per-column bias, per-element residual / GELU input) and the
+// compute-and-store, so that a kernel can issue every load of a block of
+// outputs before its first store: otherwise the compiler must assume a store
+// may alias the next load and serialises each load's full latency.
+template <typename T, int EPI>
+struct Epi {
+    static constexpr bool kBias = EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES || EPI == EPI_BIAS_GELU;
+    static constexpr bool kElem = EPI == EPI_BIAS_DROP_RES || EPI == EPI_GELU_BWD || EPI == EPI_ADD_RES;
+
+    static __device__ __forceinline__ void load_bias(const EpiArgs& e, int n, float b[4]) {
+        if constexpr (kBias) Vec4<T>::load((const T*)e.bias + n, b);
+    }
+    static __device__ __forceinline__ void load_elem(const EpiArgs& e, int m, int n, float r[4]) {
+        const size_t off = (size_t)m * e.ldo + n;
+        if constexpr (EPI == EPI_BIAS_DROP_RES) {
+            if (e.res_f32) Vec4<float>::load((const float*)e.res + off, r);
+            else Vec4<T>::load((const T*)e.res + off, r);
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+            Vec4<T>::load((const T*)e.aux + off, r);
+        } else if constexpr (EPI == EPI_ADD_RES) {
+            Vec4<float>::load((const float*)e.res + off, r);
+        }
+    }
+    static __device__ __forceinline__ void finish(const EpiArgs& e, int m, int n, float v[4], const float b[4],
+                                                  const float r[4]) {
+        const size_t off = (size_t)m * e.ldo + n;
+        if constexpr (EPI == EPI_STORE) {
+            if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
+            else Vec4<T>::store((T*)e.out + off, v);
+        } else if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += b[i];
+            const int which = n / e.H, rem = n - which * e.H, h = rem / e.d, c = rem - h * e.d;
+            const int bb = m / e.S, s = m - bb * e.S;
+            const size_t o = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
+            Vec4<T>::store((T*)e.out + o, v);
+        } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += b[i];
+            if (e.drop.thr) {
+                const uint64_t el = (uint64_t)m * e.ldo + n;  // token * H + column, n % 4 == 0
+                const uint32_t k = keep4(e.drop.rng, el >> 2, e.drop.thr);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * e.drop.scale : 0.0f;
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += r[i];
+            if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
+            else Vec4<T>::store((T*)e.out + off, v);
+        } else if constexpr (EPI == EPI_BIAS_GELU) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += b[i];
+            Vec4<T>::store((T*)e.out + off, v);
+            if (e.out2) {
+                float g[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) g[i] = gelu_f(round_through<T>(v[i]));
+                Vec4<T>::store((T*)e.out2 + off, g);
+            }
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= gelu_grad_f(r[i]);
+            Vec4<T>::store((T*)e.out + off, v);
+        } else if constexpr (EPI == EPI_HEADSPLIT) {
+            const int bb = m / e.S, s = m - bb * e.S, h = n / e.d, c = n - h * e.d;
+            const size_t o = (((size_t)bb * e.NH + h) * e.S + s) * e.d + c;
+            Vec4<T>::store((T*)e.out + o, v);
+        } else if constexpr (EPI == EPI_ADD_RES) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += r[i];
+            Vec4<T>::store((T*)e.out + off, v);
+        }
+    }
+};
+
 template <typename T, int EPI>
 __device__ __forceinline__ void epilogue4(const EpiArgs& e, int m, int n, float v[4]) {
-    if constexpr (EPI == EPI_STORE) {
-        if (e.out_f32) Vec4<float>::store((float*)e.out + (size_t)m * e.ldo + n, v);
-        else Vec4<T>::store((T*)e.out + (size_t)m * e.ldo + n, v);
-    } else if constexpr (EPI == EPI_QKV) {
-        float b[4];
-        Vec4<T>::load((const T*)e.bias + n, b);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += b[i];
-        const int which = n / e.H, rem = n - which * e.H, h = rem / e.d, c = rem - h * e.d;
-        const int bb = m / e.S, s = m - bb * e.S;
-        const size_t off = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
-        Vec4<T>::store((T*)e.out + off, v);
-    } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
-        float b[4], r[4];
-        Vec4<T>::load((const T*)e.bias + n, b);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += b[i];
-        if (e.drop.thr) {
-            const uint64_t el = (uint64_t)m * e.ldo + n;  // token * H + column, n % 4 == 0
-            const uint32_t k = keep4(e.drop.rng, el >> 2, e.drop.thr);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * e.drop.scale : 0.0f;
-        }
-        const size_t off = (size_t)m * e.ldo + n;
-        if (e.res_f32) Vec4<float>::load((const float*)e.res + off, r);
-        else Vec4<T>::load((const T*)e.res + off, r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += r[i];
-        if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
-        else Vec4<T>::store((T*)e.out + off, v);
-    } else if constexpr (EPI == EPI_BIAS_GELU) {
-        float b[4];
-        Vec4<T>::load((const T*)e.bias + n, b);
-        const size_t off = (size_t)m * e.ldo + n;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += b[i];
-        Vec4<T>::store((T*)e.out + off, v);
-        if (e.out2) {
-            float g[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) g[i] = gelu_f(round_through<T>(v[i]));
-            Vec4<T>::store((T*)e.out2 + off, g);
-        }
-    } else if constexpr (EPI == EPI_GELU_BWD) {
-        float u[4];
-        const size_t off = (size_t)m * e.ldo + n;
-        Vec4<T>::load((const T*)e.aux + off, u);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] *= gelu_grad_f(u[i]);
-        Vec4<T>::store((T*)e.out + off, v);
-    } else if constexpr (EPI == EPI_HEADSPLIT) {
-        const int bb = m / e.S, s = m - bb * e.S, h = n / e.d, c = n - h * e.d;
-        const size_t off = (((size_t)bb * e.NH + h) * e.S + s) * e.d + c;
-        Vec4<T>::store((T*)e.out + off, v);
-    } else if constexpr (EPI == EPI_ADD_RES) {
-        float r[4];
-        const size_t off = (size_t)m * e.ldo + n;
-        Vec4<float>::load((const float*)e.res + off, r);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] += r[i];
-        Vec4<T>::store((T*)e.out + off, v);
-    }
+    float b[4] = {0, 0, 0, 0}, r[4] = {0, 0, 0, 0};
+    Epi<T, EPI>::load_bias(e, n, b);
+    Epi<T, EPI>::load_elem(e, m, n, r);
+    Epi<T, EPI>::finish(e, m, n, v, b, r);
 }
 
 struct GemmParams {
@@ -99,7 +117,10 @@ struct GemmParams {
 
 // ------------------------------------------------------------------ MFMA path
 constexpr int KT = 64;        // k tile (elements)
-constexpr int MN_PAD = 16;    // padding (elements) of m/n-major LDS rows
+// Padding (elements) of m/n-major LDS rows: rows of 128 or 256 elements
+// then start 64 bytes apart modulo 256, so the four rows of a transposing
+// read of two 16-lane groups (32 bytes each) land in distinct banks.
+constexpr int MN_PAD = 32;
 
 template <bool KMAJ, int R>
 struct TileGeom {
@@ -255,22 +276,65 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) 
 
     // acc[i][j][g*4 + r]: row m = m0 + wm*WM + i*32 + (lane & 31),
     // columns n .. n+3 with n = n0 + wn*WN + j*32 + g*8 + (lane >> 5)*4.
+    if (gridDim.z > 1) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int m = m0 + wm * WM + i * 32 + (lane & 31);
+                    const int n = n0 + wn * WN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    float v[4] = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
+                                  acc[i][j][g * 4 + 3]};
+                    Vec4<float>::store(p.ws + ((size_t)blockIdx.z * p.M + m) * p.N + n, v);
+                }
+        return;
+    }
+    // Epilogue, staged through LDS (free after the main loop): for each
+    // 32-row block, the wave writes its 32 x WN fp32 tile to a private LDS
+    // region in the accumulator layout, then reads it back with each lane
+    // holding 4 consecutive columns and consecutive lanes consecutive column
+    // groups, so global loads (residual, GELU input) and stores run over
+    // contiguous rows.
+    typedef Epi<T, EPI> E;
+    constexpr int ELD = WN + 4;  // fp32 row stride: 16 rows of a column group hit distinct banks
+    static_assert(4 * 32 * ELD * 4 <= 2 * STAGE * (int)sizeof(T), "epilogue staging exceeds LDS");
+    float* est = reinterpret_cast<float*>(smem_raw) + wave * 32 * ELD;
+    constexpr int GPR = WN / 4;           // 4-column groups per row
+    constexpr int RPI = 64 / GPR;         // rows per lane-iteration
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
 #pragma unroll
         for (int j = 0; j < NI; ++j)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int m = m0 + wm * WM + i * 32 + (lane & 31);
-                const int n = n0 + wn * WN + j * 32 + g * 8 + (lane >> 5) * 4;
-                float v[4] = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
-                              acc[i][j][g * 4 + 3]};
-                if (gridDim.z > 1) {
-                    Vec4<float>::store(p.ws + ((size_t)blockIdx.z * p.M + m) * p.N + n, v);
-                } else {
-                    epilogue4<T, EPI>(p.ea, m, n, v);
-                }
+                const int col = j * 32 + g * 8 + (lane >> 5) * 4;
+                *reinterpret_cast<float4*>(est + (lane & 31) * ELD + col) =
+                    make_float4(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
             }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+        const int cg = lane % GPR, r0 = lane / GPR;
+        const int n = n0 + wn * WN + cg * 4;
+        float b[4] = {0, 0, 0, 0};
+        E::load_bias(p.ea, n, b);
+        float el[32 / RPI][4];
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+#pragma unroll
+            for (int t = 0; t < 4; ++t) el[it][t] = 0.0f;
+            E::load_elem(p.ea, m0 + wm * WM + i * 32 + it * RPI + r0, n, el[it]);
+        }
+#pragma unroll
+        for (int it = 0; it < 32 / RPI; ++it) {
+            const int rr = it * RPI + r0;
+            const float4 q = *reinterpret_cast<const float4*>(est + rr * ELD + cg * 4);
+            float v[4] = {q.x, q.y, q.z, q.w};
+            E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, el[it]);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 // Deterministic split-K reduction: out[m][n] = sum_z ws[z][m][n] in z order.

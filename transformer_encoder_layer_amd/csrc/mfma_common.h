@@ -29,10 +29,15 @@ template <> struct MfmaOp<bf16> {
     }
 };
 
-// Element offset of (row, k) in a k-major LDS tile with 64 elements per row
-// whose 16-byte chunks are XOR-swizzled by (row & 7).
+// Element offset of (row, k) in a k-major LDS tile with 64 elements
+// (128 bytes) per row whose 16-byte chunks are XOR-swizzled by row.  The
+// gfx950 LDS serves 16 lanes x 16 bytes per cycle from 64 4-byte banks, so
+// a 128-bit fragment read (16 consecutive rows, one chunk each) is
+// conflict-free only if those 16 rows cover all 16 bank groups: even and odd
+// rows already sit in different 128-byte halves, and the chunk is XORed with
+// (row >> 1) & 7 to spread each half over its 8 groups.
 __device__ __forceinline__ int kmaj_off(int row, int k) {
-    return row * 64 + ((((k >> 3) ^ (row & 7))) << 3) + (k & 7);
+    return row * 64 + ((((k >> 3) ^ ((row >> 1) & 7))) << 3) + (k & 7);
 }
 
 // Operand fragment from a swizzled k-major tile [rows][64]: lane l gets

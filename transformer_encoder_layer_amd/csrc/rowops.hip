@@ -14,7 +14,6 @@
 namespace tel {
 
 constexpr int LN_MAXC = 16;   // H <= 64 lanes * 4 * 16 = 4096
-constexpr int LN_RPW = 4;     // rows per wave in the backward
 
 template <typename T>
 __device__ __forceinline__ void load4(const void* p, int is_f32, size_t off, float v[4]) {
@@ -79,120 +78,147 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     }
 }
 
-template <typename T>
-__global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
-    __shared__ float red[4][LN_MAXC * 256 / 4 > 1024 ? 1024 : LN_MAXC * 256 / 4];
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int H = a.H;
-    float pg[LN_MAXC][4], pb[LN_MAXC][4];
-#pragma unroll
-    for (int c = 0; c < LN_MAXC; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) { pg[c][i] = 0.0f; pb[c][i] = 0.0f; }
+// LayerNorm backward: one workgroup per LN_ROWS rows, one thread per 4
+// consecutive columns (H/4 threads).  Rows are processed LN_RB at a time; the
+// two per-row sums (of g*gamma and g*gamma*xhat) are reduced across the
+// workgroup in a fixed order.  Each thread keeps the dgamma/dbeta partial
+// sums of its own 4 columns over the workgroup's rows, so the per-workgroup
+// partial rows need no further reduction inside the kernel.
+constexpr int LN_ROWS = 32;
+constexpr int LN_RB = 4;
 
-    for (int rr = 0; rr < LN_RPW; ++rr) {
-        const int row = (blockIdx.x * 4 + wave) * LN_RPW + rr;
-        if (row >= a.T) break;
-        const size_t base = (size_t)row * H;
-        const float rs = a.rstd[row];
-        const float mu = a.from_output ? 0.0f : a.mu[row];
-        float dy[LN_MAXC][4], xh[LN_MAXC][4];
-        float sg = 0.0f, sgx = 0.0f;
+template <typename T>
+__global__ __launch_bounds__(1024) void ln_bwd_kernel(LnBwdArgs a) {
+    __shared__ float red[2][16][LN_RB];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+    const int H = a.H;
+    const int c4 = tid * 4;
+    const bool act = c4 < H;
+    float gam[4] = {0, 0, 0, 0}, bet[4] = {0, 0, 0, 0};
+    if (act) {
+        Vec4<T>::load((const T*)a.gamma + c4, gam);
+        if (a.from_output) Vec4<T>::load((const T*)a.beta + c4, bet);
+    }
+    float pg[4] = {0, 0, 0, 0}, pb[4] = {0, 0, 0, 0};
+    const int rbeg = blockIdx.x * LN_ROWS;
+    const int rend = min(a.T, rbeg + LN_ROWS);
+    for (int r0 = rbeg; r0 < rend; r0 += LN_RB) {
+        float dy[LN_RB][4], xh[LN_RB][4], s1[LN_RB], s2[LN_RB];
 #pragma unroll
-        for (int c = 0; c < LN_MAXC; ++c) {
-            const int idx = c * 256 + lane * 4;
-            if (idx < H) {
-                float g[4], sv[4];
-                Vec4<T>::load((const T*)a.dout + base + idx, dy[c]);
+        for (int rb = 0; rb < LN_RB; ++rb) {
+            const int row = r0 + rb;
+            s1[rb] = 0.0f;
+            s2[rb] = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) { dy[rb][i] = 0.0f; xh[rb][i] = 0.0f; }
+            if (row < rend && act) {
+                const size_t off = (size_t)row * H + c4;
+                float sv[4];
+                Vec4<T>::load((const T*)a.dout + off, dy[rb]);
                 if (a.dout_add) {
                     float t[4];
-                    Vec4<float>::load(a.dout_add + base + idx, t);
+                    Vec4<float>::load(a.dout_add + off, t);
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dy[c][i] += t[i];
+                    for (int i = 0; i < 4; ++i) dy[rb][i] += t[i];
                 }
-                Vec4<T>::load((const T*)a.gamma + idx, g);
-                load4<T>(a.src, a.src_f32, base + idx, sv);
-                if (a.from_output) {
-                    float bt[4];
-                    Vec4<T>::load((const T*)a.beta + idx, bt);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) xh[c][i] = (sv[i] - bt[i]) / g[i];
-                } else {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) xh[c][i] = (sv[i] - mu) * rs;
-                }
+                load4<T>(a.src, a.src_f32, off, sv);
+                const float rs = a.rstd[row];
+                const float mu = a.from_output ? 0.0f : a.mu[row];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float gh = dy[c][i] * g[i];
-                    sg += gh;
-                    sgx += gh * xh[c][i];
-                    pg[c][i] += dy[c][i] * xh[c][i];
-                    pb[c][i] += dy[c][i];
+                    xh[rb][i] = a.from_output ? (sv[i] - bet[i]) / gam[i] : (sv[i] - mu) * rs;
+                    const float gh = dy[rb][i] * gam[i];
+                    s1[rb] += gh;
+                    s2[rb] += gh * xh[rb][i];
+                    pg[i] += dy[rb][i] * xh[rb][i];
+                    pb[i] += dy[rb][i];
                 }
             }
         }
-        const float mg = wave_sum(sg) / (float)H;
-        const float mgx = wave_sum(sgx) / (float)H;
 #pragma unroll
-        for (int c = 0; c < LN_MAXC; ++c) {
-            const int idx = c * 256 + lane * 4;
-            if (idx < H) {
-                float g[4], dx[4];
-                Vec4<T>::load((const T*)a.gamma + idx, g);
+        for (int rb = 0; rb < LN_RB; ++rb) {
+            s1[rb] = wave_sum(s1[rb]);
+            s2[rb] = wave_sum(s2[rb]);
+        }
+        if (lane == 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dx[i] = rs * (dy[c][i] * g[i] - mg - xh[c][i] * mgx);
+            for (int rb = 0; rb < LN_RB; ++rb) {
+                red[0][wave][rb] = s1[rb];
+                red[1][wave][rb] = s2[rb];
+            }
+        }
+        __syncthreads();
+        float mg[LN_RB], mgx[LN_RB];
+#pragma unroll
+        for (int rb = 0; rb < LN_RB; ++rb) {
+            float t1 = 0.0f, t2 = 0.0f;
+            for (int w = 0; w < nw; ++w) {
+                t1 += red[0][w][rb];
+                t2 += red[1][w][rb];
+            }
+            mg[rb] = t1 / (float)H;
+            mgx[rb] = t2 / (float)H;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int rb = 0; rb < LN_RB; ++rb) {
+            const int row = r0 + rb;
+            if (row < rend && act) {
+                const size_t off = (size_t)row * H + c4;
+                const float rs = a.rstd[row];
+                float dx[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dx[i] = rs * (dy[rb][i] * gam[i] - mg[rb] - xh[rb][i] * mgx[rb]);
                 if (a.res) {
                     float r[4];
-                    load4<T>(a.res, a.res_f32, base + idx, r);
+                    load4<T>(a.res, a.res_f32, off, r);
 #pragma unroll
                     for (int i = 0; i < 4; ++i) dx[i] += r[i];
                 }
-                store4<T>(a.out, a.out_f32, base + idx, dx);
+                store4<T>(a.out, a.out_f32, off, dx);
                 if (a.drop_out) {
                     if (a.drop.thr) {
-                        const uint32_t k = keep4(a.drop.rng, (base + idx) >> 2, a.drop.thr);
+                        const uint32_t k = keep4(a.drop.rng, off >> 2, a.drop.thr);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dx[i] = ((k >> i) & 1u) ? dx[i] * a.drop.scale : 0.0f;
                     }
-                    Vec4<T>::store((T*)a.drop_out + base + idx, dx);
+                    Vec4<T>::store((T*)a.drop_out + off, dx);
                 }
             }
         }
     }
-    // block reduction of the dgamma / dbeta partials over the 4 waves
-    for (int which = 0; which < 2; ++which) {
-        for (int c0 = 0; c0 < LN_MAXC; c0 += 4) {
-            // chunks c0..c0+3 cover columns [c0*256, c0*256 + 1024)
-            if (c0 * 256 >= H) break;
-#pragma unroll
-            for (int cc = 0; cc < 4; ++cc) {
-                const int c = c0 + cc;
-                const int idx = c * 256 + lane * 4;
-                if (c < LN_MAXC && idx < H) {
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) red[wave][cc * 256 + lane * 4 + i] = which ? pb[c][i] : pg[c][i];
-                }
-            }
-            __syncthreads();
-            for (int j = threadIdx.x; j < 1024; j += 256) {
-                const int col = c0 * 256 + j;
-                if (col < H) {
-                    const float v = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
-                    (which ? a.part_b : a.part_g)[(size_t)blockIdx.x * H + col] = v;
-                }
-            }
-            __syncthreads();
-        }
+    if (act) {
+        Vec4<float>::store(a.part_g + (size_t)blockIdx.x * H + c4, pg);
+        Vec4<float>::store(a.part_b + (size_t)blockIdx.x * H + c4, pb);
     }
 }
 
+// out[n] = sum_p part[p][n]: 32 columns x 8 row phases per workgroup; phase
+// j sums rows j, j+8, j+16, ... in order, then the 8 phase sums are added in
+// order -- a fixed summation order, independent of scheduling.
 template <typename T>
-__global__ void colsum_finalize_kernel(const float* part, int P, int N, T* out) {
-    const int n = blockIdx.x * blockDim.x + threadIdx.x;
-    if (n >= N) return;
+__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* part, int P, int N, T* out) {
+    __shared__ float red[8][33];
+    const int cl = threadIdx.x & 31, ph = threadIdx.x >> 5;
+    const int n = blockIdx.x * 32 + cl;
     float s = 0.0f;
-    for (int p = 0; p < P; ++p) s += part[(size_t)p * N + n];
-    out[n] = from_f<T>(s);
+    if (n < N) {
+        int p = ph;
+        for (; p + 24 < P; p += 32) {
+            const float a0 = part[(size_t)p * N + n], a1 = part[(size_t)(p + 8) * N + n];
+            const float a2 = part[(size_t)(p + 16) * N + n], a3 = part[(size_t)(p + 24) * N + n];
+            s += a0; s += a1; s += a2; s += a3;
+        }
+        for (; p < P; p += 8) s += part[(size_t)p * N + n];
+    }
+    red[ph][cl] = s;
+    __syncthreads();
+    if (ph == 0 && n < N) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t += red[j][cl];
+        out[n] = from_f<T>(t);
+    }
 }
 
 constexpr int CS_ROWS = 64;  // rows per partial in colsum_partial
@@ -247,21 +273,23 @@ hipError_t ln_forward(const LnFwdArgs& a, hipStream_t st) {
     return hipGetLastError();
 }
 
-int ln_backward_parts(int T) { return (T + 4 * LN_RPW - 1) / (4 * LN_RPW); }
+int ln_backward_parts(int T) { return (T + LN_ROWS - 1) / LN_ROWS; }
 
 hipError_t ln_backward(const LnBwdArgs& a, hipStream_t st) {
     dim3 grid(ln_backward_parts(a.T));
+    const int thr = ((a.H / 4 + 63) / 64) * 64;
+    if (thr > 1024) return hipErrorInvalidValue;
     switch (a.dtype) {
-        case 0: hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(256), 0, st, a); break;
-        case 1: hipLaunchKernelGGL(ln_bwd_kernel<f16>, grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(256), 0, st, a); break;
+        case 0: hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(thr), 0, st, a); break;
+        case 1: hipLaunchKernelGGL(ln_bwd_kernel<f16>, grid, dim3(thr), 0, st, a); break;
+        case 2: hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(thr), 0, st, a); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }
 
 hipError_t colsum_finalize(int dtype, const float* part, int P, int N, void* out, hipStream_t st) {
-    dim3 grid((N + 255) / 256);
+    dim3 grid((N + 31) / 32);
     switch (dtype) {
         case 0: hipLaunchKernelGGL(colsum_finalize_kernel<float>, grid, dim3(256), 0, st, part, P, N, (float*)out); break;
         case 1: hipLaunchKernelGGL(colsum_finalize_kernel<f16>, grid, dim3(256), 0, st, part, P, N, (f16*)out); break;

@@ -106,17 +106,36 @@ struct Drop {
 };
 
 // ---------------------------------------------------------------- GELU
-// Exact GELU u*Phi(u) and its derivative Phi(u) + u*phi(u), evaluated with
-// explicit roundings so that every kernel that recomputes them produces the
-// same bits.
+// Exact GELU u*Phi(u) and its derivative Phi(u) + u*phi(u) (AI-infra blog,
+// section 2.3: the erf form, not the tanh approximation).  Phi comes from
+// the complementary error function in the rational form of Abramowitz &
+// Stegun, Handbook of Mathematical Functions, formula 7.1.26
+// (|error| <= 1.5e-7 in erf), evaluated on |u|/sqrt(2) so that the left
+// tail has no cancellation; phi shares the same exponential.  Every
+// operation is explicitly rounded so that each kernel that recomputes the
+// GELU (forward epilogue, weight-gradient operand load) gets the same bits.
+__device__ __forceinline__ void normal_cdf_pdf(float u, float& cdf, float& pdf) {
+    const float x = __fmul_rn(fabsf(u), 0.70710678118654752f);
+    const float t = __builtin_amdgcn_rcpf(__fmaf_rn(0.3275911f, x, 1.0f));
+    const float e = __builtin_amdgcn_exp2f(__fmul_rn(__fmul_rn(u, u), -0.72134752044448170f));  // e^(-u^2/2)
+    float poly = __fmaf_rn(1.061405429f, t, -1.453152027f);
+    poly = __fmaf_rn(poly, t, 1.421413741f);
+    poly = __fmaf_rn(poly, t, -0.284496736f);
+    poly = __fmaf_rn(poly, t, 0.254829592f);
+    poly = __fmul_rn(poly, t);
+    const float half_erfc = __fmul_rn(__fmul_rn(0.5f, poly), e);
+    cdf = u >= 0.0f ? __fadd_rn(1.0f, -half_erfc) : half_erfc;
+    pdf = __fmul_rn(e, 0.39894228040143268f);
+}
 __device__ __forceinline__ float gelu_f(float u) {
-    const float cdf = __fmul_rn(0.5f, __fadd_rn(1.0f, erff(__fmul_rn(u, 0.70710678118654752f))));
+    float cdf, pdf;
+    normal_cdf_pdf(u, cdf, pdf);
     return __fmul_rn(u, cdf);
 }
 __device__ __forceinline__ float gelu_grad_f(float u) {
-    const float cdf = __fmul_rn(0.5f, __fadd_rn(1.0f, erff(__fmul_rn(u, 0.70710678118654752f))));
-    const float pdf = __fmul_rn(0.39894228040143268f, __expf(__fmul_rn(-0.5f, __fmul_rn(u, u))));
-    return __fadd_rn(cdf, __fmul_rn(u, pdf));
+    float cdf, pdf;
+    normal_cdf_pdf(u, cdf, pdf);
+    return __fmaf_rn(u, pdf, cdf);
 }
 
 // ---------------------------------------------------------------- wave ops
