@@ -31,8 +31,10 @@
  * e = ((b*N + h)*S + i)*S + j; 1 attention-branch output, 2 FFN-branch
  * output, element e = t*H + c with token t = b*S + s; 3 the progressive
  * layer-drop gate (element 0).  Masks are a pure function of
- * (seed, layer_id, site, step, e): nothing is stored between forward and
- * backward, so every switch setting regenerates identical masks.
+ * (seed, layer_id, site, step, e).  The forward keeps the attention keep
+ * bits (1 bit per score, in saved) unless attn_dropout_checkpoint is set, in
+ * which case the backward regenerates them; hidden-dropout bits are always
+ * regenerated.  Every switch setting therefore sees identical masks.
  *
  * Data layout: row-major, token-major activations [B*S, H] with t = b*S+s;
  * weights in nn.Linear layout W[out, in].  Params, activations and grads
@@ -86,7 +88,8 @@ typedef struct {
     int32_t layer_id;              /* dropout key word 1 */
     int32_t dtype;                 /* tel_dtype */
     float ln_eps;                  /* LayerNorm epsilon (the guide's default 1e-12) */
-    int32_t attn_dropout_checkpoint; /* masks are never stored: accepted, no effect on memory */
+    int32_t attn_dropout_checkpoint; /* do not keep the attention keep bits (1 bit per score);
+                                        backward regenerates them from the RNG */
     int32_t normalize_invertible;  /* LN backward from the LN output; drops the LN inputs */
     int32_t gelu_checkpoint;       /* keep the GELU input only; recompute GELU in backward */
 } tel_config;
@@ -108,7 +111,7 @@ typedef struct {
 typedef struct tel_layer tel_layer;
 
 /* Validate cfg and create a handle (host memory only).  Supported: dims
- * multiples of 16, head width d in {16,32,64,128}, H % N == 0, dtype f32,
+ * multiples of 16, hidden <= 2048, head width d in {16,32,64,128}, H % N == 0, dtype f32,
  * f16 or bf16.  *out is set to NULL on failure. */
 tel_status tel_layer_create(const tel_config* cfg, tel_layer** out);
 

@@ -48,6 +48,7 @@ def cfg(**kw):
     (dict(heads=3), B.TEL_ERR_INVALID_ARG),          # H % N != 0
     (dict(hidden=64, heads=8), B.TEL_ERR_UNSUPPORTED),  # d = 8
     (dict(hidden=1024, heads=4), B.TEL_ERR_UNSUPPORTED),  # d = 256
+    (dict(hidden=4096, heads=32), B.TEL_ERR_UNSUPPORTED),  # H > 2048
     (dict(seq=20), B.TEL_ERR_INVALID_ARG),
     (dict(batch=0), B.TEL_ERR_INVALID_ARG),
     (dict(attn_dropout=1.0), B.TEL_ERR_INVALID_ARG),
@@ -88,7 +89,7 @@ def test_memory_switches_shrink_saved(pre_ln):
     sizes = {}
     for name, kw in {"base": {}, "gelu": dict(gelu_checkpoint=1), "inv": dict(normalize_invertible=1),
                      "attn": dict(attn_dropout_checkpoint=1)}.items():
-        h = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=4, seq=128, hidden=256, heads=4, ffn=1024,
+        h = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=4, seq=128, hidden=256, heads=4, ffn=1024, attn_dropout=0.1,
                                    pre_ln=pre_ln, **kw))
         sizes[name] = B.tel_layer_workspace_bytes(h)[0]
         B.tel_layer_destroy(h)
@@ -98,7 +99,7 @@ def test_memory_switches_shrink_saved(pre_ln):
         assert sizes["base"] - sizes["inv"] >= T * H * 4       # fp32 LN2 input not kept
     else:
         assert sizes["inv"] < sizes["base"]
-    assert sizes["attn"] == sizes["base"]                      # masks are never stored
+    assert sizes["base"] - sizes["attn"] == 4 * 4 * 128 * 128 // 8   # attention keep bits not kept
 
 
 def test_forward_validation_before_gpu():

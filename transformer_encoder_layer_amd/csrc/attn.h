@@ -12,6 +12,9 @@ struct AttnArgs {
     const void* qkvh;   // [3][B][NH][S][d]
     const int32_t* len; // [B] valid key counts, or nullptr
     Drop drop;          // site 0; thr == 0: no dropout
+    uint32_t* bits;     // optional keep bits [B][NH][S][S/32] (bit j%32 of word j/32 = key j):
+                        // written by the forward, read by the backward; nullptr: the
+                        // backward regenerates them from the counter-based RNG
     // forward
     void* ctx;          // [B*S][H] head-merged output
     float* lse;         // [B][NH][S] log2-sum-exp2 of the scaled scores

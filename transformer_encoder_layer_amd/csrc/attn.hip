@@ -20,7 +20,10 @@
 // Backward: a query-parallel kernel computes D_i = rowsum(dO_i * O_i) and
 // dQ; a key-parallel kernel computes dK and dV (no atomics: every output
 // row is owned by one wave).  Both recompute P from Q, K and the saved
-// log-sum-exp and regenerate the dropout bits from the counter-based RNG.
+// log-sum-exp.  The dropout bits come from the 1-bit-per-element mask the
+// forward packed (one 32-bit word per query and 32 keys), or, when the
+// caller chose not to keep it (attention-dropout checkpointing), from the
+// counter-based RNG again -- the same bits either way.
 //
 // SIMT path: one thread per row, any S and d in {16, 32, 64, 128}.
 #include "attn.h"
@@ -118,15 +121,22 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
                 for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
             if (a.drop.thr) {
 #pragma unroll
-                for (int kt = 0; kt < 2; ++kt)
+                for (int kt = 0; kt < 2; ++kt) {
+                    uint32_t word = 0;  // keep bits of keys kb*64 + kt*32 + 0..31 held by this lane
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
                         const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
                         const uint32_t kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
+                        word |= kbits << (g * 8 + (lane >> 5) * 4);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
                     }
+                    if (a.bits) {
+                        word |= __shfl_xor(word, 32, 64);
+                        if (lane < 32) a.bits[(rowbase >> 5) + kb * 2 + kt] = word;
+                    }
+                }
             }
 #pragma unroll
             for (int ks2 = 0; ks2 < 4; ++ks2) {
@@ -237,7 +247,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
                 for (int g = 0; g < 4; ++g) {
                     const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
                     uint32_t kbits = 0xFu;
-                    if (a.drop.thr) kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
+                    if (a.drop.thr) {
+                        if (a.bits) kbits = (a.bits[(rowbase >> 5) + (key4 >> 5)] >> (key4 & 31)) & 0xFu;
+                        else kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
+                    }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = g * 4 + i;
@@ -285,6 +298,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
     __shared__ __align__(16) T Qs[QB * D];
     __shared__ __align__(16) T Os[QB * D];
     __shared__ float lse_s[QB], D_s[QB];
+    __shared__ uint32_t bits_s[QB][4];  // keep-bit words of this block's 128 keys for 64 queries
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
@@ -330,6 +344,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
         }
         if (tid < QB) lse_s[tid] = lse[qb * QB + tid];
         else if (tid < 2 * QB) D_s[tid - QB] = Dv[qb * QB + tid - QB];
+        if (a.bits && a.drop.thr) {
+            const int q = tid >> 2, w = tid & 3;  // 256 threads: 64 queries x 4 words
+            const int kw = blockIdx.x * 4 + w;
+            bits_s[q][w] = kw < S / 32 ? a.bits[(bhbase + qb * QB + q) * (S / 32) + kw] : 0u;
+        }
         __syncthreads();
         if (live) {
             f32x16 s[2], dp[2];
@@ -353,7 +372,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
                     const int q = qb * QB + qi;
                     const float p = kl < L ? exp2f(s[qt][r] * c - lse_s[qi]) : 0.0f;
                     float f = 1.0f;
-                    if (a.drop.thr) f = keep1(a.drop.rng, (bhbase + q) * S + kl, a.drop.thr) ? a.drop.scale : 0.0f;
+                    if (a.drop.thr) {
+                        const bool keep = a.bits ? ((bits_s[qi][wave] >> (kl & 31)) & 1u)
+                                                 : keep1(a.drop.rng, (bhbase + q) * S + kl, a.drop.thr);
+                        f = keep ? a.drop.scale : 0.0f;
+                    }
                     ds[qt][r] = p * (dp[qt][r] * f - D_s[qi]);
                     s[qt][r] = p * f;
                 }
@@ -538,13 +561,17 @@ __global__ __launch_bounds__(128) void attn_bwd_dkdv_simt(AttnArgs a) {
 static bool mfma_attn_ok(const AttnArgs& a) { return a.dtype != 0 && a.d == 64 && a.S % 64 == 0; }
 
 template <typename T, int D>
-static hipError_t simt_fwd(const AttnArgs& a, hipStream_t st) {
+static hipError_t simt_fwd(const AttnArgs& a0, hipStream_t st) {
+    AttnArgs a = a0;
+    a.bits = nullptr;  // the generic kernels regenerate the bits
     const int n = a.B * a.NH * a.S;
     hipLaunchKernelGGL((attn_fwd_simt<T, D>), dim3((n + 127) / 128), dim3(128), 0, st, a);
     return hipGetLastError();
 }
 template <typename T, int D>
-static hipError_t simt_bwd(const AttnArgs& a, hipStream_t st) {
+static hipError_t simt_bwd(const AttnArgs& a0, hipStream_t st) {
+    AttnArgs a = a0;
+    a.bits = nullptr;
     const int n = a.B * a.NH * a.S;
     hipLaunchKernelGGL((attn_bwd_dq_simt<T, D>), dim3((n + 127) / 128), dim3(128), 0, st, a);
     hipError_t e = hipGetLastError();

@@ -48,9 +48,17 @@ struct GemmDesc {
     bool b_gelu = false;  // B elements pass through GELU on load
     int epi = EPI_STORE;
     EpiArgs ea;
-    float* splitk_ws = nullptr;  // fp32 [splits][M][N] partials (weight gradients)
+    float* splitk_ws = nullptr;  // fp32 [splits][M][N] partials (+ [splits][M] row sums)
     size_t splitk_ws_elems = 0;
+    // Optional row sums of A over k (sum_k A(m,k), dtype, M values): for a
+    // weight gradient dW = dY^T X these are the bias gradients sum_t dY[t][m].
+    // Only computed when gemm_rowsum_fused() is true; the caller sums
+    // otherwise.
+    void* rowsum_out = nullptr;
 };
+
+// True if gemm_launch computes rowsum_out for this GEMM inside its kernel.
+bool gemm_rowsum_fused(const GemmDesc& g);
 
 // Launch; returns hipSuccess or the launch error.  force_simt selects the
 // generic SIMT kernel regardless of shape (used by tests).

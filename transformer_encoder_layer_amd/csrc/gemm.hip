@@ -17,6 +17,7 @@
 #include "gemm.h"
 #include "mfma_common.h"
 #include <type_traits>
+#include <algorithm>
 
 namespace tel {
 
@@ -113,6 +114,7 @@ struct GemmParams {
     int k_per_split;  // multiple of the k tile
     EpiArgs ea;
     float* ws;        // split-K partials, [splits][M][N]
+    void* rsum;       // row sums of A: dtype [M] (one split) or fp32 [splits][M] after ws
 };
 
 // ------------------------------------------------------------------ MFMA path
@@ -188,14 +190,37 @@ __device__ __forceinline__ void tile_store(T* lds, const uint4* reg, int tid) {
     }
 }
 
+// Per-thread partial row sums of an m-major A tile: with R/8 chunks per k row
+// and NT a multiple of R/8, thread tid always loads the chunk of rows
+// 8*(tid % (R/8)) .. +7, so it can add up the 8 values of every chunk it
+// loads over the whole k range (fixed order).
+template <typename T, int R, int NT>
+__device__ __forceinline__ void rowsum_acc(float (&rs)[8], const uint4* reg) {
+    constexpr int CPT = TileGeom<false, R>::CHUNKS / NT;
+    typedef T v8 __attribute__((ext_vector_type(8)));
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const uint4 u = reg[i];
+        const v8 x = *reinterpret_cast<const v8*>(&u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) rs[e] += to_f(x[e]);
+    }
+}
+
 // Map the linear workgroup id to an output tile.  Consecutive ids are
 // dispatched round-robin over the 8 XCDs; the remap gives each XCD one
 // contiguous range of tiles, walked in groups of GM tile rows so that the
 // tiles resident on one XCD share A rows and B columns in its L2.
+#ifndef GEMM_XCD_REMAP
+#define GEMM_XCD_REMAP 1
+#endif
+#ifndef GEMM_GM
+#define GEMM_GM 8
+#endif
 __device__ __forceinline__ void tile_of(int pid, int tm, int tn, int& im, int& in_) {
     const int total = tm * tn;
-    if ((total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
-    constexpr int GM = 8;
+    if (GEMM_XCD_REMAP && (total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    constexpr int GM = GEMM_GM;
     const int group = pid / (GM * tn);
     const int first = group * GM;
     const int gm = min(tm - first, GM);
@@ -204,76 +229,14 @@ __device__ __forceinline__ void tile_of(int pid, int tm, int tn, int& im, int& i
     in_ = r / gm;
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
-__global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) {
-    constexpr int NT = WGM * WGN * 64;
+// Epilogue shared by the GEMM kernels (acc layout of the 32x32x16 MFMA with
+// the operand roles swapped: lane holds 4 consecutive columns of one row).
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                              unsigned char* smem_raw, int m0, int n0, int wm, int wn, int wave,
+                                              int lane) {
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
-    typedef TileGeom<AK, BM> GA;
-    typedef TileGeom<BKM, BN> GB;
-    constexpr int STAGE = GA::ELEMS + GB::ELEMS;
-    static_assert(GA::CHUNKS % NT == 0 && GB::CHUNKS % NT == 0, "tile/thread mismatch");
-    typedef typename MfmaOp<T>::v8 v8;
-
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    T* smem = reinterpret_cast<T*>(smem_raw);
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int tm = p.M / BM, tn = p.N / BN;
-    int im, in_;
-    tile_of(blockIdx.x, tm, tn, im, in_);
-    const int m0 = im * BM, n0 = in_ * BN;
-    const int kbeg = blockIdx.z * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nk = (kend - kbeg) / KT;
-
-    const T* A = (const T*)p.A;
-    const T* B = (const T*)p.B;
-
-    f32x16 acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    uint4 ra[GA::CHUNKS / NT], rb[GB::CHUNKS / NT];
-    tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg, tid);
-    tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg, tid);
-    tile_store<T, AK, BM, NT, false>(smem, ra, tid);
-    tile_store<T, BKM, BN, NT, BGELU>(smem + GA::ELEMS, rb, tid);
-    __syncthreads();
-
-    for (int kt = 0; kt < nk; ++kt) {
-        const T* sa = smem + (kt & 1) * STAGE;
-        const T* sb = sa + GA::ELEMS;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg + (kt + 1) * KT, tid);
-            tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg + (kt + 1) * KT, tid);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KT / 16; ++ks) {
-            v8 fa[MI], fb[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) fa[i] = frag_load<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
-#pragma unroll
-            for (int j = 0; j < NI; ++j) fb[j] = frag_load<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
-        }
-        if (more) {
-            T* da = smem + ((kt + 1) & 1) * STAGE;
-            tile_store<T, AK, BM, NT, false>(da, ra, tid);
-            tile_store<T, BKM, BN, NT, BGELU>(da + GA::ELEMS, rb, tid);
-        }
-        __syncthreads();
-    }
-
     // acc[i][j][g*4 + r]: row m = m0 + wm*WM + i*32 + (lane & 31),
     // columns n .. n+3 with n = n0 + wn*WN + j*32 + g*8 + (lane >> 5)*4.
     if (gridDim.z > 1) {
@@ -299,7 +262,6 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) 
     // contiguous rows.
     typedef Epi<T, EPI> E;
     constexpr int ELD = WN + 4;  // fp32 row stride: 16 rows of a column group hit distinct banks
-    static_assert(4 * 32 * ELD * 4 <= 2 * STAGE * (int)sizeof(T), "epilogue staging exceeds LDS");
     float* est = reinterpret_cast<float*>(smem_raw) + wave * 32 * ELD;
     constexpr int GPR = WN / 4;           // 4-column groups per row
     constexpr int RPI = 64 / GPR;         // rows per lane-iteration
@@ -337,11 +299,357 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) 
     }
 }
 
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
+__global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) {
+    constexpr int NT = WGM * WGN * 64;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int MI = WM / 32, NI = WN / 32;
+    typedef TileGeom<AK, BM> GA;
+    typedef TileGeom<BKM, BN> GB;
+    constexpr int STAGE = GA::ELEMS + GB::ELEMS;
+    static_assert(GA::CHUNKS % NT == 0 && GB::CHUNKS % NT == 0, "tile/thread mismatch");
+    typedef typename MfmaOp<T>::v8 v8;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* smem = reinterpret_cast<T*>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int tm = p.M / BM, tn = p.N / BN;
+    int im, in_;
+    tile_of(blockIdx.x, tm, tn, im, in_);
+    const int m0 = im * BM, n0 = in_ * BN;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nk = (kend - kbeg) / KT;
+
+    const T* A = (const T*)p.A;
+    const T* B = (const T*)p.B;
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // bias gradient fused into a weight gradient: the workgroups of tile
+    // column 0 also sum their A rows (uniform branch per workgroup)
+    const bool do_rsum = !AK && p.rsum != nullptr && in_ == 0;
+    float rs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    uint4 ra[GA::CHUNKS / NT], rb[GB::CHUNKS / NT];
+    tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg, tid);
+    tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg, tid);
+    if constexpr (!AK) {
+        if (do_rsum) rowsum_acc<T, BM, NT>(rs, ra);
+    }
+    tile_store<T, AK, BM, NT, false>(smem, ra, tid);
+    tile_store<T, BKM, BN, NT, BGELU>(smem + GA::ELEMS, rb, tid);
+    __syncthreads();
+
+    // Double-buffered LDS: the global loads of k-tile kt+1 are issued before
+    // the MFMAs of tile kt and written to the other buffer after them.
+    for (int kt = 0; kt < nk; ++kt) {
+        const T* sa = smem + (kt & 1) * STAGE;
+        const T* sb = sa + GA::ELEMS;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg + (kt + 1) * KT, tid);
+            tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg + (kt + 1) * KT, tid);
+        }
+#pragma unroll
+        for (int ks = 0; ks < KT / 16; ++ks) {
+            v8 fa[MI], fb[NI];
+#pragma unroll
+            for (int i = 0; i < MI; ++i) fa[i] = frag_load<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
+#pragma unroll
+            for (int j = 0; j < NI; ++j) fb[j] = frag_load<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
+        }
+        if (more) {
+            if constexpr (!AK) {
+                if (do_rsum) rowsum_acc<T, BM, NT>(rs, ra);
+            }
+            T* da = smem + ((kt + 1) & 1) * STAGE;
+            tile_store<T, AK, BM, NT, false>(da, ra, tid);
+            tile_store<T, BKM, BN, NT, BGELU>(da + GA::ELEMS, rb, tid);
+        }
+        __syncthreads();
+    }
+
+    if constexpr (!AK) {
+        if (do_rsum) {
+            // threads tid, tid + R/8, tid + 2R/8, ... hold the same 8 rows:
+            // add them in that order through LDS (free after the main loop)
+            constexpr int CPR = BM / 8;
+            float* red = reinterpret_cast<float*>(smem_raw);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[tid * 8 + e] = rs[e];
+            __syncthreads();
+            if (tid < CPR) {
+                float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (int q = tid; q < NT; q += CPR)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] += red[q * 8 + e];
+                const int mrow = m0 + tid * 8;
+                if (gridDim.z > 1) {
+                    float* out = reinterpret_cast<float*>(p.rsum) + (size_t)blockIdx.z * p.M + mrow;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out[e] = t[e];
+                } else {
+                    T* out = reinterpret_cast<T*>(p.rsum) + mrow;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out[e] = from_f<T>(t[e]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+
+    gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
+}
+
+// ------------------------------------------------------------------ direct-load path
+// Tiles of 32 k per stage, 4 stages in LDS.  Operand data goes from global
+// memory straight into LDS (global_load_lds_dwordx4: lane i of a wave writes
+// 16 bytes at the wave's LDS base + 16 i), so no registers stage it and no
+// LDS-store instructions sit in the MFMA stream; loads run three k-tiles
+// ahead.  Both operand layouts are stored unpadded with an XOR swizzle of
+// their 16-byte chunks, chosen so the fragment reads are bank-conflict free
+// (k-major rows of 64 bytes: chunk ^ ((row >> 2) & 3); m/n-major rows of
+// R >= 128 elements: chunk ^ 4 (k & 3)).
+constexpr int DKT = 32;    // k per stage
+constexpr int DNS = 4;     // stages
+
+__device__ __forceinline__ int kmaj32_off(int row, int k) {
+    return row * 32 + (((k >> 3) ^ ((row >> 2) & 3)) << 3) + (k & 7);
+}
+template <int R>
+__device__ __forceinline__ int mn32_off(int k, int col) {
+    return k * R + (((col >> 3) ^ (4 * (k & 3))) << 3) + (col & 7);
+}
+
+// One wave-wide direct load: lane i copies 16 bytes from src to LDS
+// lds_base + 16 i.  Written as inline asm on purpose: the compiler would
+// otherwise treat every later LDS read as dependent on every direct load in
+// flight and wait for all of them, serialising the stage ring.  The
+// instruction has no result registers (its inputs, the address and M0, are
+// read at issue); its completion is ordered explicitly with s_waitcnt vmcnt
+// and the workgroup barrier before any wave reads the stage.
+__device__ __forceinline__ void dl_load16(const void* src, const void* lds_base) {
+    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0v) : "memory", "m0");
+}
+
+// Issue the direct loads of one operand tile (R rows of m or n, 32 of k):
+// R*32*2/1024 wave-instructions spread over the NW waves.
+template <typename T, bool KMAJ, int R, int NW>
+__device__ __forceinline__ void dl_issue(T* lds, const T* base, int ld, int row0, int k0, int wave, int lane) {
+    constexpr int NQ = R * DKT * (int)sizeof(T) / 1024;
+    static_assert(NQ % NW == 0, "tile/wave mismatch");
+#pragma unroll
+    for (int j = 0; j < NQ / NW; ++j) {
+        const int q = wave + j * NW;
+        const int slot = q * 64 + lane;  // 16-byte slot of the tile this lane fills
+        const T* src;
+        if constexpr (KMAJ) {
+            const int row = slot >> 2, p = slot & 3;
+            const int c = p ^ ((row >> 2) & 3);
+            src = base + (size_t)(row0 + row) * ld + k0 + c * 8;
+        } else {
+            constexpr int CPR = R / 8;
+            const int k = slot / CPR, p = slot % CPR;
+            const int ch = p ^ (4 * (k & 3));
+            src = base + (size_t)(k0 + k) * ld + row0 + ch * 8;
+        }
+        dl_load16(src, lds + q * 512);
+    }
+}
+
+template <typename T, bool KMAJ, int R>
+__device__ __forceinline__ typename MfmaOp<T>::v8 dl_frag(const T* lds, int rb, int ks, int lane) {
+    if constexpr (KMAJ) {
+        typedef typename MfmaOp<T>::v8 v8;
+        const int row = rb + (lane & 31);
+        return *reinterpret_cast<const v8*>(lds + kmaj32_off(row, ks * 16 + (lane >> 5) * 8));
+    } else {
+        const int i = lane & 15, G = lane >> 4;
+        const int k0 = ks * 16 + (G >> 1) * 8 + (i >> 2);
+        const int col = rb + (G & 1) * 16 + (i & 3) * 4;
+        const i16x4 lo = ds_read_tr16(lds + mn32_off<R>(k0, col));
+        const i16x4 hi = ds_read_tr16(lds + mn32_off<R>(k0 + 4, col));
+        return join8<T>(lo, hi);
+    }
+}
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
+__global__ __launch_bounds__(WGM* WGN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_dl_kernel(GemmParams p) {
+    constexpr int NW = WGM * WGN, NT = NW * 64;
+    constexpr int WM = BM / WGM, WN = BN / WGN;
+    constexpr int MI = WM / 32, NI = WN / 32;
+    constexpr int AEL = BM * DKT, BEL = BN * DKT, STAGE = AEL + BEL;
+    constexpr int LPW = (AEL + BEL) * (int)sizeof(T) / 1024 / NW;  // direct loads per wave per stage
+    typedef typename MfmaOp<T>::v8 v8;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* smem = reinterpret_cast<T*>(smem_raw);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave / WGN, wn = wave % WGN;
+    const int tm = p.M / BM, tn = p.N / BN;
+    int im, in_;
+    tile_of(blockIdx.x, tm, tn, im, in_);
+    const int m0 = im * BM, n0 = in_ * BN;
+    const int kbeg = blockIdx.z * p.k_per_split;
+    const int kend = min(p.K, kbeg + p.k_per_split);
+    const int nk = (kend - kbeg) / DKT;
+    const T* A = (const T*)p.A;
+    const T* B = (const T*)p.B;
+
+    // bias gradient fused into a weight gradient (tile column 0 only): each
+    // thread sums a fixed 8-row chunk of A over the k rows it reads from LDS
+    const bool do_rsum = !AK && p.rsum != nullptr && in_ == 0;
+    float rs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+
+    f32x16 acc[MI][NI];
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    auto issue = [&](int kt) {
+        T* st = smem + (kt % DNS) * STAGE;
+        dl_issue<T, AK, BM, NW>(st, A, p.lda, m0, kbeg + kt * DKT, wave, lane);
+        dl_issue<T, BKM, BN, NW>(st + AEL, B, p.ldb, n0, kbeg + kt * DKT, wave, lane);
+    };
+    // fragments of one 16-wide k-step of a stage
+    auto read_ks = [&](int kt, int ks, v8 (&fa)[MI], v8 (&fb)[NI]) {
+        const T* sa = smem + (kt % DNS) * STAGE;
+        const T* sb = sa + AEL;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) fa[i] = dl_frag<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
+#pragma unroll
+        for (int j = 0; j < NI; ++j) fb[j] = dl_frag<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
+    };
+    auto rowsums = [&](int kt) {
+        if constexpr (!AK) {
+            if (do_rsum) {
+                const T* sa = smem + (kt % DNS) * STAGE;
+                constexpr int CPR = BM / 8;
+#pragma unroll
+                for (int c = tid; c < DKT * CPR; c += NT) {
+                    const int k = c / CPR;
+                    typedef T t8 __attribute__((ext_vector_type(8)));
+                    const t8 x = *reinterpret_cast<const t8*>(sa + mn32_off<BM>(k, (c % CPR) * 8));
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) rs[e] += to_f(x[e]);
+                }
+            }
+        }
+    };
+    auto mfmas = [&](const v8 (&fa)[MI], const v8 (&fb)[NI]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
+    };
+
+#pragma unroll
+    for (int s0 = 0; s0 < DNS - 1; ++s0)
+        if (s0 < nk) issue(s0);
+    if (nk > 2) wait_vmcnt<2 * LPW>();
+    else if (nk > 1) wait_vmcnt<LPW>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    // Per k-tile kt (fragments of its first k-step already in f0):
+    //   read its second k-step -> f1; MFMAs on f0;
+    //   make tile kt+1 visible (its loads landed on every wave; every wave is
+    //   past tile kt-1, whose stage the loads of tile kt+3 now overwrite);
+    //   read tile kt+1's first k-step -> f0; MFMAs on f1.
+    v8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+    read_ks(0, 0, fa0, fb0);
+    for (int kt = 0; kt < nk; ++kt) {
+        read_ks(kt, 1, fa1, fb1);
+        rowsums(kt);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kt + 1 < nk) {
+            if (kt + 2 < nk) wait_vmcnt<LPW>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (kt + DNS - 1 < nk) issue(kt + DNS - 1);
+            read_ks(kt + 1, 0, fa0, fb0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+
+    if constexpr (!AK) {
+        if (do_rsum) {
+            // threads tid, tid + CPR, ... hold the same 8 rows: add in that order
+            constexpr int CPR = BM / 8;
+            float* red = reinterpret_cast<float*>(smem_raw);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) red[tid * 8 + e] = rs[e];
+            __syncthreads();
+            if (tid < CPR) {
+                float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                for (int q = tid; q < NT; q += CPR)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) t[e] += red[q * 8 + e];
+                const int mrow = m0 + tid * 8;
+                if (gridDim.z > 1) {
+                    float* out = reinterpret_cast<float*>(p.rsum) + (size_t)blockIdx.z * p.M + mrow;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out[e] = t[e];
+                } else {
+                    T* out = reinterpret_cast<T*>(p.rsum) + mrow;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out[e] = from_f<T>(t[e]);
+                }
+            }
+            __syncthreads();
+        }
+    }
+    gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
+}
+
 // Deterministic split-K reduction: out[m][n] = sum_z ws[z][m][n] in z order.
+// The first M/4 threads also add the per-split row sums (bias gradients).
 template <typename T>
-__global__ void splitk_reduce_kernel(const float* ws, int splits, int M, int N, EpiArgs ea) {
+__global__ void splitk_reduce_kernel(const float* ws, int splits, int M, int N, EpiArgs ea, const float* rs_part,
+                                     T* rs_out) {
     const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
     const size_t MN = (size_t)M * N;
+    if (rs_out && i4 < (size_t)M) {
+        float r[4] = {0, 0, 0, 0};
+        for (int z = 0; z < splits; ++z) {
+            float t[4];
+            Vec4<float>::load(rs_part + (size_t)z * M + i4, t);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) r[i] += t[i];
+        }
+        Vec4<T>::store(rs_out + i4, r);
+    }
     if (i4 >= MN) return;
     float v[4] = {0, 0, 0, 0};
     for (int z = 0; z < splits; ++z) {
@@ -419,7 +727,7 @@ static int splitk_for(const GemmDesc& g, int BM, int BN) {
     const int ksteps = g.K / KT;
     int s = 1;
     while (tiles * s < 256 && s * 2 <= ksteps / 8 && ksteps % (s * 2) == 0) s *= 2;
-    if ((size_t)s * g.M * g.N > g.splitk_ws_elems) s = 1;
+    if ((size_t)s * g.M * g.N + (size_t)s * g.M > g.splitk_ws_elems) s = 1;
     return s;
 }
 
@@ -442,7 +750,9 @@ static hipError_t set_lds(Kern k, size_t bytes) {
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
 static hipError_t launch_mfma(const GemmDesc& g, hipStream_t st, int splits) {
-    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws};
+    float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
+    void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
+    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
     auto kern = gemm_mfma_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI, BGELU>;
     const size_t lds = 2 * (TileGeom<AK, BM>::ELEMS + TileGeom<BKM, BN>::ELEMS) * sizeof(T);
     static bool attr_done = false;
@@ -457,12 +767,53 @@ static hipError_t launch_mfma(const GemmDesc& g, hipStream_t st, int splits) {
     if (e != hipSuccess || splits == 1) return e;
     const size_t n4 = (size_t)g.M * g.N / 4;
     hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea);
+                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea, rs_part,
+                       rsum ? reinterpret_cast<T*>(g.rowsum_out) : (T*)nullptr);
+    return hipGetLastError();
+}
+
+template <int BM, int BN, int WGN>
+constexpr size_t epilogue_lds_bytes() {
+    return (size_t)(WGN * 2) * 32 * (BN / WGN + 4) * 4;  // 4 waves x 32 rows x (WN + 4) floats
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
+static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
+    float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
+    void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
+    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
+    auto kern = gemm_dl_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI>;
+    size_t lds = (size_t)DNS * (BM + BN) * DKT * sizeof(T);
+    lds = std::max(lds, epilogue_lds_bytes<BM, BN, WGN>());
+    lds = std::max(lds, (size_t)WGM * WGN * 64 * 8 * 4);
+    static bool attr_done = false;
+    if (!attr_done) {
+        hipError_t e = set_lds(kern, lds);
+        if (e != hipSuccess) return e;
+        attr_done = true;
+    }
+    dim3 grid((g.M / BM) * (g.N / BN), 1, splits);
+    hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const size_t n4 = (size_t)g.M * g.N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea, rs_part,
+                       rsum ? reinterpret_cast<T*>(g.rowsum_out) : (T*)nullptr);
     return hipGetLastError();
 }
 
 template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
 static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
+    if constexpr (!BGELU && AK) {
+        // projections and input gradients stream their operands straight into
+        // LDS; weight gradients (both operands m/n-major) and the GELU-on-load
+        // variant use the register-staged kernel, which measured faster there
+        // and can transform B on its way to LDS
+        if (c.BM == 256 && c.BN == 256) return launch_dl<T, 256, 256, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+        if (c.BM == 256 && c.BN == 128) return launch_dl<T, 256, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+        return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
+    }
     if (c.BM == 256 && c.BN == 256) {
         int s = splitk_for(g, 256, 256);
         return launch_mfma<T, 256, 256, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
@@ -501,7 +852,7 @@ static hipError_t dispatch_mfma(const GemmDesc& g, hipStream_t st, TileCfg c) {
 
 template <typename T, int EPI, bool BGELU>
 static hipError_t launch_simt(const GemmDesc& g, hipStream_t st) {
-    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K, g.ea, nullptr};
+    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K, g.ea, nullptr, nullptr};
     dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
     hipLaunchKernelGGL((gemm_simt_kernel<T, EPI, BGELU>), grid, dim3(256), 0, st, p, (int)g.a_kmajor,
                        (int)g.b_kmajor);
@@ -564,7 +915,12 @@ size_t gemm_splitk_elems(const GemmDesc& g) {
     h.splitk_ws = reinterpret_cast<float*>(16);
     h.splitk_ws_elems = (size_t)-1;
     const int s = splitk_for(h, c.BM, c.BN);
-    return s > 1 ? (size_t)s * g.M * g.N : 0;
+    return s > 1 ? (size_t)s * g.M * g.N + (size_t)s * g.M : 0;
+}
+
+bool gemm_rowsum_fused(const GemmDesc& g) {
+    if (g.dtype == 0 || g.a_kmajor || g.b_kmajor || g.epi != EPI_STORE) return false;
+    return pick_tiles(g).BM != 0;
 }
 
 }  // namespace tel

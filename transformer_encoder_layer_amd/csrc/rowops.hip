@@ -13,7 +13,6 @@
 
 namespace tel {
 
-constexpr int LN_MAXC = 16;   // H <= 64 lanes * 4 * 16 = 4096
 
 template <typename T>
 __device__ __forceinline__ void load4(const void* p, int is_f32, size_t off, float v[4]) {
@@ -26,19 +25,28 @@ __device__ __forceinline__ void store4(void* p, int is_f32, size_t off, const fl
     else Vec4<T>::store((T*)p + off, v);
 }
 
-template <typename T>
+// Lane layout shared by the LayerNorm kernels: one 64-lane wave per row;
+// lane l holds the NC groups of 4 consecutive columns c*256 + 4l .. +3
+// (c < NC, NC = ceil(H / 256)), so each load or store of a group is one
+// 8- or 16-byte access and a wave covers 256 contiguous columns per group.
+template <int NC>
+__device__ __forceinline__ bool col_ok(int c, int lane, int H) { return c * 256 + lane * 4 < H; }
+
+template <typename T, int NC>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (row >= a.T) return;
     const int H = a.H;
     const size_t base = (size_t)row * H;
-    float v[LN_MAXC][4];
+    float v[NC][4];
     float s = 0.0f;
 #pragma unroll
-    for (int c = 0; c < LN_MAXC; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int idx = c * 256 + lane * 4;
-        if (idx < H) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[c][i] = 0.0f;
+        if (col_ok<NC>(c, lane, H)) {
             load4<T>(a.x, a.x_f32, base + idx, v[c]);
             s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
         }
@@ -46,9 +54,8 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const float mean = wave_sum(s) / (float)H;
     float s2 = 0.0f;
 #pragma unroll
-    for (int c = 0; c < LN_MAXC; ++c) {
-        const int idx = c * 256 + lane * 4;
-        if (idx < H) {
+    for (int c = 0; c < NC; ++c) {
+        if (col_ok<NC>(c, lane, H)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float dlt = v[c][i] - mean;
@@ -59,9 +66,9 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const float var = wave_sum(s2) / (float)H;
     const float rs = 1.0f / sqrtf(var + a.eps);
 #pragma unroll
-    for (int c = 0; c < LN_MAXC; ++c) {
+    for (int c = 0; c < NC; ++c) {
         const int idx = c * 256 + lane * 4;
-        if (idx < H) {
+        if (col_ok<NC>(c, lane, H)) {
             float g[4], b[4], y[4];
             Vec4<T>::load((const T*)a.gamma + idx, g);
             Vec4<T>::load((const T*)a.beta + idx, b);
@@ -78,118 +85,107 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     }
 }
 
-// LayerNorm backward: one workgroup per LN_ROWS rows, one thread per 4
-// consecutive columns (H/4 threads).  Rows are processed LN_RB at a time; the
-// two per-row sums (of g*gamma and g*gamma*xhat) are reduced across the
-// workgroup in a fixed order.  Each thread keeps the dgamma/dbeta partial
-// sums of its own 4 columns over the workgroup's rows, so the per-workgroup
-// partial rows need no further reduction inside the kernel.
-constexpr int LN_ROWS = 32;
-constexpr int LN_RB = 4;
+// LayerNorm backward: 4 waves per workgroup, each wave LN_RPW rows (two at
+// a time, so that twice the loads are in flight).  Per row: gh = dy * gamma,
+// dx = rstd * (gh - mean(gh) - xhat * mean(gh * xhat)) with the two means
+// reduced by wave shuffles; dgamma/dbeta partials stay in the lanes' own
+// columns and are added over the 4 waves in fixed order at the end, giving
+// one partial row per workgroup.
+constexpr int LN_RPW = 4;
 
-template <typename T>
-__global__ __launch_bounds__(1024) void ln_bwd_kernel(LnBwdArgs a) {
-    __shared__ float red[2][16][LN_RB];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+template <typename T, int NC>
+__global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
+    __shared__ float red[4][NC * 256];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H;
-    const int c4 = tid * 4;
-    const bool act = c4 < H;
-    float gam[4] = {0, 0, 0, 0}, bet[4] = {0, 0, 0, 0};
-    if (act) {
-        Vec4<T>::load((const T*)a.gamma + c4, gam);
-        if (a.from_output) Vec4<T>::load((const T*)a.beta + c4, bet);
+    float gam[NC][4], bet[NC][4], pg[NC][4], pb[NC][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { gam[c][i] = 1.0f; bet[c][i] = 0.0f; pg[c][i] = 0.0f; pb[c][i] = 0.0f; }
+        if (col_ok<NC>(c, lane, H)) {
+            Vec4<T>::load((const T*)a.gamma + c * 256 + lane * 4, gam[c]);
+            if (a.from_output) Vec4<T>::load((const T*)a.beta + c * 256 + lane * 4, bet[c]);
+        }
     }
-    float pg[4] = {0, 0, 0, 0}, pb[4] = {0, 0, 0, 0};
-    const int rbeg = blockIdx.x * LN_ROWS;
-    const int rend = min(a.T, rbeg + LN_ROWS);
-    for (int r0 = rbeg; r0 < rend; r0 += LN_RB) {
-        float dy[LN_RB][4], xh[LN_RB][4], s1[LN_RB], s2[LN_RB];
+    const int row0 = (blockIdx.x * 4 + wave) * LN_RPW;
+    for (int rr = 0; rr < LN_RPW; rr += 2) {
+        float dy[2][NC][4], xh[2][NC][4], r[2][NC][4];
+        float s1[2] = {0, 0}, s2[2] = {0, 0}, rsv[2] = {0, 0};
 #pragma unroll
-        for (int rb = 0; rb < LN_RB; ++rb) {
-            const int row = r0 + rb;
-            s1[rb] = 0.0f;
-            s2[rb] = 0.0f;
+        for (int u = 0; u < 2; ++u) {
+            const int row = row0 + rr + u;
+            const bool rok = row < a.T;
+            const size_t base = (size_t)(rok ? row : 0) * H;
+            const float rs = rok ? a.rstd[row] : 0.0f;
+            const float mu = (rok && !a.from_output) ? a.mu[row] : 0.0f;
+            rsv[u] = rs;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) { dy[rb][i] = 0.0f; xh[rb][i] = 0.0f; }
-            if (row < rend && act) {
-                const size_t off = (size_t)row * H + c4;
-                float sv[4];
-                Vec4<T>::load((const T*)a.dout + off, dy[rb]);
-                if (a.dout_add) {
-                    float t[4];
-                    Vec4<float>::load(a.dout_add + off, t);
+            for (int c = 0; c < NC; ++c) {
+                const int idx = c * 256 + lane * 4;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) dy[rb][i] += t[i];
+                for (int i = 0; i < 4; ++i) { dy[u][c][i] = 0.0f; xh[u][c][i] = 0.0f; r[u][c][i] = 0.0f; }
+                if (rok && col_ok<NC>(c, lane, H)) {
+                    float sv[4];
+                    Vec4<T>::load((const T*)a.dout + base + idx, dy[u][c]);
+                    if (a.dout_add) {
+                        float t[4];
+                        Vec4<float>::load(a.dout_add + base + idx, t);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dy[u][c][i] += t[i];
+                    }
+                    load4<T>(a.src, a.src_f32, base + idx, sv);
+                    if (a.res) load4<T>(a.res, a.res_f32, base + idx, r[u][c]);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        xh[u][c][i] = a.from_output ? (sv[i] - bet[c][i]) / gam[c][i] : (sv[i] - mu) * rs;
+                        const float gh = dy[u][c][i] * gam[c][i];
+                        s1[u] += gh;
+                        s2[u] += gh * xh[u][c][i];
+                        pg[c][i] += dy[u][c][i] * xh[u][c][i];
+                        pb[c][i] += dy[u][c][i];
+                    }
                 }
-                load4<T>(a.src, a.src_f32, off, sv);
-                const float rs = a.rstd[row];
-                const float mu = a.from_output ? 0.0f : a.mu[row];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    xh[rb][i] = a.from_output ? (sv[i] - bet[i]) / gam[i] : (sv[i] - mu) * rs;
-                    const float gh = dy[rb][i] * gam[i];
-                    s1[rb] += gh;
-                    s2[rb] += gh * xh[rb][i];
-                    pg[i] += dy[rb][i] * xh[rb][i];
-                    pb[i] += dy[rb][i];
-                }
             }
         }
 #pragma unroll
-        for (int rb = 0; rb < LN_RB; ++rb) {
-            s1[rb] = wave_sum(s1[rb]);
-            s2[rb] = wave_sum(s2[rb]);
-        }
-        if (lane == 0) {
+        for (int u = 0; u < 2; ++u) {
+            const int row = row0 + rr + u;
+            if (row >= a.T) continue;
+            const float mg = wave_sum(s1[u]) / (float)H;
+            const float mgx = wave_sum(s2[u]) / (float)H;
+            const size_t base = (size_t)row * H;
 #pragma unroll
-            for (int rb = 0; rb < LN_RB; ++rb) {
-                red[0][wave][rb] = s1[rb];
-                red[1][wave][rb] = s2[rb];
-            }
-        }
-        __syncthreads();
-        float mg[LN_RB], mgx[LN_RB];
-#pragma unroll
-        for (int rb = 0; rb < LN_RB; ++rb) {
-            float t1 = 0.0f, t2 = 0.0f;
-            for (int w = 0; w < nw; ++w) {
-                t1 += red[0][w][rb];
-                t2 += red[1][w][rb];
-            }
-            mg[rb] = t1 / (float)H;
-            mgx[rb] = t2 / (float)H;
-        }
-        __syncthreads();
-#pragma unroll
-        for (int rb = 0; rb < LN_RB; ++rb) {
-            const int row = r0 + rb;
-            if (row < rend && act) {
-                const size_t off = (size_t)row * H + c4;
-                const float rs = a.rstd[row];
+            for (int c = 0; c < NC; ++c) {
+                const int idx = c * 256 + lane * 4;
+                if (!col_ok<NC>(c, lane, H)) continue;
                 float dx[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) dx[i] = rs * (dy[rb][i] * gam[i] - mg[rb] - xh[rb][i] * mgx[rb]);
-                if (a.res) {
-                    float r[4];
-                    load4<T>(a.res, a.res_f32, off, r);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) dx[i] += r[i];
-                }
-                store4<T>(a.out, a.out_f32, off, dx);
+                for (int i = 0; i < 4; ++i)
+                    dx[i] = rsv[u] * (dy[u][c][i] * gam[c][i] - mg - xh[u][c][i] * mgx) + r[u][c][i];
+                store4<T>(a.out, a.out_f32, base + idx, dx);
                 if (a.drop_out) {
                     if (a.drop.thr) {
-                        const uint32_t k = keep4(a.drop.rng, off >> 2, a.drop.thr);
+                        const uint32_t k = keep4(a.drop.rng, (base + idx) >> 2, a.drop.thr);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dx[i] = ((k >> i) & 1u) ? dx[i] * a.drop.scale : 0.0f;
                     }
-                    Vec4<T>::store((T*)a.drop_out + off, dx);
+                    Vec4<T>::store((T*)a.drop_out + base + idx, dx);
                 }
             }
         }
     }
-    if (act) {
-        Vec4<float>::store(a.part_g + (size_t)blockIdx.x * H + c4, pg);
-        Vec4<float>::store(a.part_b + (size_t)blockIdx.x * H + c4, pb);
+    for (int which = 0; which < 2; ++which) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) red[wave][c * 256 + lane * 4 + i] = which ? pb[c][i] : pg[c][i];
+        __syncthreads();
+        for (int j = threadIdx.x; j < H; j += 256) {
+            const float v = (red[0][j] + red[1][j]) + (red[2][j] + red[3][j]);
+            (which ? a.part_b : a.part_g)[(size_t)blockIdx.x * H + j] = v;
+        }
+        __syncthreads();
     }
 }
 
@@ -262,30 +258,54 @@ __global__ __launch_bounds__(256) void mask_dump_kernel(Drop d, uint8_t* out, si
 }
 
 // ------------------------------------------------------------------ launchers
-hipError_t ln_forward(const LnFwdArgs& a, hipStream_t st) {
-    dim3 grid((a.T + 3) / 4);
-    switch (a.dtype) {
-        case 0: hipLaunchKernelGGL(ln_fwd_kernel<float>, grid, dim3(256), 0, st, a); break;
-        case 1: hipLaunchKernelGGL(ln_fwd_kernel<f16>, grid, dim3(256), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(ln_fwd_kernel<bf16>, grid, dim3(256), 0, st, a); break;
-        default: return hipErrorInvalidValue;
+template <typename T>
+static hipError_t ln_forward_t(const LnFwdArgs& a, hipStream_t st) {
+    dim3 grid((a.T + 3) / 4), blk(256);
+    switch ((a.H + 255) / 256) {
+        case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, blk, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((ln_fwd_kernel<T, 3>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4>), grid, blk, 0, st, a); break;
+        case 5: case 6: hipLaunchKernelGGL((ln_fwd_kernel<T, 6>), grid, blk, 0, st, a); break;
+        case 7: case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8>), grid, blk, 0, st, a); break;
+        default: hipLaunchKernelGGL((ln_fwd_kernel<T, 16>), grid, blk, 0, st, a); break;
     }
     return hipGetLastError();
 }
 
-int ln_backward_parts(int T) { return (T + LN_ROWS - 1) / LN_ROWS; }
-
-hipError_t ln_backward(const LnBwdArgs& a, hipStream_t st) {
-    dim3 grid(ln_backward_parts(a.T));
-    const int thr = ((a.H / 4 + 63) / 64) * 64;
-    if (thr > 1024) return hipErrorInvalidValue;
+hipError_t ln_forward(const LnFwdArgs& a, hipStream_t st) {
     switch (a.dtype) {
-        case 0: hipLaunchKernelGGL(ln_bwd_kernel<float>, grid, dim3(thr), 0, st, a); break;
-        case 1: hipLaunchKernelGGL(ln_bwd_kernel<f16>, grid, dim3(thr), 0, st, a); break;
-        case 2: hipLaunchKernelGGL(ln_bwd_kernel<bf16>, grid, dim3(thr), 0, st, a); break;
-        default: return hipErrorInvalidValue;
+        case 0: return ln_forward_t<float>(a, st);
+        case 1: return ln_forward_t<f16>(a, st);
+        case 2: return ln_forward_t<bf16>(a, st);
+    }
+    return hipErrorInvalidValue;
+}
+
+int ln_backward_parts(int T) { return (T + 4 * LN_RPW - 1) / (4 * LN_RPW); }
+
+template <typename T>
+static hipError_t ln_backward_t(const LnBwdArgs& a, hipStream_t st) {
+    dim3 grid(ln_backward_parts(a.T)), blk(256);
+    switch ((a.H + 255) / 256) {
+        case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((ln_bwd_kernel<T, 3>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, st, a); break;
+        case 5: case 6: hipLaunchKernelGGL((ln_bwd_kernel<T, 6>), grid, blk, 0, st, a); break;
+        case 7: case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), grid, blk, 0, st, a); break;
+        default: return hipErrorInvalidValue;  // H <= 2048 (LDS of the partial reduction)
     }
     return hipGetLastError();
+}
+
+hipError_t ln_backward(const LnBwdArgs& a, hipStream_t st) {
+    switch (a.dtype) {
+        case 0: return ln_backward_t<float>(a, st);
+        case 1: return ln_backward_t<f16>(a, st);
+        case 2: return ln_backward_t<bf16>(a, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t colsum_finalize(int dtype, const float* part, int P, int N, void* out, hipStream_t st) {

@@ -58,6 +58,7 @@ struct Buf {
 struct Plan {
     // saved (forward -> backward)
     Buf ln1_out, mu1, rs1, qkvh, ctx, lse, mu2, rs2, ln2_out, u, g;
+    Buf abits;    // attention keep bits, 1 per score (not kept under attention-dropout checkpointing)
     Buf res1;     // Pre-LN x1 (fp32) | Post-LN z1 (fp32)
     Buf x1e;      // Post-LN LN1 output, dtype
     Buf x1f;      // Post-LN LN1 output, fp32 (residual of the FFN branch)
@@ -118,7 +119,10 @@ static void make_plan(tel_layer* L) {
     const size_t BNS = (size_t)L->B * L->NH * L->S;
     const bool inv = L->cfg.normalize_invertible != 0;
     const bool gck = L->cfg.gelu_checkpoint != 0;
+    const bool keep_bits = L->cfg.attn_dropout > 0.0f && !L->cfg.attn_dropout_checkpoint &&
+                           L->d == 64 && L->S % 64 == 0 && L->cfg.dtype != TEL_F32;
     size_t sv = 0, sc = 0;
+    if (keep_bits) place(p.abits, BNS * (size_t)(L->S / 32) * 4, true, sv, sc);
     if (L->cfg.pre_ln) {
         place(p.ln1_out, T * H * e, true, sv, sc);
         place(p.mu1, T * f4, true, sv, sc);
@@ -191,7 +195,7 @@ static tel_status validate_cfg(const tel_config* c) {
         return fail(TEL_ERR_INVALID_ARG, "seq, hidden and ffn must be multiples of 16");
     const int d = c->hidden / c->heads;
     if (d != 16 && d != 32 && d != 64 && d != 128) return fail(TEL_ERR_UNSUPPORTED, "head width %d not in {16,32,64,128}", d);
-    if (c->hidden > 4096) return fail(TEL_ERR_UNSUPPORTED, "hidden %d > 4096", c->hidden);
+    if (c->hidden > 2048) return fail(TEL_ERR_UNSUPPORTED, "hidden %d > 2048", c->hidden);
     if (!(c->attn_dropout >= 0.0f && c->attn_dropout < 1.0f) || !(c->hidden_dropout >= 0.0f && c->hidden_dropout < 1.0f))
         return fail(TEL_ERR_INVALID_ARG, "dropout probabilities must lie in [0,1)");
     if (c->dtype != TEL_F32 && c->dtype != TEL_F16 && c->dtype != TEL_BF16)
@@ -315,6 +319,7 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     aa.dtype = dt; aa.B = L->B; aa.S = L->S; aa.NH = L->NH; aa.d = L->d;
     aa.qkvh = bs.of(p.qkvh); aa.len = key_lengths; aa.drop = d0;
     aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
+    aa.bits = p.abits.used ? (uint32_t*)bs.of(p.abits) : nullptr;
 
     auto proj = [&](const void* A, const void* W, int N, int K, int epi) {
         GemmDesc g;
@@ -420,7 +425,13 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         return g;
     };
     // dW[out][in] = dY^T . X, written to the caller's gradient (dtype)
-    auto wgrad = [&](const void* dY, const void* X, int out, int in, void* dW, bool gelu) {
+    auto bias_grad = [&](const void* dY, int N, void* out) -> hipError_t {
+        hipError_t e = colsum_partial(dt, dY, T, N, part_col, st);
+        if (e != hipSuccess) return e;
+        return colsum_finalize(dt, part_col, colP, N, out, st);
+    };
+    // dW = dY^T X and db = sum_t dY: fused into the GEMM when its kernel can
+    auto wgrad = [&](const void* dY, const void* X, int out, int in, void* dW, bool gelu, void* db) -> hipError_t {
         GemmDesc g;
         g.dtype = dt; g.M = out; g.N = in; g.K = T;
         g.A = dY; g.lda = out; g.a_kmajor = false;
@@ -429,12 +440,11 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g.epi = EPI_STORE;
         g.ea.out = dW; g.ea.ldo = in;
         g.splitk_ws = skws; g.splitk_ws_elems = skn;
-        return gemm_launch(g, st);
-    };
-    auto bias_grad = [&](const void* dY, int N, void* out) -> hipError_t {
-        hipError_t e = colsum_partial(dt, dY, T, N, part_col, st);
-        if (e != hipSuccess) return e;
-        return colsum_finalize(dt, part_col, colP, N, out, st);
+        const bool fused = gemm_rowsum_fused(g);
+        if (fused) g.rowsum_out = db;
+        hipError_t e = gemm_launch(g, st);
+        if (e != hipSuccess || fused) return e;
+        return bias_grad(dY, out, db);
     };
     auto ln_grads = [&](void* gg, void* gb) -> hipError_t {
         hipError_t e = colsum_finalize(dt, part_ln_g, lnP, H, gg, st);
@@ -447,6 +457,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     aa.qkvh = bs.of(p.qkvh); aa.len = key_lengths; aa.drop = d0;
     aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
     aa.dout = bs.of(p.dout); aa.dvec = (float*)bs.of(p.dvec); aa.dqkv = bs.of(p.dqkv);
+    aa.bits = p.abits.used ? (uint32_t*)bs.of(p.abits) : nullptr;
 
     const void* g_src = gck ? bs.of(p.u) : bs.of(p.g);  // FFN2 input (or GELU input to recompute it from)
 
@@ -456,13 +467,11 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, EPI_GELU_BWD);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck));
-        HIP_TRY(bias_grad(bs.of(p.df), H, G->b_2));
+        TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck, G->b_2));
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_FFN1_WGRAD, wgrad(bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, false));
-        HIP_TRY(bias_grad(bs.of(p.du), F, G->b_1));
+        TIMED(TEL_K_FFN1_WGRAD, wgrad(bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, false, G->b_1));
         // x1 -> LN2: dx1 = dy + LN2'(da2); dz = drop1(dx1)
         LnBwdArgs lb{};
         lb.dtype = dt; lb.T = T; lb.H = H;
@@ -480,15 +489,13 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
         g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
         TIMED(TEL_K_OUT_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false));
-        HIP_TRY(bias_grad(bs.of(p.dz), H, G->b_o));
+        TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false, G->b_o));
         TIMED(TEL_K_ATTN_BWD, attn_backward(aa, st));
         // QKV projection
         g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, false));
-        HIP_TRY(bias_grad(bs.of(p.dqkv), 3 * H, G->b_qkv));
+        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, false, G->b_qkv));
         // x -> LN1: dx = dx1 + LN1'(da1)
         lb = LnBwdArgs{};
         lb.dtype = dt; lb.T = T; lb.H = H;
@@ -517,13 +524,11 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, EPI_GELU_BWD);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck));
-        HIP_TRY(bias_grad(bs.of(p.df), H, G->b_2));
+        TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck, G->b_2));
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_FFN1_WGRAD, wgrad(bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, false));
-        HIP_TRY(bias_grad(bs.of(p.du), F, G->b_1));
+        TIMED(TEL_K_FFN1_WGRAD, wgrad(bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, false, G->b_1));
         // x1 = LN1(z1): dz1 = LN1'(dgemm + dz2); dz = drop1(dz1)
         lb = LnBwdArgs{};
         lb.dtype = dt; lb.T = T; lb.H = H;
@@ -539,15 +544,13 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
         g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
         TIMED(TEL_K_OUT_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false));
-        HIP_TRY(bias_grad(bs.of(p.dz), H, G->b_o));
+        TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false, G->b_o));
         TIMED(TEL_K_ATTN_BWD, attn_backward(aa, st));
         // dx = dz1 + dqkv W_qkv
         g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_ADD_RES);
         g.ea.out = dx; g.ea.ldo = H; g.ea.res = bs.of(p.dres);
         TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), x, 3 * H, H, G->w_qkv, false));
-        HIP_TRY(bias_grad(bs.of(p.dqkv), 3 * H, G->b_qkv));
+        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), x, 3 * H, H, G->w_qkv, false, G->b_qkv));
     }
     L->pending_fwd--;
     g_err.clear();
