@@ -281,19 +281,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
         const int n = n0 + wn * WN + cg * 4;
         float b[4] = {0, 0, 0, 0};
         E::load_bias(p.ea, n, b);
-        float el[32 / RPI][4];
+        // rows in chunks of CH: the chunk's element loads are issued together,
+        // then finished; the chunk loop stays rolled so that this block loop
+        // (which indexes acc) can be fully unrolled even with a large finish
+        constexpr int NIT = 32 / RPI, CH = NIT < 4 ? NIT : 4;
+#pragma unroll 1
+        for (int c0 = 0; c0 < NIT; c0 += CH) {
+            float el[CH][4];
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
+            for (int it = 0; it < CH; ++it) {
 #pragma unroll
-            for (int t = 0; t < 4; ++t) el[it][t] = 0.0f;
-            E::load_elem(p.ea, m0 + wm * WM + i * 32 + it * RPI + r0, n, el[it]);
-        }
+                for (int t = 0; t < 4; ++t) el[it][t] = 0.0f;
+                E::load_elem(p.ea, m0 + wm * WM + i * 32 + (c0 + it) * RPI + r0, n, el[it]);
+            }
 #pragma unroll
-        for (int it = 0; it < 32 / RPI; ++it) {
-            const int rr = it * RPI + r0;
-            const float4 q = *reinterpret_cast<const float4*>(est + rr * ELD + cg * 4);
-            float v[4] = {q.x, q.y, q.z, q.w};
-            E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, el[it]);
+            for (int it = 0; it < CH; ++it) {
+                const int rr = (c0 + it) * RPI + r0;
+                const float4 q = *reinterpret_cast<const float4*>(est + rr * ELD + cg * 4);
+                float v[4] = {q.x, q.y, q.z, q.w};
+                E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, el[it]);
+            }
         }
         __builtin_amdgcn_wave_barrier();
     }
