@@ -503,8 +503,7 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
-__global__ __launch_bounds__(WGM* WGN * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void gemm_dl_kernel(GemmParams p) {
+__global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
     constexpr int NW = WGM * WGN, NT = NW * 64;
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
@@ -739,8 +738,14 @@ static int splitk_for(const GemmDesc& g, int BM, int BN) {
 }
 
 static TileCfg pick_tiles(const GemmDesc& g) {
-    // largest tile whose grid still yields >= 256 workgroups, else 128x128
+    // largest tile whose grid still yields >= 256 workgroups, else 128x128;
+    // a weight gradient with at least 64 tiles of 256x256 takes them and
+    // fills the chip with a split-K of at most 4 (smaller ones measured
+    // faster on 128x128 tiles)
     const TileCfg cands[] = {{256, 256}, {256, 128}, {128, 128}};
+    if (!g.a_kmajor && !g.b_kmajor && g.epi == EPI_STORE && g.splitk_ws && mfma_ok(g, 256, 256) &&
+        (g.M / 256) * (g.N / 256) >= 64)
+        return {256, 256};
     for (const TileCfg& c : cands) {
         if (!mfma_ok(g, c.BM, c.BN)) continue;
         const int tiles = (g.M / c.BM) * (g.N / c.BN);
@@ -755,13 +760,20 @@ static hipError_t set_lds(Kern k, size_t bytes) {
                                (int)bytes);
 }
 
+template <int BM, int BN, int WGM, int WGN>
+constexpr size_t epilogue_lds_bytes() {
+    return (size_t)(WGM * WGN) * 32 * (BN / WGN + 4) * 4;  // every wave: 32 rows x (WN + 4) floats
+}
+
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
 static hipError_t launch_mfma(const GemmDesc& g, hipStream_t st, int splits) {
     float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
     void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
     GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
     auto kern = gemm_mfma_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI, BGELU>;
-    const size_t lds = 2 * (TileGeom<AK, BM>::ELEMS + TileGeom<BKM, BN>::ELEMS) * sizeof(T);
+    size_t lds = 2 * (TileGeom<AK, BM>::ELEMS + TileGeom<BKM, BN>::ELEMS) * sizeof(T);
+    lds = std::max(lds, epilogue_lds_bytes<BM, BN, WGM, WGN>());
+    lds = std::max(lds, (size_t)WGM * WGN * 64 * 8 * 4);  // row-sum reduction
     static bool attr_done = false;
     if (!attr_done) {
         hipError_t e = set_lds(kern, lds);
@@ -779,10 +791,6 @@ static hipError_t launch_mfma(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int WGN>
-constexpr size_t epilogue_lds_bytes() {
-    return (size_t)(WGN * 2) * 32 * (BN / WGN + 4) * 4;  // 4 waves x 32 rows x (WN + 4) floats
-}
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
 static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
@@ -791,7 +799,7 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
     auto kern = gemm_dl_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI>;
     size_t lds = (size_t)DNS * (BM + BN) * DKT * sizeof(T);
-    lds = std::max(lds, epilogue_lds_bytes<BM, BN, WGN>());
+    lds = std::max(lds, epilogue_lds_bytes<BM, BN, WGM, WGN>());
     lds = std::max(lds, (size_t)WGM * WGN * 64 * 8 * 4);
     static bool attr_done = false;
     if (!attr_done) {
@@ -810,6 +818,13 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
+// 256x256 tiles run 8 waves (2 per SIMD) in a 2 x 4 grid of 128x64 wave
+// tiles: the second wave of each SIMD issues its MFMAs while the first waits
+// on LDS or the barrier, which more than pays for the 1.5x LDS fragment
+// reads of the narrower wave tile.
+constexpr int W256N = 4;
+// 256x128 tiles likewise run 8 waves, in a 4 x 2 grid of 64x64 wave tiles.
+constexpr int W128M = 4;
 template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
 static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
     if constexpr (!BGELU && AK) {
@@ -817,17 +832,17 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
         // LDS; weight gradients (both operands m/n-major) and the GELU-on-load
         // variant use the register-staged kernel, which measured faster there
         // and can transform B on its way to LDS
-        if (c.BM == 256 && c.BN == 256) return launch_dl<T, 256, 256, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
-        if (c.BM == 256 && c.BN == 128) return launch_dl<T, 256, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+        if (c.BM == 256 && c.BN == 256) return launch_dl<T, 256, 256, 2, W256N, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+        if (c.BM == 256 && c.BN == 128) return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
         return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
     }
     if (c.BM == 256 && c.BN == 256) {
         int s = splitk_for(g, 256, 256);
-        return launch_mfma<T, 256, 256, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
+        return launch_mfma<T, 256, 256, 2, W256N, AK, BKM, EPI, BGELU>(g, st, s);
     }
     if (c.BM == 256 && c.BN == 128) {
         int s = splitk_for(g, 256, 128);
-        return launch_mfma<T, 256, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
+        return launch_mfma<T, 256, 128, W128M, 2, AK, BKM, EPI, BGELU>(g, st, s);
     }
     int s = splitk_for(g, 128, 128);
     return launch_mfma<T, 128, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
@@ -916,11 +931,12 @@ hipError_t gemm_launch(const GemmDesc& g, hipStream_t st, bool force_simt) {
 
 size_t gemm_splitk_elems(const GemmDesc& g) {
     if (g.dtype == 0) return 0;
-    TileCfg c = pick_tiles(g);
-    if (!c.BM) return 0;
+    // decide tiles and splits exactly as a launch with a workspace will
     GemmDesc h = g;
     h.splitk_ws = reinterpret_cast<float*>(16);
     h.splitk_ws_elems = (size_t)-1;
+    TileCfg c = pick_tiles(h);
+    if (!c.BM) return 0;
     const int s = splitk_for(h, c.BM, c.BN);
     return s > 1 ? (size_t)s * g.M * g.N + (size_t)s * g.M : 0;
 }
