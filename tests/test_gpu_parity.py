@@ -61,6 +61,13 @@ def test_small_lowp_ragged_seq(dtype):
 
 
 @pytest.mark.parametrize("dtype", ["f16", "bf16"])
+def test_small_lowp_seq64(dtype):
+    # S = 64: the single-workgroup attention backward with half its waves idle
+    w = syn.Workload("s64", 3, 64, 256, 4, 1024, True, dtype, 0.1, 0.1, 13, lengths=(1, 64))
+    _run(w, step=4)
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
 def test_small_lowp_d32_simt_attention(dtype):
     # head width 32 takes the generic attention kernel
     w = syn.Workload("d32", 2, 64, 128, 4, 512, False, dtype, 0.1, 0.1, 9, lengths=(5, 64))

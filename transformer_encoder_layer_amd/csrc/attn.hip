@@ -421,6 +421,215 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ MFMA bwd, S <= 128
+// The whole backward of one (batch, head) in one workgroup when S <= 128:
+// Q, dO and K fit in LDS, P is recomputed once, and no intermediate leaves
+// the chip.
+//   load:    Q, dO, K -> LDS; D_i = rowsum(dO_i * O_i), the log-sum-exp and
+//            the dropout keep words (stored bits, or regenerated) -> LDS.
+//   phase 1: wave w owns keys 32w .. 32w+31 (lane = key, register = query,
+//            as in the key-parallel kernel): S and dP for every query, then
+//            dV += P~^T dO and dK += dS^T Q accumulate in registers.
+//   phase 2: dS goes to LDS as [query][key] over the then-dead Q/dO tiles,
+//            and wave w computes dQ = dS K for queries 32w .. 32w+31.
+// Element (q, key) of the dS tile sits at q*S + ((key/8) ^ (q mod C))*8 +
+// key mod 8 (C = S/8 chunks of 16 bytes per row), so the 16 rows a 16-lane
+// group reads hit 16 distinct 16-byte bank groups.
+template <typename T>
+__global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
+    constexpr int D = 64, SMAX = 128;
+    typedef typename MfmaOp<T>::v8 v8;
+    __shared__ __align__(16) T lds[3 * SMAX * D];  // Q | dO | K; dS [S][S] overlays Q and dO
+    __shared__ float lse_s[SMAX], D_s[SMAX];
+    __shared__ uint32_t bits_s[SMAX][SMAX / 32];
+    T* Qs = lds;
+    T* dOs = lds + SMAX * D;
+    T* Ks = lds + 2 * SMAX * D;
+    T* dSs = lds;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
+    const int L = a.len ? a.len[b] : S;
+    const size_t head = (size_t)S * D;
+    const size_t bh = (size_t)b * NH + h;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const T* dO = (const T*)a.dout + bh * head;
+    const float c = kLog2e * 0.125f;
+    const int NW32 = S / 32;       // 32-key words per query row
+    const int CMASK = S / 8 - 1;   // dS row chunks - 1
+
+    // ---- load
+    for (int cidx = tid; cidx < S * 8; cidx += 256) {
+        const int row = cidx >> 3, ch = cidx & 7;
+        const size_t g = (size_t)row * D + ch * 8;
+        *reinterpret_cast<uint4*>(Qs + kmaj_off(row, ch * 8)) = *reinterpret_cast<const uint4*>(Q + g);
+        *reinterpret_cast<uint4*>(dOs + kmaj_off(row, ch * 8)) = *reinterpret_cast<const uint4*>(dO + g);
+        *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = *reinterpret_cast<const uint4*>(K + g);
+    }
+    {
+        // D_q: two threads per query row, 32 columns each
+        const int q = tid >> 1, half = tid & 1;
+        float part = 0.0f;
+        if (q < S) {
+            const T* orow = (const T*)a.ctx + (size_t)(b * S + q) * H + h * D + half * 32;
+            const T* drow = dO + (size_t)q * D + half * 32;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const v8 ov = *reinterpret_cast<const v8*>(orow + j * 8);
+                const v8 dv = *reinterpret_cast<const v8*>(drow + j * 8);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) part += to_f(dv[i]) * to_f(ov[i]);
+            }
+        }
+        part += __shfl_xor(part, 1, 64);
+        if (q < S && half == 0) {
+            D_s[q] = part;
+            lse_s[q] = a.lse[bh * S + q];
+        }
+    }
+    if (a.drop.thr) {
+        for (int cidx = tid; cidx < S * NW32; cidx += 256) {
+            const int q = cidx / NW32, w = cidx - q * NW32;
+            const uint64_t e0 = (bh * S + q) * (uint64_t)S + w * 32;  // element of key w*32
+            uint32_t word;
+            if (a.bits) {
+                word = a.bits[(bh * S + q) * NW32 + w];
+            } else {
+                word = 0;
+#pragma unroll
+                for (int g = 0; g < 8; ++g) word |= keep4(a.drop.rng, (e0 >> 2) + g, a.drop.thr) << (4 * g);
+            }
+            bits_s[q][w] = word;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 1: keys of this wave
+    const int kw0 = wave * 32;
+    const bool active = kw0 < S;
+    const int kl = kw0 + (lane & 31);
+    f32x16 dk[2], dv[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) { dk[ct][r] = 0.0f; dv[ct][r] = 0.0f; }
+    v8 dsf[SMAX / 32][2];  // dS of each 32-query tile as MFMA operands, kept for phase 2
+    if (active) {
+        v8 kf[4], vf[4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int off = ks * 16 + (lane >> 5) * 8;
+            kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)kl * D + off);
+            vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)kl * D + off);
+        }
+#pragma unroll
+        for (int qt = 0; qt < SMAX / 32; ++qt) {
+            if (qt * 32 < S) {
+                f32x16 sc, dp;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { sc[r] = 0.0f; dp[r] = 0.0f; }
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    sc = MfmaOp<T>::mma(frag_kmaj<T>(Qs, qt * 32, ks, lane), kf[ks], sc);
+                    dp = MfmaOp<T>::mma(frag_kmaj<T>(dOs, qt * 32, ks, lane), vf[ks], dp);
+                }
+                // sc[r]: query qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl
+                f32x16 ds;
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int qi = qt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                    const float p = kl < L ? exp2f(sc[r] * c - lse_s[qi]) : 0.0f;
+                    float f = 1.0f;
+                    if (a.drop.thr) f = ((bits_s[qi][wave] >> (kl & 31)) & 1u) ? a.drop.scale : 0.0f;
+                    ds[r] = p * (dp[r] * f - D_s[qi]);
+                    sc[r] = p * f;
+                }
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    v8 pf, sf;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        pf[i] = from_f<T>(sc[(2 * half) * 4 + i]);
+                        pf[4 + i] = from_f<T>(sc[(2 * half + 1) * 4 + i]);
+                        sf[i] = from_f<T>(ds[(2 * half) * 4 + i]);
+                        sf[4 + i] = from_f<T>(ds[(2 * half + 1) * 4 + i]);
+                    }
+                    const int qb0 = qt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct) {
+                        dv[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(dOs, ct * 32, qb0, qb0 + 8, lane), pf, dv[ct]);
+                        dk[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Qs, ct * 32, qb0, qb0 + 8, lane), sf, dk[ct]);
+                    }
+                    dsf[qt][half] = sf;
+                }
+            }
+        }
+    }
+    __syncthreads();  // every wave is done with Q and dO
+    if (active) {
+        // dsf[qt][half] element i (< 4): query qt*32 + 16*half + 4*(lane>>5) + i,
+        // element 4 + i: the same + 8; key kl
+#pragma unroll
+        for (int qt = 0; qt < SMAX / 32; ++qt) {
+            if (qt * 32 < S) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int q = qt * 32 + 16 * half + 4 * (lane >> 5) + (e & 3) + (e >> 2) * 8;
+                        dSs[q * S + ((((kl >> 3) ^ (q & CMASK))) << 3) + (kl & 7)] = dsf[qt][half][e];
+                    }
+            }
+        }
+        T* outk = (T*)a.dqkv + (size_t)(b * S + kl) * (3 * H) + H + h * D;
+        T* outv = outk + H;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float vk[4], vv[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    vk[i] = dk[ct][g * 4 + i] * 0.125f;
+                    vv[i] = dv[ct][g * 4 + i];
+                }
+                const int col = ct * 32 + g * 8 + (lane >> 5) * 4;
+                Vec4<T>::store(outk + col, vk);
+                Vec4<T>::store(outv + col, vv);
+            }
+    }
+    __syncthreads();
+
+    // ---- phase 2: dQ of queries 32w .. 32w+31
+    if (active) {
+        const int q = kw0 + (lane & 31);
+        f32x16 dq[2];
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dq[ct][r] = 0.0f;
+        for (int kb = 0; kb < S; kb += 16) {
+            const int r0 = kb + 8 * (lane >> 5);
+            const v8 bf = *reinterpret_cast<const v8*>(dSs + q * S + (((r0 >> 3) ^ (q & CMASK)) << 3));
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct)
+                dq[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Ks, ct * 32, r0, r0 + 4, lane), bf, dq[ct]);
+        }
+        T* out = (T*)a.dqkv + (size_t)(b * S + q) * (3 * H) + h * D;
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) v[i] = dq[ct][g * 4 + i] * 0.125f;
+                Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+            }
+    }
+}
+
 // ------------------------------------------------------------------ SIMT
 template <typename T, int D>
 __global__ __launch_bounds__(128) void attn_fwd_simt(AttnArgs a) {
@@ -601,6 +810,10 @@ static hipError_t fwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
 template <typename T>
 static hipError_t bwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
     if constexpr (!std::is_same<T, float>::value) {
+        if (!force_simt && mfma_attn_ok(a) && a.S <= 128) {
+            hipLaunchKernelGGL(attn_bwd_short_mfma<T>, dim3(1, a.NH, a.B), dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
         if (!force_simt && mfma_attn_ok(a)) {
             dim3 grid((a.S + 127) / 128, a.NH, a.B);
             hipLaunchKernelGGL(attn_bwd_dq_mfma<T>, grid, dim3(256), 0, st, a);

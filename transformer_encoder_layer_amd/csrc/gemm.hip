@@ -441,43 +441,55 @@ __device__ __forceinline__ int mn32_off(int k, int col) {
     return k * R + (((col >> 3) ^ (4 * (k & 3))) << 3) + (col & 7);
 }
 
-// One wave-wide direct load: lane i copies 16 bytes from src to LDS
-// lds_base + 16 i.  Written as inline asm on purpose: the compiler would
-// otherwise treat every later LDS read as dependent on every direct load in
-// flight and wait for all of them, serialising the stage ring.  The
-// instruction has no result registers (its inputs, the address and M0, are
-// read at issue); its completion is ordered explicitly with s_waitcnt vmcnt
-// and the workgroup barrier before any wave reads the stage.
-__device__ __forceinline__ void dl_load16(const void* src, const void* lds_base) {
-    const uint32_t m0v = __builtin_amdgcn_readfirstlane(
-        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)lds_base);
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" : : "v"(src), "s"(m0v) : "memory", "m0");
+// One wave-wide direct load: lane i copies the 16 bytes at sbase + voff to
+// LDS byte address m0v + 16 i (m0v wave-uniform).  The scalar-base form
+// keeps the per-lane offset fixed over the k loop: advancing to the next k
+// tile is one scalar add on sbase, and the LDS address is scalar arithmetic,
+// so a load costs two instructions.  Written as inline asm on purpose: the
+// compiler would otherwise treat every later LDS read as dependent on every
+// direct load in flight and wait for all of them, serialising the stage
+// ring.  The instruction has no result registers (its inputs are read at
+// issue); its completion is ordered explicitly with s_waitcnt vmcnt and the
+// workgroup barrier before any wave reads the stage.  M0 is written and
+// consumed inside the same statement, and nothing else in these kernels
+// uses it.
+__device__ __forceinline__ void dl_load16(const void* sbase, uint32_t voff, uint32_t m0v) {
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" : : "v"(voff), "s"(sbase), "s"(m0v)
+                 : "memory");
 }
 
-// Issue the direct loads of one operand tile (R rows of m or n, 32 of k):
-// R*32*2/1024 wave-instructions spread over the NW waves.
+// Direct-load plan of one operand tile (R rows of m or n, 32 of k) for one
+// wave: the wave issues PER of the tile's NQ wave-loads (q = wave + j*NW);
+// voff[j] is this lane's source byte offset from the tile origin (row0, k0).
 template <typename T, bool KMAJ, int R, int NW>
-__device__ __forceinline__ void dl_issue(T* lds, const T* base, int ld, int row0, int k0, int wave, int lane) {
-    constexpr int NQ = R * DKT * (int)sizeof(T) / 1024;
+struct DlPlan {
+    static constexpr int NQ = R * DKT * (int)sizeof(T) / 1024;
+    static constexpr int PER = NQ / NW;
     static_assert(NQ % NW == 0, "tile/wave mismatch");
+    uint32_t voff[PER];
+
+    __device__ __forceinline__ DlPlan(int ld, int wave, int lane) {
 #pragma unroll
-    for (int j = 0; j < NQ / NW; ++j) {
-        const int q = wave + j * NW;
-        const int slot = q * 64 + lane;  // 16-byte slot of the tile this lane fills
-        const T* src;
-        if constexpr (KMAJ) {
-            const int row = slot >> 2, p = slot & 3;
-            const int c = p ^ ((row >> 2) & 3);
-            src = base + (size_t)(row0 + row) * ld + k0 + c * 8;
-        } else {
-            constexpr int CPR = R / 8;
-            const int k = slot / CPR, p = slot % CPR;
-            const int ch = p ^ (4 * (k & 3));
-            src = base + (size_t)(k0 + k) * ld + row0 + ch * 8;
+        for (int j = 0; j < PER; ++j) {
+            const int slot = (wave + j * NW) * 64 + lane;  // 16-byte slot of the tile this lane fills
+            if constexpr (KMAJ) {
+                const int row = slot >> 2, p = slot & 3;
+                const int c = p ^ ((row >> 2) & 3);
+                voff[j] = (uint32_t)((row * ld + c * 8) * (int)sizeof(T));
+            } else {
+                constexpr int CPR = R / 8;
+                const int k = slot / CPR, p = slot % CPR;
+                const int ch = p ^ (4 * (k & 3));
+                voff[j] = (uint32_t)((k * ld + ch * 8) * (int)sizeof(T));
+            }
         }
-        dl_load16(src, lds + q * 512);
     }
-}
+    // tile whose origin is at byte address `origin`, into LDS bytes lds_bytes
+    __device__ __forceinline__ void issue(const char* origin, uint32_t lds_bytes, int wave) const {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) dl_load16(origin, voff[j], lds_bytes + (uint32_t)(wave + j * NW) * 1024u);
+    }
+};
 
 template <typename T, bool KMAJ, int R>
 __device__ __forceinline__ typename MfmaOp<T>::v8 dl_frag(const T* lds, int rb, int ks, int lane) {
@@ -517,126 +529,161 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / WGN, wn = wave % WGN;
     const int tm = p.M / BM, tn = p.N / BN;
-    int im, in_;
-    tile_of(blockIdx.x, tm, tn, im, in_);
-    const int m0 = im * BM, n0 = in_ * BN;
-    const int kbeg = blockIdx.z * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nk = (kend - kbeg) / DKT;
-    const T* A = (const T*)p.A;
-    const T* B = (const T*)p.B;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const DlPlan<T, AK, BM, NW> pa(p.lda, wave_s, lane);
+    const DlPlan<T, BKM, BN, NW> pb(p.ldb, wave_s, lane);
+    // Persistent over tiles: a workgroup takes tiles blockIdx.x, +gridDim.x,
+    // ...; the stores of one tile's epilogue drain while the next tile's
+    // loads and MFMAs run.
+    for (int pid = blockIdx.x; pid < tm * tn; pid += gridDim.x) {
+        if (pid != (int)blockIdx.x) __syncthreads();  // the last epilogue is done with LDS
+        int im, in_;
+        tile_of(pid, tm, tn, im, in_);
+        const int m0 = im * BM, n0 = in_ * BN;
+        const int kbeg = blockIdx.z * p.k_per_split;
+        const int kend = min(p.K, kbeg + p.k_per_split);
+        const int nk = (kend - kbeg) / DKT;
+        const T* A = (const T*)p.A;
+        const T* B = (const T*)p.B;
 
-    // bias gradient fused into a weight gradient (tile column 0 only): each
-    // thread sums a fixed 8-row chunk of A over the k rows it reads from LDS
-    const bool do_rsum = !AK && p.rsum != nullptr && in_ == 0;
-    float rs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        // bias gradient fused into a weight gradient (tile column 0 only): each
+        // thread sums a fixed 8-row chunk of A over the k rows it reads from LDS
+        const bool do_rsum = !AK && p.rsum != nullptr && in_ == 0;
+        float rs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 
-    f32x16 acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    auto issue = [&](int kt) {
-        T* st = smem + (kt % DNS) * STAGE;
-        dl_issue<T, AK, BM, NW>(st, A, p.lda, m0, kbeg + kt * DKT, wave, lane);
-        dl_issue<T, BKM, BN, NW>(st + AEL, B, p.ldb, n0, kbeg + kt * DKT, wave, lane);
-    };
-    // fragments of one 16-wide k-step of a stage
-    auto read_ks = [&](int kt, int ks, v8 (&fa)[MI], v8 (&fb)[NI]) {
-        const T* sa = smem + (kt % DNS) * STAGE;
-        const T* sb = sa + AEL;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) fa[i] = dl_frag<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
-#pragma unroll
-        for (int j = 0; j < NI; ++j) fb[j] = dl_frag<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
-    };
-    auto rowsums = [&](int kt) {
-        if constexpr (!AK) {
-            if (do_rsum) {
-                const T* sa = smem + (kt % DNS) * STAGE;
-                constexpr int CPR = BM / 8;
-#pragma unroll
-                for (int c = tid; c < DKT * CPR; c += NT) {
-                    const int k = c / CPR;
-                    typedef T t8 __attribute__((ext_vector_type(8)));
-                    const t8 x = *reinterpret_cast<const t8*>(sa + mn32_off<BM>(k, (c % CPR) * 8));
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) rs[e] += to_f(x[e]);
-                }
-            }
-        }
-    };
-    auto mfmas = [&](const v8 (&fa)[MI], const v8 (&fb)[NI]) {
+        f32x16 acc[MI][NI];
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
-    };
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+        // scalar tile origins (advanced by one k tile per issue) and LDS byte addresses
+        const char* oa = reinterpret_cast<const char*>(A + (AK ? (size_t)m0 * p.lda + kbeg : (size_t)kbeg * p.lda + m0));
+        const char* ob = reinterpret_cast<const char*>(B + (BKM ? (size_t)n0 * p.ldb + kbeg : (size_t)kbeg * p.ldb + n0));
+        const size_t sta = (size_t)(AK ? DKT : DKT * p.lda) * sizeof(T);
+        const size_t stb = (size_t)(BKM ? DKT : DKT * p.ldb) * sizeof(T);
+        const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem_raw;
+        int issued = 0;  // k tiles issued so far
+        auto issue_next = [&]() {
+            const uint32_t st = lds0 + (uint32_t)((issued % DNS) * STAGE * (int)sizeof(T));
+            pa.issue(oa, st, wave_s);
+            pb.issue(ob, st + AEL * (uint32_t)sizeof(T), wave_s);
+            oa += sta;
+            ob += stb;
+            ++issued;
+        };
+        // fragments of one 16-wide k-step of a stage
+        auto read_ks = [&](int kt, int ks, v8 (&fa)[MI], v8 (&fb)[NI]) {
+            const T* sa = smem + (kt % DNS) * STAGE;
+            const T* sb = sa + AEL;
 #pragma unroll
-    for (int s0 = 0; s0 < DNS - 1; ++s0)
-        if (s0 < nk) issue(s0);
-    if (nk > 2) wait_vmcnt<2 * LPW>();
-    else if (nk > 1) wait_vmcnt<LPW>();
-    else wait_vmcnt<0>();
-    __syncthreads();
-    // Per k-tile kt (fragments of its first k-step already in f0):
-    //   read its second k-step -> f1; MFMAs on f0;
-    //   make tile kt+1 visible (its loads landed on every wave; every wave is
-    //   past tile kt-1, whose stage the loads of tile kt+3 now overwrite);
-    //   read tile kt+1's first k-step -> f0; MFMAs on f1.
-    v8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
-    read_ks(0, 0, fa0, fb0);
-    for (int kt = 0; kt < nk; ++kt) {
-        read_ks(kt, 1, fa1, fb1);
-        rowsums(kt);
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kt + 1 < nk) {
-            if (kt + 2 < nk) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
-            __syncthreads();
-            if (kt + DNS - 1 < nk) issue(kt + DNS - 1);
-            read_ks(kt + 1, 0, fa0, fb0);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        mfmas(fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
-    }
-    __syncthreads();
-
-    if constexpr (!AK) {
-        if (do_rsum) {
-            // threads tid, tid + CPR, ... hold the same 8 rows: add in that order
-            constexpr int CPR = BM / 8;
-            float* red = reinterpret_cast<float*>(smem_raw);
+            for (int i = 0; i < MI; ++i) fa[i] = dl_frag<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) red[tid * 8 + e] = rs[e];
-            __syncthreads();
-            if (tid < CPR) {
-                float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                for (int q = tid; q < NT; q += CPR)
+            for (int j = 0; j < NI; ++j) fb[j] = dl_frag<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
+        };
+        auto rowsums = [&](int kt) {
+            if constexpr (!AK) {
+                if (do_rsum) {
+                    const T* sa = smem + (kt % DNS) * STAGE;
+                    constexpr int CPR = BM / 8;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] += red[q * 8 + e];
-                const int mrow = m0 + tid * 8;
-                if (gridDim.z > 1) {
-                    float* out = reinterpret_cast<float*>(p.rsum) + (size_t)blockIdx.z * p.M + mrow;
+                    for (int c = tid; c < DKT * CPR; c += NT) {
+                        const int k = c / CPR;
+                        typedef T t8 __attribute__((ext_vector_type(8)));
+                        const t8 x = *reinterpret_cast<const t8*>(sa + mn32_off<BM>(k, (c % CPR) * 8));
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) out[e] = t[e];
-                } else {
-                    T* out = reinterpret_cast<T*>(p.rsum) + mrow;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) out[e] = from_f<T>(t[e]);
+                        for (int e = 0; e < 8; ++e) rs[e] += to_f(x[e]);
+                    }
                 }
             }
+        };
+        auto mfmas = [&](const v8 (&fa)[MI], const v8 (&fb)[NI]) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+#pragma unroll
+                for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
+        };
+
+#pragma unroll
+        for (int s0 = 0; s0 < DNS - 1; ++s0)
+            if (s0 < nk) issue_next();
+        if (nk > 2) wait_vmcnt<2 * LPW>();
+        else if (nk > 1) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        // Per k-tile kt (fragments of its first k-step already in f0):
+        //   read its second k-step -> f1; MFMAs on f0;
+        //   make tile kt+1 visible (its loads landed on every wave; every wave is
+        //   past tile kt-1, whose stage the loads of tile kt+3 now overwrite);
+        //   read tile kt+1's first k-step -> f0; MFMAs on f1.
+        // The steady state (a tile still to issue) is one branch-free block, so
+        // the scheduling fences hold; the last DNS-1 tiles run in a peeled loop.
+        v8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+        read_ks(0, 0, fa0, fb0);
+        int kt = 0;
+        for (; kt < nk - (DNS - 1); ++kt) {
+            read_ks(kt, 1, fa1, fb1);
+            rowsums(kt);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            wait_vmcnt<(DNS - 3) * LPW>();
             __syncthreads();
+            issue_next();
+            read_ks(kt + 1, 0, fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        for (; kt < nk; ++kt) {
+            read_ks(kt, 1, fa1, fb1);
+            rowsums(kt);
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(fa0, fb0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (kt + 1 < nk) {
+                if (kt + 2 < nk) wait_vmcnt<LPW>();
+                else wait_vmcnt<0>();
+                __syncthreads();
+                read_ks(kt + 1, 0, fa0, fb0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            mfmas(fa1, fb1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+
+        if constexpr (!AK) {
+            if (do_rsum) {
+                // threads tid, tid + CPR, ... hold the same 8 rows: add in that order
+                constexpr int CPR = BM / 8;
+                float* red = reinterpret_cast<float*>(smem_raw);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) red[tid * 8 + e] = rs[e];
+                __syncthreads();
+                if (tid < CPR) {
+                    float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+                    for (int q = tid; q < NT; q += CPR)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) t[e] += red[q * 8 + e];
+                    const int mrow = m0 + tid * 8;
+                    if (gridDim.z > 1) {
+                        float* out = reinterpret_cast<float*>(p.rsum) + (size_t)blockIdx.z * p.M + mrow;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) out[e] = t[e];
+                    } else {
+                        T* out = reinterpret_cast<T*>(p.rsum) + mrow;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) out[e] = from_f<T>(t[e]);
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
     }
-    gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
 }
 
 // Deterministic split-K reduction: out[m][n] = sum_z ws[z][m][n] in z order.
@@ -801,13 +848,24 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     size_t lds = (size_t)DNS * (BM + BN) * DKT * sizeof(T);
     lds = std::max(lds, epilogue_lds_bytes<BM, BN, WGM, WGN>());
     lds = std::max(lds, (size_t)WGM * WGN * 64 * 8 * 4);
-    static bool attr_done = false;
-    if (!attr_done) {
+    static int slots = 0;  // workgroups of this kernel resident on the whole device
+    if (!slots) {
         hipError_t e = set_lds(kern, lds);
         if (e != hipSuccess) return e;
-        attr_done = true;
+        int per_cu = 0, dev = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, WGM * WGN * 64, lds);
+        if (e != hipSuccess) return e;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        slots = std::max(1, per_cu) * std::max(1, cus);
     }
-    dim3 grid((g.M / BM) * (g.N / BN), 1, splits);
+    const int tiles = (g.M / BM) * (g.N / BN);
+    // persistent grid: at most one resident wave of workgroups, a multiple of
+    // the 8 XCDs so each workgroup's tiles stay on its XCD's range
+    int gx = std::min(tiles, std::max(8, slots / splits / 8 * 8));
+    dim3 grid(gx, 1, splits);
     hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
@@ -827,11 +885,10 @@ constexpr int W256N = 4;
 constexpr int W128M = 4;
 template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
 static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
-    if constexpr (!BGELU && AK) {
-        // projections and input gradients stream their operands straight into
-        // LDS; weight gradients (both operands m/n-major) and the GELU-on-load
-        // variant use the register-staged kernel, which measured faster there
-        // and can transform B on its way to LDS
+    if constexpr (!BGELU) {
+        // operands stream straight into LDS; only the GELU-on-load variant
+        // (weight gradient under GELU checkpointing) uses the register-staged
+        // kernel, which can transform B on its way to LDS
         if (c.BM == 256 && c.BN == 256) return launch_dl<T, 256, 256, 2, W256N, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
         if (c.BM == 256 && c.BN == 128) return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
         return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
