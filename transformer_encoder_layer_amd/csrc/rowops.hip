@@ -14,17 +14,6 @@
 namespace tel {
 
 
-template <typename T>
-__device__ __forceinline__ void load4(const void* p, int is_f32, size_t off, float v[4]) {
-    if (is_f32) Vec4<float>::load((const float*)p + off, v);
-    else Vec4<T>::load((const T*)p + off, v);
-}
-template <typename T>
-__device__ __forceinline__ void store4(void* p, int is_f32, size_t off, const float v[4]) {
-    if (is_f32) Vec4<float>::store((float*)p + off, v);
-    else Vec4<T>::store((T*)p + off, v);
-}
-
 // Lane layout shared by the LayerNorm kernels: one 64-lane wave per row;
 // lane l holds the NC groups of 4 consecutive columns c*256 + 4l .. +3
 // (c < NC, NC = ceil(H / 256)), so each load or store of a group is one
@@ -32,24 +21,45 @@ __device__ __forceinline__ void store4(void* p, int is_f32, size_t off, const fl
 template <int NC>
 __device__ __forceinline__ bool col_ok(int c, int lane, int H) { return c * 256 + lane * 4 < H; }
 
-template <typename T, int NC>
+// Every load of a row is issued unconditionally so that they are all in
+// flight together: a lane whose column group lies beyond H (H need not be a
+// multiple of 256) reads the row's last group instead and its values are
+// masked to zero; rows past T read row T-1 and store nothing.  (Loads under
+// per-lane or per-flag branches would each be followed by a full memory
+// wait at the branch join.)
+__device__ __forceinline__ int col_clamped(int c, int lane, int H) { return min(c * 256 + lane * 4, H - 4); }
+
+template <typename T, bool F32>
+__device__ __forceinline__ void load4k(const void* p, size_t off, float v[4]) {
+    if constexpr (F32) Vec4<float>::load((const float*)p + off, v);
+    else Vec4<T>::load((const T*)p + off, v);
+}
+template <typename T, bool F32>
+__device__ __forceinline__ void store4k(void* p, size_t off, const float v[4]) {
+    if constexpr (F32) Vec4<float>::store((float*)p + off, v);
+    else Vec4<T>::store((T*)p + off, v);
+}
+
+template <typename T, int NC, bool XF32>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= a.T) return;
     const int H = a.H;
-    const size_t base = (size_t)row * H;
-    float v[NC][4];
+    const int rowc = min(row, a.T - 1);
+    const size_t base = (size_t)rowc * H;
+    float v[NC][4], g[NC][4], bt[NC][4];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+        const int idx = col_clamped(c, lane, H);
+        load4k<T, XF32>(a.x, base + idx, v[c]);
+        Vec4<T>::load((const T*)a.gamma + idx, g[c]);
+        Vec4<T>::load((const T*)a.beta + idx, bt[c]);
+    }
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int idx = c * 256 + lane * 4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[c][i] = 0.0f;
-        if (col_ok<NC>(c, lane, H)) {
-            load4<T>(a.x, a.x_f32, base + idx, v[c]);
-            s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
-        }
+        if (!col_ok<NC>(c, lane, H)) v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.0f;
+        s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
     }
     const float mean = wave_sum(s) / (float)H;
     float s2 = 0.0f;
@@ -65,15 +75,14 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     }
     const float var = wave_sum(s2) / (float)H;
     const float rs = 1.0f / sqrtf(var + a.eps);
+    if (row >= a.T) return;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int idx = c * 256 + lane * 4;
         if (col_ok<NC>(c, lane, H)) {
-            float g[4], b[4], y[4];
-            Vec4<T>::load((const T*)a.gamma + idx, g);
-            Vec4<T>::load((const T*)a.beta + idx, b);
+            float y[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) y[i] = (v[c][i] - mean) * rs * g[i] + b[i];
+            for (int i = 0; i < 4; ++i) y[i] = (v[c][i] - mean) * rs * g[c][i] + bt[c][i];
             Vec4<T>::store((T*)a.out + base + idx, y);
             if (a.out_f32) Vec4<float>::store(a.out_f32 + base + idx, y);
             if (a.out_copy) Vec4<T>::store((T*)a.out_copy + base + idx, y);
@@ -90,70 +99,84 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
 // dx = rstd * (gh - mean(gh) - xhat * mean(gh * xhat)) with the two means
 // reduced by wave shuffles; dgamma/dbeta partials stay in the lanes' own
 // columns and are added over the 4 waves in fixed order at the end, giving
-// one partial row per workgroup.
+// one partial row per workgroup.  The tensor layout is a compile-time mode:
+//   bit 0 LN source fp32, bit 1 source is the LN output (invertible),
+//   bits 2-3 residual term added to dx (0 none, 1 dtype, 2 fp32),
+//   bit 4 fp32 term added to dy, bit 5 dx stored fp32, bit 6 drop(dx) stored.
 constexpr int LN_RPW = 4;
+enum : int {
+    LNB_SRC_F32 = 1, LNB_FROM_OUT = 2, LNB_RES_LOWP = 4, LNB_RES_F32 = 8, LNB_ADD = 16, LNB_OUT_F32 = 32,
+    LNB_DROP = 64
+};
 
-template <typename T, int NC>
+template <typename T, int NC, int MODE>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
+    constexpr bool SRC_F32 = MODE & LNB_SRC_F32, FROM_OUT = MODE & LNB_FROM_OUT, ADD = MODE & LNB_ADD;
+    constexpr bool OUT_F32 = MODE & LNB_OUT_F32, DROP = MODE & LNB_DROP;
+    constexpr int RES = (MODE & LNB_RES_F32) ? 2 : (MODE & LNB_RES_LOWP) ? 1 : 0;
     __shared__ float red[4][NC * 256];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int H = a.H;
     float gam[NC][4], bet[NC][4], pg[NC][4], pb[NC][4];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+        const int idx = col_clamped(c, lane, H);
+        Vec4<T>::load((const T*)a.gamma + idx, gam[c]);
+        if constexpr (FROM_OUT) Vec4<T>::load((const T*)a.beta + idx, bet[c]);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { gam[c][i] = 1.0f; bet[c][i] = 0.0f; pg[c][i] = 0.0f; pb[c][i] = 0.0f; }
-        if (col_ok<NC>(c, lane, H)) {
-            Vec4<T>::load((const T*)a.gamma + c * 256 + lane * 4, gam[c]);
-            if (a.from_output) Vec4<T>::load((const T*)a.beta + c * 256 + lane * 4, bet[c]);
-        }
+        for (int i = 0; i < 4; ++i) { pg[c][i] = 0.0f; pb[c][i] = 0.0f; }
     }
     const int row0 = (blockIdx.x * 4 + wave) * LN_RPW;
     for (int rr = 0; rr < LN_RPW; rr += 2) {
-        float dy[2][NC][4], xh[2][NC][4], r[2][NC][4];
-        float s1[2] = {0, 0}, s2[2] = {0, 0}, rsv[2] = {0, 0};
+        float dy[2][NC][4], sv[2][NC][4], r[2][NC][4], xh[2][NC][4];
+        float rsv[2], muv[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int row = row0 + rr + u;
-            const bool rok = row < a.T;
-            const size_t base = (size_t)(rok ? row : 0) * H;
-            const float rs = rok ? a.rstd[row] : 0.0f;
-            const float mu = (rok && !a.from_output) ? a.mu[row] : 0.0f;
-            rsv[u] = rs;
+            const int rowc = min(row0 + rr + u, a.T - 1);
+            const size_t base = (size_t)rowc * H;
+            rsv[u] = a.rstd[rowc];
+            muv[u] = FROM_OUT ? 0.0f : a.mu[rowc];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const int idx = c * 256 + lane * 4;
+                const int idx = col_clamped(c, lane, H);
+                Vec4<T>::load((const T*)a.dout + base + idx, dy[u][c]);
+                if constexpr (ADD) {
+                    float t[4];
+                    Vec4<float>::load(a.dout_add + base + idx, t);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) { dy[u][c][i] = 0.0f; xh[u][c][i] = 0.0f; r[u][c][i] = 0.0f; }
-                if (rok && col_ok<NC>(c, lane, H)) {
-                    float sv[4];
-                    Vec4<T>::load((const T*)a.dout + base + idx, dy[u][c]);
-                    if (a.dout_add) {
-                        float t[4];
-                        Vec4<float>::load(a.dout_add + base + idx, t);
+                    for (int i = 0; i < 4; ++i) dy[u][c][i] += t[i];
+                }
+                load4k<T, SRC_F32>(a.src, base + idx, sv[u][c]);
+                if constexpr (RES != 0) load4k<T, RES == 2>(a.res, base + idx, r[u][c]);
+            }
+        }
+        float s1[2] = {0, 0}, s2[2] = {0, 0};
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) dy[u][c][i] += t[i];
-                    }
-                    load4<T>(a.src, a.src_f32, base + idx, sv);
-                    if (a.res) load4<T>(a.res, a.res_f32, base + idx, r[u][c]);
+        for (int u = 0; u < 2; ++u) {
+            const bool rok = row0 + rr + u < a.T;
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        xh[u][c][i] = a.from_output ? (sv[i] - bet[c][i]) / gam[c][i] : (sv[i] - mu) * rs;
-                        const float gh = dy[u][c][i] * gam[c][i];
-                        s1[u] += gh;
-                        s2[u] += gh * xh[u][c][i];
-                        pg[c][i] += dy[u][c][i] * xh[u][c][i];
-                        pb[c][i] += dy[u][c][i];
-                    }
+            for (int c = 0; c < NC; ++c) {
+                const bool ok = rok && col_ok<NC>(c, lane, H);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float d = ok ? dy[u][c][i] : 0.0f;
+                    const float x = FROM_OUT ? (sv[u][c][i] - bet[c][i]) / gam[c][i] : (sv[u][c][i] - muv[u]) * rsv[u];
+                    dy[u][c][i] = d;
+                    xh[u][c][i] = ok ? x : 0.0f;
+                    const float gh = d * gam[c][i];
+                    s1[u] += gh;
+                    s2[u] += gh * xh[u][c][i];
+                    pg[c][i] += d * xh[u][c][i];
+                    pb[c][i] += d;
                 }
             }
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int row = row0 + rr + u;
-            if (row >= a.T) continue;
             const float mg = wave_sum(s1[u]) / (float)H;
             const float mgx = wave_sum(s2[u]) / (float)H;
+            if (row >= a.T) continue;
             const size_t base = (size_t)row * H;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
@@ -161,10 +184,12 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
                 if (!col_ok<NC>(c, lane, H)) continue;
                 float dx[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    dx[i] = rsv[u] * (dy[u][c][i] * gam[c][i] - mg - xh[u][c][i] * mgx) + r[u][c][i];
-                store4<T>(a.out, a.out_f32, base + idx, dx);
-                if (a.drop_out) {
+                for (int i = 0; i < 4; ++i) {
+                    dx[i] = rsv[u] * (dy[u][c][i] * gam[c][i] - mg - xh[u][c][i] * mgx);
+                    if constexpr (RES != 0) dx[i] += r[u][c][i];
+                }
+                store4k<T, OUT_F32>(a.out, base + idx, dx);
+                if constexpr (DROP) {
                     if (a.drop.thr) {
                         const uint32_t k = keep4(a.drop.rng, (base + idx) >> 2, a.drop.thr);
 #pragma unroll
@@ -258,19 +283,23 @@ __global__ __launch_bounds__(256) void mask_dump_kernel(Drop d, uint8_t* out, si
 }
 
 // ------------------------------------------------------------------ launchers
-template <typename T>
-static hipError_t ln_forward_t(const LnFwdArgs& a, hipStream_t st) {
+template <typename T, bool XF32>
+static hipError_t ln_forward_x(const LnFwdArgs& a, hipStream_t st) {
     dim3 grid((a.T + 3) / 4), blk(256);
     switch ((a.H + 255) / 256) {
-        case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2>), grid, blk, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((ln_fwd_kernel<T, 3>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4>), grid, blk, 0, st, a); break;
-        case 5: case 6: hipLaunchKernelGGL((ln_fwd_kernel<T, 6>), grid, blk, 0, st, a); break;
-        case 7: case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8>), grid, blk, 0, st, a); break;
-        default: hipLaunchKernelGGL((ln_fwd_kernel<T, 16>), grid, blk, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1, XF32>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2, XF32>), grid, blk, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((ln_fwd_kernel<T, 3, XF32>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4, XF32>), grid, blk, 0, st, a); break;
+        case 5: case 6: hipLaunchKernelGGL((ln_fwd_kernel<T, 6, XF32>), grid, blk, 0, st, a); break;
+        case 7: case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8, XF32>), grid, blk, 0, st, a); break;
+        default: return hipErrorInvalidValue;  // H <= 2048
     }
     return hipGetLastError();
+}
+template <typename T>
+static hipError_t ln_forward_t(const LnFwdArgs& a, hipStream_t st) {
+    return a.x_f32 ? ln_forward_x<T, true>(a, st) : ln_forward_x<T, false>(a, st);
 }
 
 hipError_t ln_forward(const LnFwdArgs& a, hipStream_t st) {
@@ -284,19 +313,45 @@ hipError_t ln_forward(const LnFwdArgs& a, hipStream_t st) {
 
 int ln_backward_parts(int T) { return (T + 4 * LN_RPW - 1) / (4 * LN_RPW); }
 
-template <typename T>
-static hipError_t ln_backward_t(const LnBwdArgs& a, hipStream_t st) {
+template <typename T, int MODE>
+static hipError_t ln_backward_m(const LnBwdArgs& a, hipStream_t st) {
     dim3 grid(ln_backward_parts(a.T)), blk(256);
     switch ((a.H + 255) / 256) {
-        case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2>), grid, blk, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((ln_bwd_kernel<T, 3>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4>), grid, blk, 0, st, a); break;
-        case 5: case 6: hipLaunchKernelGGL((ln_bwd_kernel<T, 6>), grid, blk, 0, st, a); break;
-        case 7: case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8>), grid, blk, 0, st, a); break;
+        case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1, MODE>), grid, blk, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2, MODE>), grid, blk, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((ln_bwd_kernel<T, 3, MODE>), grid, blk, 0, st, a); break;
+        case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4, MODE>), grid, blk, 0, st, a); break;
+        case 5: case 6: hipLaunchKernelGGL((ln_bwd_kernel<T, 6, MODE>), grid, blk, 0, st, a); break;
+        case 7: case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8, MODE>), grid, blk, 0, st, a); break;
         default: return hipErrorInvalidValue;  // H <= 2048 (LDS of the partial reduction)
     }
     return hipGetLastError();
+}
+
+// The tensor layouts the layer's four LayerNorm backward passes use, each
+// with and without the invertible (from-output) form.
+template <typename T>
+static hipError_t ln_backward_t(const LnBwdArgs& a, hipStream_t st) {
+    const int mode = (a.src_f32 ? LNB_SRC_F32 : 0) | (a.from_output ? LNB_FROM_OUT : 0) |
+                     (a.res ? (a.res_f32 ? LNB_RES_F32 : LNB_RES_LOWP) : 0) | (a.dout_add ? LNB_ADD : 0) |
+                     (a.out_f32 ? LNB_OUT_F32 : 0) | (a.drop_out ? LNB_DROP : 0);
+    switch (mode) {
+#define TEL_LNB(M) case (M): return ln_backward_m<T, (M)>(a, st);
+        // Pre-LN, LN2: dx1 = dy + LN2'(da2) in fp32, drop(dx1) for the attention branch
+        TEL_LNB(LNB_SRC_F32 | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
+        // Pre-LN, LN1: dx = dx1 + LN1'(da1)
+        TEL_LNB(LNB_RES_F32)
+        TEL_LNB(LNB_FROM_OUT | LNB_RES_F32)
+        // Post-LN, LN2: dz2 = LN2'(dy) in fp32, drop(dz2) for the FFN branch
+        TEL_LNB(LNB_SRC_F32 | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_FROM_OUT | LNB_OUT_F32 | LNB_DROP)
+        // Post-LN, LN1: dz1 = LN1'(da1 + dz2) in fp32, drop(dz1) for the attention branch
+        TEL_LNB(LNB_SRC_F32 | LNB_ADD | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_SRC_F32 | LNB_FROM_OUT | LNB_ADD | LNB_OUT_F32 | LNB_DROP)
+#undef TEL_LNB
+    }
+    return hipErrorNotSupported;
 }
 
 hipError_t ln_backward(const LnBwdArgs& a, hipStream_t st) {
