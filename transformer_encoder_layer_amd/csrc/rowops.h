@@ -43,6 +43,9 @@ hipError_t ln_backward(const LnBwdArgs& a, hipStream_t st);
 
 // out[n] = sum_p part[p][n] (fixed order), stored as dtype.
 hipError_t colsum_finalize(int dtype, const float* part, int P, int N, void* out, hipStream_t st);
+// The same for two vectors in one launch: out0 from part0, out1 from part1.
+hipError_t colsum_finalize2(int dtype, const float* part0, const float* part1, int P, int N, void* out0, void* out1,
+                            hipStream_t st);
 // Column sums of a dtype matrix [rows][N] -> fp32 partials [P][N]; returns P.
 int colsum_parts(int rows);
 hipError_t colsum_partial(int dtype, const void* in, int rows, int N, float* part, hipStream_t st);

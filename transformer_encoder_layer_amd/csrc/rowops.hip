@@ -214,30 +214,34 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
     }
 }
 
-// out[n] = sum_p part[p][n]: 32 columns x 8 row phases per workgroup; phase
-// j sums rows j, j+8, j+16, ... in order, then the 8 phase sums are added in
-// order -- a fixed summation order, independent of scheduling.
+// out_v[n] = sum_p part_v[p][n] for up to two vectors v (blockIdx.y): 8
+// columns x 32 row phases per workgroup; phase j sums rows j, j+32, ... in
+// order, then the 32 phase sums are added in order -- a fixed summation
+// order, independent of scheduling, with only P/32 dependent load rounds.
 template <typename T>
-__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* part, int P, int N, T* out) {
-    __shared__ float red[8][33];
-    const int cl = threadIdx.x & 31, ph = threadIdx.x >> 5;
-    const int n = blockIdx.x * 32 + cl;
+__global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* part0, const float* part1, int P, int N,
+                                                              T* out0, T* out1) {
+    __shared__ float red[32][9];
+    const float* part = blockIdx.y ? part1 : part0;
+    T* out = blockIdx.y ? out1 : out0;
+    const int cl = threadIdx.x & 7, ph = threadIdx.x >> 3;
+    const int n = blockIdx.x * 8 + cl;
     float s = 0.0f;
     if (n < N) {
         int p = ph;
-        for (; p + 24 < P; p += 32) {
-            const float a0 = part[(size_t)p * N + n], a1 = part[(size_t)(p + 8) * N + n];
-            const float a2 = part[(size_t)(p + 16) * N + n], a3 = part[(size_t)(p + 24) * N + n];
+        for (; p + 96 < P; p += 128) {
+            const float a0 = part[(size_t)p * N + n], a1 = part[(size_t)(p + 32) * N + n];
+            const float a2 = part[(size_t)(p + 64) * N + n], a3 = part[(size_t)(p + 96) * N + n];
             s += a0; s += a1; s += a2; s += a3;
         }
-        for (; p < P; p += 8) s += part[(size_t)p * N + n];
+        for (; p < P; p += 32) s += part[(size_t)p * N + n];
     }
     red[ph][cl] = s;
     __syncthreads();
     if (ph == 0 && n < N) {
         float t = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) t += red[j][cl];
+        for (int j = 0; j < 32; ++j) t += red[j][cl];
         out[n] = from_f<T>(t);
     }
 }
@@ -364,11 +368,16 @@ hipError_t ln_backward(const LnBwdArgs& a, hipStream_t st) {
 }
 
 hipError_t colsum_finalize(int dtype, const float* part, int P, int N, void* out, hipStream_t st) {
-    dim3 grid((N + 31) / 32);
+    return colsum_finalize2(dtype, part, nullptr, P, N, out, nullptr, st);
+}
+
+hipError_t colsum_finalize2(int dtype, const float* part0, const float* part1, int P, int N, void* out0, void* out1,
+                            hipStream_t st) {
+    dim3 grid((N + 7) / 8, part1 ? 2 : 1);
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(colsum_finalize_kernel<float>, grid, dim3(256), 0, st, part, P, N, (float*)out); break;
-        case 1: hipLaunchKernelGGL(colsum_finalize_kernel<f16>, grid, dim3(256), 0, st, part, P, N, (f16*)out); break;
-        case 2: hipLaunchKernelGGL(colsum_finalize_kernel<bf16>, grid, dim3(256), 0, st, part, P, N, (bf16*)out); break;
+        case 0: hipLaunchKernelGGL(colsum_finalize_kernel<float>, grid, dim3(256), 0, st, part0, part1, P, N, (float*)out0, (float*)out1); break;
+        case 1: hipLaunchKernelGGL(colsum_finalize_kernel<f16>, grid, dim3(256), 0, st, part0, part1, P, N, (f16*)out0, (f16*)out1); break;
+        case 2: hipLaunchKernelGGL(colsum_finalize_kernel<bf16>, grid, dim3(256), 0, st, part0, part1, P, N, (bf16*)out0, (bf16*)out1); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

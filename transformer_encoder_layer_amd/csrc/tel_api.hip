@@ -447,9 +447,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         return bias_grad(dY, out, db);
     };
     auto ln_grads = [&](void* gg, void* gb) -> hipError_t {
-        hipError_t e = colsum_finalize(dt, part_ln_g, lnP, H, gg, st);
-        if (e != hipSuccess) return e;
-        return colsum_finalize(dt, part_ln_b, lnP, H, gb, st);
+        return colsum_finalize2(dt, part_ln_g, part_ln_b, lnP, H, gg, gb, st);
     };
 
     AttnArgs aa{};
