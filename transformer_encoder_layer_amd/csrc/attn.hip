@@ -460,56 +460,95 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
     const int NW32 = S / 32;       // 32-key words per query row
     const int CMASK = S / 8 - 1;   // dS row chunks - 1
 
-    // ---- load
-    for (int cidx = tid; cidx < S * 8; cidx += 256) {
-        const int row = cidx >> 3, ch = cidx & 7;
-        const size_t g = (size_t)row * D + ch * 8;
-        *reinterpret_cast<uint4*>(Qs + kmaj_off(row, ch * 8)) = *reinterpret_cast<const uint4*>(Q + g);
-        *reinterpret_cast<uint4*>(dOs + kmaj_off(row, ch * 8)) = *reinterpret_cast<const uint4*>(dO + g);
-        *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = *reinterpret_cast<const uint4*>(K + g);
+    // ---- load: every global read of this phase is issued before the first
+    // use (fixed-count loops; slots past S read row 0 and are not stored)
+    constexpr int CPT = SMAX * 8 / 256;  // 16-byte chunks per thread and tensor
+    uint4 cq[CPT], cdo[CPT], ck[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+        const size_t g = (size_t)(row < S ? row : 0) * D + ch * 8;
+        cq[i] = *reinterpret_cast<const uint4*>(Q + g);
+        cdo[i] = *reinterpret_cast<const uint4*>(dO + g);
+        ck[i] = *reinterpret_cast<const uint4*>(K + g);
+    }
+    // D_q: two threads per query row, 32 columns each
+    const int dq_row = tid >> 1, dq_half = tid & 1;
+    const int dq_q = dq_row < S ? dq_row : 0;
+    v8 ov[4], dv8[4];
+    {
+        const T* orow = (const T*)a.ctx + (size_t)(b * S + dq_q) * H + h * D + dq_half * 32;
+        const T* drow = dO + (size_t)dq_q * D + dq_half * 32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ov[j] = *reinterpret_cast<const v8*>(orow + j * 8);
+            dv8[j] = *reinterpret_cast<const v8*>(drow + j * 8);
+        }
+    }
+    const float lse_v = a.lse[bh * S + dq_q];
+    // keep words: S * S/32 <= 512 per workgroup, two per thread
+    uint32_t kw[2] = {0u, 0u};
+    const bool stored_bits = a.drop.thr && a.bits;
+    if (stored_bits) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int cidx = tid + i * 256;
+            kw[i] = a.bits[bh * S * NW32 + (cidx < S * NW32 ? cidx : 0)];
+        }
+    }
+    // this wave's key and value rows as MFMA operands
+    const int kw0 = wave * 32;
+    const bool active = kw0 < S;
+    const int kl = kw0 + (lane & 31);
+    const int klc = kl < S ? kl : 0;
+    v8 kf[4], vf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int off = ks * 16 + (lane >> 5) * 8;
+        kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)klc * D + off);
+        vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)klc * D + off);
+    }
+    // (rows S .. SMAX-1 of the tiles are never read; storing them
+    // unconditionally keeps the loads above from being sunk into branches)
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+        *reinterpret_cast<uint4*>(Qs + kmaj_off(row, ch * 8)) = cq[i];
+        *reinterpret_cast<uint4*>(dOs + kmaj_off(row, ch * 8)) = cdo[i];
+        *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = ck[i];
     }
     {
-        // D_q: two threads per query row, 32 columns each
-        const int q = tid >> 1, half = tid & 1;
         float part = 0.0f;
-        if (q < S) {
-            const T* orow = (const T*)a.ctx + (size_t)(b * S + q) * H + h * D + half * 32;
-            const T* drow = dO + (size_t)q * D + half * 32;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v8 ov = *reinterpret_cast<const v8*>(orow + j * 8);
-                const v8 dv = *reinterpret_cast<const v8*>(drow + j * 8);
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
-                for (int i = 0; i < 8; ++i) part += to_f(dv[i]) * to_f(ov[i]);
-            }
-        }
+            for (int i = 0; i < 8; ++i) part += to_f(dv8[j][i]) * to_f(ov[j][i]);
         part += __shfl_xor(part, 1, 64);
-        if (q < S && half == 0) {
-            D_s[q] = part;
-            lse_s[q] = a.lse[bh * S + q];
+        if (dq_row < S && dq_half == 0) {
+            D_s[dq_row] = part;
+            lse_s[dq_row] = lse_v;
         }
     }
-    if (a.drop.thr) {
-        for (int cidx = tid; cidx < S * NW32; cidx += 256) {
-            const int q = cidx / NW32, w = cidx - q * NW32;
-            const uint64_t e0 = (bh * S + q) * (uint64_t)S + w * 32;  // element of key w*32
-            uint32_t word;
-            if (a.bits) {
-                word = a.bits[(bh * S + q) * NW32 + w];
-            } else {
-                word = 0;
+    {
 #pragma unroll
-                for (int g = 0; g < 8; ++g) word |= keep4(a.drop.rng, (e0 >> 2) + g, a.drop.thr) << (4 * g);
+        for (int i = 0; i < 2; ++i) {
+            const int cidx = tid + i * 256;
+            if (cidx < S * NW32) {
+                const int q = cidx / NW32, w = cidx - q * NW32;
+                uint32_t word = a.drop.thr ? kw[i] : 0xFFFFFFFFu;  // no dropout: keep all
+                if (a.drop.thr && !stored_bits) {
+                    const uint64_t e0 = (bh * S + q) * (uint64_t)S + w * 32;  // element of key w*32
+                    word = 0;
+#pragma unroll
+                    for (int g = 0; g < 8; ++g) word |= keep4(a.drop.rng, (e0 >> 2) + g, a.drop.thr) << (4 * g);
+                }
+                bits_s[q][w] = word;
             }
-            bits_s[q][w] = word;
         }
     }
     __syncthreads();
 
     // ---- phase 1: keys of this wave
-    const int kw0 = wave * 32;
-    const bool active = kw0 < S;
-    const int kl = kw0 + (lane & 31);
     f32x16 dk[2], dv[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
@@ -517,13 +556,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
         for (int r = 0; r < 16; ++r) { dk[ct][r] = 0.0f; dv[ct][r] = 0.0f; }
     v8 dsf[SMAX / 32][2];  // dS of each 32-query tile as MFMA operands, kept for phase 2
     if (active) {
-        v8 kf[4], vf[4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int off = ks * 16 + (lane >> 5) * 8;
-            kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)kl * D + off);
-            vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)kl * D + off);
-        }
 #pragma unroll
         for (int qt = 0; qt < SMAX / 32; ++qt) {
             if (qt * 32 < S) {
@@ -540,9 +572,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int qi = qt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const float p = kl < L ? exp2f(sc[r] * c - lse_s[qi]) : 0.0f;
-                    float f = 1.0f;
-                    if (a.drop.thr) f = ((bits_s[qi][wave] >> (kl & 31)) & 1u) ? a.drop.scale : 0.0f;
+                    const float p = exp2f(kl < L ? sc[r] * c - lse_s[qi] : -INFINITY);
+                    const float f = (bits_s[qi][wave] >> (kl & 31)) & 1u ? a.drop.scale : 0.0f;
                     ds[r] = p * (dp[r] * f - D_s[qi]);
                     sc[r] = p * f;
                 }
