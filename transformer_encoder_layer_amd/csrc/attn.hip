@@ -172,6 +172,144 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
     }
 }
 
+// ------------------------------------------------------------------ MFMA fwd, S <= 128
+// When all S <= 128 keys of a (batch, head) fit in LDS, one workgroup loads
+// K and V once (every load issued together) and each wave scores its 32
+// queries against all keys at once: the softmax is a plain two-pass one
+// (exact row maximum, then exp2 and sum), with no online rescaling.
+template <typename T>
+__global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
+    constexpr int D = 64, SMAX = 128, VLD = D + 32;
+    typedef typename MfmaOp<T>::v8 v8;
+    __shared__ __align__(16) T Ks[SMAX * D];
+    __shared__ __align__(16) T Vs[SMAX * VLD];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int b = blockIdx.z, h = blockIdx.y;
+    const int S = a.S, NH = a.NH, B = a.B;
+    const int L = a.len ? a.len[b] : S;
+    const size_t head = (size_t)S * D;
+    const T* Q = (const T*)a.qkvh + ((size_t)(0 * B + b) * NH + h) * head;
+    const T* K = (const T*)a.qkvh + ((size_t)(1 * B + b) * NH + h) * head;
+    const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
+    const float c = kLog2e * 0.125f;  // log2(e) / sqrt(64)
+
+    constexpr int CPT = SMAX * 8 / 256;
+    uint4 ck[CPT], cv[CPT];
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+        const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+        const size_t g = (size_t)(row < S ? row : 0) * D + ch * 8;
+        ck[i] = *reinterpret_cast<const uint4*>(K + g);
+        cv[i] = *reinterpret_cast<const uint4*>(V + g);
+    }
+    const int q0 = wave * 32;
+    const bool active = q0 < S;
+    const int ql = q0 + (lane & 31);
+    const int qlc = ql < S ? ql : 0;
+    v8 qf[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)qlc * D + ks * 16 + (lane >> 5) * 8);
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {  // rows S .. SMAX-1 are never read
+        const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
+        *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = ck[i];
+        *reinterpret_cast<uint4*>(Vs + row * VLD + ch * 8) = cv[i];
+    }
+    __syncthreads();
+    if (!active) return;
+
+    f32x16 s[SMAX / 32];
+    float m = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < SMAX / 32; ++kt) {
+        if (kt * 32 < S) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks, kt * 32, ks, lane), qf[ks], s[kt]);
+            // s[kt][r]: key kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key = kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const float v = key < L ? s[kt][r] * c : -INFINITY;
+                s[kt][r] = v;
+                m = fmaxf(m, v);
+            }
+        }
+    }
+    m = fmaxf(m, __shfl_xor(m, 32, 64));
+    float l = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < SMAX / 32; ++kt) {
+        if (kt * 32 < S) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const float p = exp2f(s[kt][r] - m);
+                s[kt][r] = p;
+                l += p;
+            }
+        }
+    }
+    l += __shfl_xor(l, 32, 64);
+    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + ql) * (uint64_t)S;
+    if (a.drop.thr) {
+#pragma unroll
+        for (int kt = 0; kt < SMAX / 32; ++kt) {
+            if (kt * 32 < S) {
+                uint32_t word = 0;  // keep bits of keys kt*32 + 0..31 held by this lane
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int key4 = kt * 32 + g * 8 + (lane >> 5) * 4;
+                    const uint32_t kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
+                    word |= kbits << (g * 8 + (lane >> 5) * 4);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
+                }
+                if (a.bits) {
+                    word |= __shfl_xor(word, 32, 64);
+                    if (lane < 32) a.bits[(rowbase >> 5) + kt] = word;
+                }
+            }
+        }
+    }
+    f32x16 o[2];
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[ct][r] = 0.0f;
+#pragma unroll
+    for (int kt = 0; kt < SMAX / 32; ++kt) {
+        if (kt * 32 < S) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                v8 pf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pf[i] = from_f<T>(s[kt][(2 * half) * 4 + i]);
+                    pf[4 + i] = from_f<T>(s[kt][(2 * half + 1) * 4 + i]);
+                }
+                const int kb0 = kt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+                    o[ct] = MfmaOp<T>::mma(frag_tr<T>(Vs, VLD, ct * 32, kb0, kb0 + 8, lane), pf, o[ct]);
+            }
+        }
+    }
+    const float inv = a.drop.scale / l;
+    T* out = (T*)a.ctx + (size_t)(b * S + ql) * (NH * D) + h * D;
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
+            Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+        }
+    if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = m + log2f(l);
+}
+
 // ------------------------------------------------------------------ MFMA bwd: D and dQ
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
@@ -823,6 +961,10 @@ static hipError_t simt_bwd(const AttnArgs& a0, hipStream_t st) {
 template <typename T>
 static hipError_t fwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
     if constexpr (!std::is_same<T, float>::value) {
+        if (!force_simt && mfma_attn_ok(a) && a.S <= 128) {
+            hipLaunchKernelGGL(attn_fwd_short_mfma<T>, dim3(1, a.NH, a.B), dim3(256), 0, st, a);
+            return hipGetLastError();
+        }
         if (!force_simt && mfma_attn_ok(a)) {
             dim3 grid((a.S + 127) / 128, a.NH, a.B);
             hipLaunchKernelGGL(attn_fwd_mfma<T>, grid, dim3(256), 0, st, a);

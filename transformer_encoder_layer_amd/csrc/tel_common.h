@@ -77,10 +77,12 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
     for (int round = 0; round < 10; ++round) {
-        const uint32_t a0 = 0xD2511F53u * c0;
-        const uint32_t b0 = __umulhi(0xD2511F53u, c0);
-        const uint32_t a2 = 0xCD9E8D57u * c2;
-        const uint32_t b2 = __umulhi(0xCD9E8D57u, c2);
+        // one 32 x 32 -> 64-bit product per multiplier (a single
+        // v_mad_u64_u32) instead of separate low and high multiplies
+        const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+        const uint64_t p2 = (uint64_t)0xCD9E8D57u * c2;
+        const uint32_t a0 = (uint32_t)p0, b0 = (uint32_t)(p0 >> 32);
+        const uint32_t a2 = (uint32_t)p2, b2 = (uint32_t)(p2 >> 32);
         const uint32_t n0 = b2 ^ c1 ^ k0;
         const uint32_t n2 = b0 ^ c3 ^ k1;
         c0 = n0; c1 = a2; c2 = n2; c3 = a0;
