@@ -609,8 +609,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
 #pragma unroll
         for (int s0 = 0; s0 < DNS - 1; ++s0)
             if (s0 < nk) issue_next();
-        if (nk > 2) wait_vmcnt<2 * LPW>();
-        else if (nk > 1) wait_vmcnt<LPW>();
+        // tile 0 landed: the tiles issued after it may still be in flight
+        if (nk >= DNS - 1) wait_vmcnt<(DNS - 2) * LPW>();
+        else if (nk == 2) wait_vmcnt<LPW>();
         else wait_vmcnt<0>();
         __syncthreads();
         // Per k-tile kt (fragments of its first k-step already in f0):
