@@ -429,14 +429,21 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ MFMA bwd: dK, dV
+// Key-parallel: wave w of workgroup x owns keys 128x + 32w .. +31 and walks
+// every 64-query block.  The blocks flow through two LDS buffers: the
+// global loads of block qb+1 (Q, dO, log-sum-exp, D and the keep words) are
+// issued into registers before the MFMAs of block qb, so one barrier per
+// block suffices and the load latency hides behind the compute.  Keep words
+// are always staged: the stored mask, or regenerated per 32 keys with one
+// Philox call per 4 keys, or all ones without dropout.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
     constexpr int D = 64, QB = 64;
     typedef typename MfmaOp<T>::v8 v8;
-    __shared__ __align__(16) T Qs[QB * D];
-    __shared__ __align__(16) T Os[QB * D];
-    __shared__ float lse_s[QB], D_s[QB];
-    __shared__ uint32_t bits_s[QB][4];  // keep-bit words of this block's 128 keys for 64 queries
+    __shared__ __align__(16) T Qs[2][QB * D];
+    __shared__ __align__(16) T Os[2][QB * D];
+    __shared__ float lse_s[2][QB], D_s[2][QB];
+    __shared__ uint32_t bits_s[2][QB][4];  // keep words of this block's 128 keys for 64 queries
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
@@ -453,16 +460,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
     const float* Dv = a.dvec + (size_t)(b * NH + h) * S;
     const float c = kLog2e * 0.125f;
     const int kl = key0 + (lane & 31);
+    const int klc = kl < S ? kl : 0;
     const uint64_t bhbase = (uint64_t)(b * NH + h) * S;
+    const int NW32 = S / 32;
 
     v8 kf[4], vf[4];
-    if (live) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int off = ks * 16 + (lane >> 5) * 8;
-            kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)kl * D + off);
-            vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)kl * D + off);
-        }
+    for (int ks = 0; ks < 4; ++ks) {
+        const int off = ks * 16 + (lane >> 5) * 8;
+        kf[ks] = *reinterpret_cast<const v8*>(K + (size_t)klc * D + off);
+        vf[ks] = *reinterpret_cast<const v8*>(V + (size_t)klc * D + off);
     }
     f32x16 dk[2], dv[2];
 #pragma unroll
@@ -470,74 +477,99 @@ __global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dk[ct][r] = 0.0f; dv[ct][r] = 0.0f; }
 
-    const int nqb = S / QB;
-    for (int qb = 0; qb < nqb; ++qb) {
+    // per-thread share of one block: 2 chunks of Q and of dO, one of the
+    // log-sum-exp / D values, one keep word (query tid/4, key word tid%4)
+    uint4 pq0, pq1, po0, po1;
+    float pld = 0.0f;
+    uint32_t pw = 0xFFFFFFFFu;
+    const int wq = tid >> 2, ww = tid & 3;
+    const int kwi = blockIdx.x * 4 + ww;  // 32-key word index of this thread's keep word
+    const int row0 = tid >> 3, row1 = (tid + 256) >> 3, ch = tid & 7;
+    auto fetch = [&](int qb) {
+        pq0 = *reinterpret_cast<const uint4*>(Q + (size_t)(qb * QB + row0) * D + ch * 8);
+        pq1 = *reinterpret_cast<const uint4*>(Q + (size_t)(qb * QB + row1) * D + ch * 8);
+        po0 = *reinterpret_cast<const uint4*>(dO + (size_t)(qb * QB + row0) * D + ch * 8);
+        po1 = *reinterpret_cast<const uint4*>(dO + (size_t)(qb * QB + row1) * D + ch * 8);
+        if (tid < QB) pld = lse[qb * QB + tid];
+        else if (tid < 2 * QB) pld = Dv[qb * QB + tid - QB];
+        if (a.drop.thr && a.bits && kwi < NW32) pw = a.bits[(bhbase + qb * QB + wq) * NW32 + kwi];
+    };
+    auto stage = [&](int qb, int buf) {
+        *reinterpret_cast<uint4*>(&Qs[buf][kmaj_off(row0, ch * 8)]) = pq0;
+        *reinterpret_cast<uint4*>(&Qs[buf][kmaj_off(row1, ch * 8)]) = pq1;
+        *reinterpret_cast<uint4*>(&Os[buf][kmaj_off(row0, ch * 8)]) = po0;
+        *reinterpret_cast<uint4*>(&Os[buf][kmaj_off(row1, ch * 8)]) = po1;
+        if (tid < QB) lse_s[buf][tid] = pld;
+        else if (tid < 2 * QB) D_s[buf][tid - QB] = pld;
+        uint32_t word = 0xFFFFFFFFu;
+        if (a.drop.thr) {
+            if (a.bits) {
+                word = pw;
+            } else if (kwi < NW32) {
+                const uint64_t e0 = (bhbase + qb * QB + wq) * (uint64_t)S + kwi * 32;
+                word = 0;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
-            const uint4 qv = *reinterpret_cast<const uint4*>(Q + (size_t)(qb * QB + row) * D + ch * 8);
-            const uint4 ov = *reinterpret_cast<const uint4*>(dO + (size_t)(qb * QB + row) * D + ch * 8);
-            *reinterpret_cast<uint4*>(Qs + kmaj_off(row, ch * 8)) = qv;
-            *reinterpret_cast<uint4*>(Os + kmaj_off(row, ch * 8)) = ov;
+                for (int g = 0; g < 8; ++g) word |= keep4(a.drop.rng, (e0 >> 2) + g, a.drop.thr) << (4 * g);
+            }
         }
-        if (tid < QB) lse_s[tid] = lse[qb * QB + tid];
-        else if (tid < 2 * QB) D_s[tid - QB] = Dv[qb * QB + tid - QB];
-        if (a.bits && a.drop.thr) {
-            const int q = tid >> 2, w = tid & 3;  // 256 threads: 64 queries x 4 words
-            const int kw = blockIdx.x * 4 + w;
-            bits_s[q][w] = kw < S / 32 ? a.bits[(bhbase + qb * QB + q) * (S / 32) + kw] : 0u;
-        }
+        bits_s[buf][wq][ww] = word;
+    };
+
+    const int nqb = S / QB;
+    fetch(0);
+    for (int qb = 0; qb < nqb; ++qb) {
+        const int buf = qb & 1;
+        stage(qb, buf);
         __syncthreads();
+        if (qb + 1 < nqb) fetch(qb + 1);
         if (live) {
-            f32x16 s[2], dp[2];
+            // one 32-query tile at a time keeps only its scores and dP live
 #pragma unroll
             for (int qt = 0; qt < 2; ++qt) {
+                f32x16 sc, dp;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) { s[qt][r] = 0.0f; dp[qt][r] = 0.0f; }
+                for (int r = 0; r < 16; ++r) { sc[r] = 0.0f; dp[r] = 0.0f; }
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    s[qt] = MfmaOp<T>::mma(frag_kmaj<T>(Qs, qt * 32, ks, lane), kf[ks], s[qt]);
-                    dp[qt] = MfmaOp<T>::mma(frag_kmaj<T>(Os, qt * 32, ks, lane), vf[ks], dp[qt]);
+                    sc = MfmaOp<T>::mma(frag_kmaj<T>(Qs[buf], qt * 32, ks, lane), kf[ks], sc);
+                    dp = MfmaOp<T>::mma(frag_kmaj<T>(Os[buf], qt * 32, ks, lane), vf[ks], dp);
                 }
-            }
-            // s[qt][r]: query qb*64 + qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl
-            f32x16 ds[2];
+                // sc[r]: query qb*64 + qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl
 #pragma unroll
-            for (int qt = 0; qt < 2; ++qt)
+                for (int g = 0; g < 4; ++g) {
+                    const int qi0 = qt * 32 + 8 * g + 4 * (lane >> 5);
+                    const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[buf][qi0]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&D_s[buf][qi0]);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = qt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const int q = qb * QB + qi;
-                    const float p = kl < L ? exp2f(s[qt][r] * c - lse_s[qi]) : 0.0f;
-                    float f = 1.0f;
-                    if (a.drop.thr) {
-                        const bool keep = a.bits ? ((bits_s[qi][wave] >> (kl & 31)) & 1u)
-                                                 : keep1(a.drop.rng, (bhbase + q) * S + kl, a.drop.thr);
-                        f = keep ? a.drop.scale : 0.0f;
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = g * 4 + i;
+                        const float p = exp2f(kl < L ? sc[r] * c - lv[i] : -INFINITY);
+                        const float f = (bits_s[buf][qi0 + i][wave] >> (kl & 31)) & 1u ? a.drop.scale : 0.0f;
+                        const float dsv = p * (dp[r] * f - dvv[i]);
+                        sc[r] = p * f;
+                        dp[r] = dsv;
                     }
-                    ds[qt][r] = p * (dp[qt][r] * f - D_s[qi]);
-                    s[qt][r] = p * f;
                 }
 #pragma unroll
-            for (int ks2 = 0; ks2 < 4; ++ks2) {
-                const int qt = ks2 >> 1, half = ks2 & 1;
-                v8 pf, sf;
+                for (int half = 0; half < 2; ++half) {
+                    v8 pf, sf;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pf[i] = from_f<T>(s[qt][(2 * half) * 4 + i]);
-                    pf[4 + i] = from_f<T>(s[qt][(2 * half + 1) * 4 + i]);
-                    sf[i] = from_f<T>(ds[qt][(2 * half) * 4 + i]);
-                    sf[4 + i] = from_f<T>(ds[qt][(2 * half + 1) * 4 + i]);
-                }
-                const int qb0 = qt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+                    for (int i = 0; i < 4; ++i) {
+                        pf[i] = from_f<T>(sc[(2 * half) * 4 + i]);
+                        pf[4 + i] = from_f<T>(sc[(2 * half + 1) * 4 + i]);
+                        sf[i] = from_f<T>(dp[(2 * half) * 4 + i]);
+                        sf[4 + i] = from_f<T>(dp[(2 * half + 1) * 4 + i]);
+                    }
+                    const int qb0 = qt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
 #pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    dv[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Os, ct * 32, qb0, qb0 + 8, lane), pf, dv[ct]);
-                    dk[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Qs, ct * 32, qb0, qb0 + 8, lane), sf, dk[ct]);
+                    for (int ct = 0; ct < 2; ++ct) {
+                        dv[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Os[buf], ct * 32, qb0, qb0 + 8, lane), pf, dv[ct]);
+                        dk[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Qs[buf], ct * 32, qb0, qb0 + 8, lane), sf, dk[ct]);
+                    }
                 }
             }
         }
-        __syncthreads();
     }
     if (active) {
         T* outk = (T*)a.dqkv + (size_t)(b * S + kl) * (3 * H) + H + h * D;
