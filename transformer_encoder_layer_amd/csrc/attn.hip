@@ -38,12 +38,15 @@ __device__ __forceinline__ bool keep1(const Rng& r, uint64_t e, uint32_t thr) {
 }
 
 // ------------------------------------------------------------------ MFMA fwd
+// One workgroup = 4 waves x 32 queries of one (batch, head); 64-key blocks
+// of K and V flow through two LDS buffers, the next block fetched into
+// registers before the MFMAs of the current one (one barrier per block).
 template <typename T>
 __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
     constexpr int D = 64, KB = 64, VLD = D + 32;  // V rows 192 B apart: conflict-free transposing reads
     typedef typename MfmaOp<T>::v8 v8;
-    __shared__ __align__(16) T Ks[KB * D];
-    __shared__ __align__(16) T Vs[KB * VLD];
+    __shared__ __align__(16) T Ks[2][KB * D];
+    __shared__ __align__(16) T Vs[2][KB * VLD];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = a.S, NH = a.NH, B = a.B;
@@ -57,30 +60,36 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
     const T* V = (const T*)a.qkvh + ((size_t)(2 * B + b) * NH + h) * head;
     const float c = kLog2e * 0.125f;  // log2(e) / sqrt(64)
     const int ql = q0 + (lane & 31);
+    const int qlc = ql < S ? ql : 0;
 
     v8 qf[4];
-    if (active) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)ql * D + ks * 16 + (lane >> 5) * 8);
-    }
+    for (int ks = 0; ks < 4; ++ks) qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)qlc * D + ks * 16 + (lane >> 5) * 8);
     float m_run = -INFINITY, l_run = 0.0f;
     f32x16 o[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[ct][r] = 0.0f;
-    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + ql) * (uint64_t)S;
+    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + qlc) * (uint64_t)S;
 
+    const int row0 = tid >> 3, row1 = row0 + 32, ch = tid & 7;
+    uint4 pk0, pk1, pv0, pv1;
+    auto fetch = [&](int kb) {
+        pk0 = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row0) * D + ch * 8);
+        pk1 = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row1) * D + ch * 8);
+        pv0 = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row0) * D + ch * 8);
+        pv1 = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row1) * D + ch * 8);
+    };
+    if (nkb > 0) fetch(0);
     for (int kb = 0; kb < nkb; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
-            const uint4 kv = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row) * D + ch * 8);
-            const uint4 vv = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row) * D + ch * 8);
-            *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = kv;
-            *reinterpret_cast<uint4*>(Vs + row * VLD + ch * 8) = vv;
-        }
+        const int buf = kb & 1;
+        *reinterpret_cast<uint4*>(&Ks[buf][kmaj_off(row0, ch * 8)]) = pk0;
+        *reinterpret_cast<uint4*>(&Ks[buf][kmaj_off(row1, ch * 8)]) = pk1;
+        *reinterpret_cast<uint4*>(&Vs[buf][row0 * VLD + ch * 8]) = pv0;
+        *reinterpret_cast<uint4*>(&Vs[buf][row1 * VLD + ch * 8]) = pv1;
         __syncthreads();
+        if (kb + 1 < nkb) fetch(kb + 1);
         if (active) {
             f32x16 s[2];
 #pragma unroll
@@ -88,7 +97,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks, kt * 32, ks, lane), qf[ks], s[kt]);
+                for (int ks = 0; ks < 4; ++ks) s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks[buf], kt * 32, ks, lane), qf[ks], s[kt]);
             }
             // s[kt][r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
             float mloc = -INFINITY;
@@ -150,10 +159,9 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
                 const int kb0 = kt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
 #pragma unroll
                 for (int ct = 0; ct < 2; ++ct)
-                    o[ct] = MfmaOp<T>::mma(frag_tr<T>(Vs, VLD, ct * 32, kb0, kb0 + 8, lane), pf, o[ct]);
+                    o[ct] = MfmaOp<T>::mma(frag_tr<T>(Vs[buf], VLD, ct * 32, kb0, kb0 + 8, lane), pf, o[ct]);
             }
         }
-        __syncthreads();
     }
     if (active) {
         const float l = l_run + __shfl_xor(l_run, 32, 64);
@@ -311,12 +319,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
 }
 
 // ------------------------------------------------------------------ MFMA bwd: D and dQ
+// Query-parallel: wave w of workgroup x owns queries 128x + 32w .. +31 and
+// walks the 64-key blocks below len[b].  K and V blocks flow through two LDS
+// buffers, the next block (and this lane's two keep words of it) fetched into
+// registers before the MFMAs of the current one, one barrier per block.
 template <typename T>
 __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
     constexpr int D = 64, KB = 64;
     typedef typename MfmaOp<T>::v8 v8;
-    __shared__ __align__(16) T Ks[KB * D];
-    __shared__ __align__(16) T Vs[KB * D];
+    __shared__ __align__(16) T Ks[2][KB * D];
+    __shared__ __align__(16) T Vs[2][KB * D];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
@@ -331,88 +343,101 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
     const T* dO = (const T*)a.dout + ((size_t)b * NH + h) * head;
     const float c = kLog2e * 0.125f;
     const int ql = q0 + (lane & 31);
+    const int qlc = ql < S ? ql : 0;
 
     v8 qf[4], df[4];
-    float Dq = 0.0f, lse2 = 0.0f;
-    if (active) {
-        const T* O = (const T*)a.ctx + (size_t)(b * S + ql) * H + h * D;
+    float Dq, lse2;
+    {
+        const T* O = (const T*)a.ctx + (size_t)(b * S + qlc) * H + h * D;
         float part = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const int off = ks * 16 + (lane >> 5) * 8;
-            qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)ql * D + off);
-            df[ks] = *reinterpret_cast<const v8*>(dO + (size_t)ql * D + off);
+            qf[ks] = *reinterpret_cast<const v8*>(Q + (size_t)qlc * D + off);
+            df[ks] = *reinterpret_cast<const v8*>(dO + (size_t)qlc * D + off);
             const v8 ov = *reinterpret_cast<const v8*>(O + off);
 #pragma unroll
             for (int i = 0; i < 8; ++i) part += to_f(df[ks][i]) * to_f(ov[i]);
         }
         Dq = part + __shfl_xor(part, 32, 64);
-        lse2 = a.lse[(size_t)(b * NH + h) * S + ql];
-        if (lane < 32) a.dvec[(size_t)(b * NH + h) * S + ql] = Dq;
+        lse2 = a.lse[(size_t)(b * NH + h) * S + qlc];
+        if (active && lane < 32) a.dvec[(size_t)(b * NH + h) * S + ql] = Dq;
     }
     f32x16 dq[2];
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int r = 0; r < 16; ++r) dq[ct][r] = 0.0f;
-    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + ql) * (uint64_t)S;
+    const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + qlc) * (uint64_t)S;
+    const bool stored_bits = a.drop.thr && a.bits;
 
-    for (int kb = 0; kb < nkb; ++kb) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int cidx = tid + i * 256, row = cidx >> 3, ch = cidx & 7;
-            const uint4 kv = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row) * D + ch * 8);
-            const uint4 vv = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row) * D + ch * 8);
-            *reinterpret_cast<uint4*>(Ks + kmaj_off(row, ch * 8)) = kv;
-            *reinterpret_cast<uint4*>(Vs + kmaj_off(row, ch * 8)) = vv;
+    const int row0 = tid >> 3, row1 = row0 + 32, ch = tid & 7;
+    uint4 pk0, pk1, pv0, pv1;
+    uint32_t pb0 = 0xFFFFFFFFu, pb1 = 0xFFFFFFFFu;
+    auto fetch = [&](int kb) {
+        pk0 = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row0) * D + ch * 8);
+        pk1 = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row1) * D + ch * 8);
+        pv0 = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row0) * D + ch * 8);
+        pv1 = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row1) * D + ch * 8);
+        if (stored_bits) {
+            pb0 = a.bits[(rowbase >> 5) + kb * 2];
+            pb1 = a.bits[(rowbase >> 5) + kb * 2 + 1];
         }
+    };
+    if (nkb > 0) fetch(0);
+    for (int kb = 0; kb < nkb; ++kb) {
+        const int buf = kb & 1;
+        *reinterpret_cast<uint4*>(&Ks[buf][kmaj_off(row0, ch * 8)]) = pk0;
+        *reinterpret_cast<uint4*>(&Ks[buf][kmaj_off(row1, ch * 8)]) = pk1;
+        *reinterpret_cast<uint4*>(&Vs[buf][kmaj_off(row0, ch * 8)]) = pv0;
+        *reinterpret_cast<uint4*>(&Vs[buf][kmaj_off(row1, ch * 8)]) = pv1;
+        const uint32_t w0 = pb0, w1 = pb1;
         __syncthreads();
+        if (kb + 1 < nkb) fetch(kb + 1);
         if (active) {
-            f32x16 s[2], dp[2];
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt) {
+                f32x16 sc, dp;
 #pragma unroll
-                for (int r = 0; r < 16; ++r) { s[kt][r] = 0.0f; dp[kt][r] = 0.0f; }
+                for (int r = 0; r < 16; ++r) { sc[r] = 0.0f; dp[r] = 0.0f; }
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) {
-                    s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks, kt * 32, ks, lane), qf[ks], s[kt]);
-                    dp[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Vs, kt * 32, ks, lane), df[ks], dp[kt]);
+                    sc = MfmaOp<T>::mma(frag_kmaj<T>(Ks[buf], kt * 32, ks, lane), qf[ks], sc);
+                    dp = MfmaOp<T>::mma(frag_kmaj<T>(Vs[buf], kt * 32, ks, lane), df[ks], dp);
                 }
-            }
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt)
+                // sc[r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
+                const uint32_t word = kt ? w1 : w0;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
                     uint32_t kbits = 0xFu;
                     if (a.drop.thr) {
-                        if (a.bits) kbits = (a.bits[(rowbase >> 5) + (key4 >> 5)] >> (key4 & 31)) & 0xFu;
+                        if (stored_bits) kbits = (word >> (key4 & 31)) & 0xFu;
                         else kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
                     }
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = g * 4 + i;
-                        const float p = (key4 + i < L) ? exp2f(s[kt][r] * c - lse2) : 0.0f;
+                        const float p = exp2f(key4 + i < L ? sc[r] * c - lse2 : -INFINITY);
                         const float f = ((kbits >> i) & 1u) ? a.drop.scale : 0.0f;
-                        s[kt][r] = p * (dp[kt][r] * f - Dq);
+                        sc[r] = p * (dp[r] * f - Dq);
                     }
                 }
 #pragma unroll
-            for (int ks2 = 0; ks2 < 4; ++ks2) {
-                const int kt = ks2 >> 1, half = ks2 & 1;
-                v8 pf;
+                for (int half = 0; half < 2; ++half) {
+                    v8 pf;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    pf[i] = from_f<T>(s[kt][(2 * half) * 4 + i]);
-                    pf[4 + i] = from_f<T>(s[kt][(2 * half + 1) * 4 + i]);
+                    for (int i = 0; i < 4; ++i) {
+                        pf[i] = from_f<T>(sc[(2 * half) * 4 + i]);
+                        pf[4 + i] = from_f<T>(sc[(2 * half + 1) * 4 + i]);
+                    }
+                    const int kb0 = kt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
+#pragma unroll
+                    for (int ct = 0; ct < 2; ++ct)
+                        dq[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Ks[buf], ct * 32, kb0, kb0 + 8, lane), pf, dq[ct]);
                 }
-                const int kb0 = kt * 32 + (2 * half) * 8 + (lane >> 5) * 4;
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct)
-                    dq[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Ks, ct * 32, kb0, kb0 + 8, lane), pf, dq[ct]);
             }
         }
-        __syncthreads();
     }
     if (active) {
         T* out = (T*)a.dqkv + (size_t)(b * S + ql) * (3 * H) + h * D;
