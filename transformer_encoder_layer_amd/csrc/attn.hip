@@ -462,7 +462,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
 // are always staged: the stored mask, or regenerated per 32 keys with one
 // Philox call per 4 keys, or all ones without dropout.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_dkdv_mfma(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
     constexpr int D = 64, QB = 64;
     typedef typename MfmaOp<T>::v8 v8;
     __shared__ __align__(16) T Qs[2][QB * D];
