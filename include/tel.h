@@ -25,12 +25,14 @@
  *
  * Dropout (inverted: kept value * 1/(1-p)) draws its bits from
  * Philox4x32-10 (Salmon et al., SC'11): key = (seed mod 2^32, layer_id),
- * counter = (floor(e/4) low, floor(e/4) high, site, step mod 2^32), word
- * e mod 4; an element is dropped iff its word < floor(p * 2^32) with p the
- * fp32 value in tel_config.  Sites: 0 attention probabilities, element
- * e = ((b*N + h)*S + i)*S + j; 1 attention-branch output, 2 FFN-branch
- * output, element e = t*H + c with token t = b*S + s; 3 the progressive
- * layer-drop gate (element 0).  Masks are a pure function of
+ * counter = (floor(e/8) low, floor(e/8) high, site, step mod 2^32); one
+ * call serves the 8 elements 8g .. 8g+7, element e taking the 16-bit half
+ * (e mod 2) of output word (e/2 mod 4), and it is dropped iff that value
+ * < floor(p * 2^16) with p the fp32 value in tel_config.  Sites: 0 attention
+ * probabilities, element e = ((b*N + h)*S + i)*S + j; 1 attention-branch
+ * output, 2 FFN-branch output, element e = t*H + c with token t = b*S + s;
+ * 3 the progressive layer-drop gate (output word 0 of block 0, compared as
+ * a 32-bit value with floor(theta * 2^32)).  Masks are a pure function of
  * (seed, layer_id, site, step, e).  The forward keeps the attention keep
  * bits (1 bit per score, in saved) unless attn_dropout_checkpoint is set, in
  * which case the backward regenerates them; hidden-dropout bits are always

@@ -117,24 +117,32 @@ void orc_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t ou
     out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
 }
 
-/* Random word for logical element e of a dropout site.
- * key = (seed mod 2^32, layer_id); counter = (floor(e/4) low, high, site,
- * step mod 2^32); the word is output e mod 4. */
-static uint32_t rng_word(uint64_t seed, int32_t layer, uint32_t site, uint64_t step, uint64_t e)
+/* Philox output word w of counter block g of one site:
+ * key = (seed mod 2^32, layer_id); counter = (g low, g high, site,
+ * step mod 2^32). */
+static uint32_t rng_block_word(uint64_t seed, int32_t layer, uint32_t site, uint64_t step, uint64_t g, int w)
 {
-    uint64_t g = e >> 2;
     uint32_t ctr[4] = { (uint32_t)g, (uint32_t)(g >> 32), site, (uint32_t)step };
     uint32_t key[2] = { (uint32_t)seed, (uint32_t)layer };
     uint32_t out[4];
     orc_philox4x32_10(ctr, key, out);
-    return out[e & 3];
+    return out[w];
 }
 
-/* An element is dropped iff its word < floor(p * 2^32). */
+/* 16-bit random value of logical element e of a dropout site: one Philox
+ * call (128 bits) serves 8 consecutive elements; element e takes word
+ * (e/2) mod 4 of block floor(e/8), low half for even e, high half for odd. */
+static uint32_t rng_half(uint64_t seed, int32_t layer, uint32_t site, uint64_t step, uint64_t e)
+{
+    const uint32_t w = rng_block_word(seed, layer, site, step, e >> 3, (int)((e >> 1) & 3));
+    return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
+}
+
+/* An element is dropped iff its 16-bit value < floor(p * 2^16). */
 static uint64_t drop_threshold(double p)
 {
     if (!(p > 0.0)) return 0;
-    return (uint64_t)floor(p * 4294967296.0);
+    return (uint64_t)floor(p * 65536.0);
 }
 
 uint64_t orc_drop_threshold(double p) { return drop_threshold(p); }
@@ -142,7 +150,7 @@ uint64_t orc_drop_threshold(double p) { return drop_threshold(p); }
 static int keep_elem(uint64_t seed, int32_t layer, uint32_t site, uint64_t step, uint64_t e, uint64_t thr)
 {
     if (thr == 0) return 1;
-    return (uint64_t)rng_word(seed, layer, site, step, e) >= thr;
+    return (uint64_t)rng_half(seed, layer, site, step, e) >= thr;
 }
 
 /* Dump keep bits (1 keep, 0 drop) for elements e0 .. e0+n-1 of one site. */
@@ -165,7 +173,7 @@ double orc_pld_theta(double t, double theta_bar, double gamma)
 int orc_pld_keep(uint64_t seed, int32_t layer, uint64_t step, double theta)
 {
     uint64_t thr = (uint64_t)floor(theta * 4294967296.0);
-    return (uint64_t)rng_word(seed, layer, 3u, step, 0) < thr;
+    return (uint64_t)rng_block_word(seed, layer, 3u, step, 0, 0) < thr;
 }
 
 /* ------------------------------------------------------------------ */

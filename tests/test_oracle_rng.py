@@ -32,12 +32,29 @@ def test_philox_known_answers():
 
 
 def test_drop_threshold_exact():
-    # floor(p * 2^32) in exact rational arithmetic, p as the fp32 value the library receives
+    # floor(p * 2^16) in exact rational arithmetic, p as the fp32 value the library receives
     for p in (0.0, 0.1, 0.25, 0.5, 0.9):
         pf = np.float32(p)
-        want = math.floor(Fraction(float(pf)) * 2 ** 32)
+        want = math.floor(Fraction(float(pf)) * 2 ** 16)
         assert oracle.drop_threshold(float(pf)) == want
-    assert oracle.drop_threshold(float(np.float32(0.1))) == 429496736
+    assert oracle.drop_threshold(float(np.float32(0.1))) == 6553
+
+
+def test_mask_uses_philox_halfwords():
+    # element e of a site: 16-bit half (e mod 2) of word (e/2 mod 4) of the
+    # Philox4x32-10 block floor(e/8) (counter = (block, 0, site, step),
+    # key = (seed, layer)); dropped iff that half < floor(p * 2^16).  The
+    # Philox function itself is pinned by the known-answer vectors above.
+    seed, layer, site, step = 1234, 5, 2, 77
+    p = float(np.float32(0.25))
+    thr = oracle.drop_threshold(p)
+    e0, n = 8 * 1000 + 3, 64
+    mask = oracle.dropout_mask(seed, layer, site, step, p, e0, n)
+    for i in range(n):
+        e = e0 + i
+        words = oracle.philox4x32_10([e >> 3, 0, site, step], [seed, layer])
+        half = (words[(e >> 1) & 3] >> (16 * (e & 1))) & 0xFFFF
+        assert mask[i] == (1 if half >= thr else 0), e
 
 
 def test_mask_p0_is_identity():

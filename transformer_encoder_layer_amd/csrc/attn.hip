@@ -12,8 +12,9 @@
 // online (running max / running sum) softmax, so only the per-row
 // log-sum-exp is written -- never the S x S matrix.  Scores are produced
 // transposed (keys x queries) so that each lane owns one query and four
-// consecutive keys: the row max/sum needs one cross-lane exchange, and one
-// Philox call yields the dropout bits of those four keys.  The probability
+// consecutive keys: the row max/sum needs one cross-lane exchange, and the
+// two lanes of a query split the Philox calls (8 keys each) of every 32-key
+// keep word and swap the results.  The probability
 // tile feeds the P.V product straight from registers; V is read with the
 // transposing LDS load using the same key permutation.
 //
@@ -35,6 +36,19 @@ static constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ bool keep1(const Rng& r, uint64_t e, uint32_t thr) {
     return (keep4(r, e >> 2, thr) >> (e & 3)) & 1u;
+}
+
+// Keep word of the 32 keys of one query row starting at element e0 (a
+// multiple of 32), computed by the two lanes l and l^32 that share the row:
+// each evaluates two of the four 8-key Philox blocks and they swap results.
+// Bit j of the word is key j.  Every lane of the wave must call it.
+__device__ __forceinline__ uint32_t keep_word32(const Rng& r, uint64_t e0, uint32_t thr, int lane) {
+    const int hh = lane >> 5;
+    const uint32_t m0 = keep8(r, (e0 >> 3) + hh, thr);      // block hh
+    const uint32_t m1 = keep8(r, (e0 >> 3) + 2 + hh, thr);  // block 2 + hh
+    const uint32_t o0 = __shfl_xor(m0, 32, 64), o1 = __shfl_xor(m1, 32, 64);
+    const uint32_t b0 = hh ? o0 : m0, b1 = hh ? m0 : o0, b2 = hh ? o1 : m1, b3 = hh ? m1 : o1;
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
 // ------------------------------------------------------------------ MFMA fwd
@@ -131,20 +145,16 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
             if (a.drop.thr) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    uint32_t word = 0;  // keep bits of keys kb*64 + kt*32 + 0..31 held by this lane
+                    // keep bits of keys kb*64 + kt*32 + 0..31
+                    const uint32_t word = keep_word32(a.drop.rng, rowbase + kb * KB + kt * 32, a.drop.thr, lane);
 #pragma unroll
                     for (int g = 0; g < 4; ++g) {
-                        const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
-                        const uint32_t kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
-                        word |= kbits << (g * 8 + (lane >> 5) * 4);
+                        const uint32_t kbits = word >> (g * 8 + (lane >> 5) * 4);
 #pragma unroll
                         for (int i = 0; i < 4; ++i)
                             if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
                     }
-                    if (a.bits) {
-                        word |= __shfl_xor(word, 32, 64);
-                        if (lane < 32) a.bits[(rowbase >> 5) + kb * 2 + kt] = word;
-                    }
+                    if (a.bits && lane < 32) a.bits[(rowbase >> 5) + kb * 2 + kt] = word;
                 }
             }
 #pragma unroll
@@ -264,20 +274,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
 #pragma unroll
         for (int kt = 0; kt < SMAX / 32; ++kt) {
             if (kt * 32 < S) {
-                uint32_t word = 0;  // keep bits of keys kt*32 + 0..31 held by this lane
+                // keep bits of keys kt*32 + 0..31
+                const uint32_t word = keep_word32(a.drop.rng, rowbase + kt * 32, a.drop.thr, lane);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
-                    const int key4 = kt * 32 + g * 8 + (lane >> 5) * 4;
-                    const uint32_t kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
-                    word |= kbits << (g * 8 + (lane >> 5) * 4);
+                    const uint32_t kbits = word >> (g * 8 + (lane >> 5) * 4);
 #pragma unroll
                     for (int i = 0; i < 4; ++i)
                         if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
                 }
-                if (a.bits) {
-                    word |= __shfl_xor(word, 32, 64);
-                    if (lane < 32) a.bits[(rowbase >> 5) + kt] = word;
-                }
+                if (a.bits && lane < 32) a.bits[(rowbase >> 5) + kt] = word;
             }
         }
     }
@@ -406,15 +412,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
                     dp = MfmaOp<T>::mma(frag_kmaj<T>(Vs[buf], kt * 32, ks, lane), df[ks], dp);
                 }
                 // sc[r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
-                const uint32_t word = kt ? w1 : w0;
+                uint32_t word = 0xFFFFFFFFu;
+                if (a.drop.thr)
+                    word = stored_bits ? (kt ? w1 : w0)
+                                       : keep_word32(a.drop.rng, rowbase + kb * KB + kt * 32, a.drop.thr, lane);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
-                    uint32_t kbits = 0xFu;
-                    if (a.drop.thr) {
-                        if (stored_bits) kbits = (word >> (key4 & 31)) & 0xFu;
-                        else kbits = keep4(a.drop.rng, (rowbase + key4) >> 2, a.drop.thr);
-                    }
+                    const uint32_t kbits = (word >> (key4 & 31)) & 0xFu;
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = g * 4 + i;
@@ -460,7 +465,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
 // issued into registers before the MFMAs of block qb, so one barrier per
 // block suffices and the load latency hides behind the compute.  Keep words
 // are always staged: the stored mask, or regenerated per 32 keys with one
-// Philox call per 4 keys, or all ones without dropout.
+// Philox call per 8 keys, or all ones without dropout.
 template <typename T>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
     constexpr int D = 64, QB = 64;
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
                 const uint64_t e0 = (bhbase + qb * QB + wq) * (uint64_t)S + kwi * 32;
                 word = 0;
 #pragma unroll
-                for (int g = 0; g < 8; ++g) word |= keep4(a.drop.rng, (e0 >> 2) + g, a.drop.thr) << (4 * g);
+                for (int g = 0; g < 4; ++g) word |= keep8(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
             }
         }
         bits_s[buf][wq][ww] = word;
@@ -735,7 +740,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
                     const uint64_t e0 = (bh * S + q) * (uint64_t)S + w * 32;  // element of key w*32
                     word = 0;
 #pragma unroll
-                    for (int g = 0; g < 8; ++g) word |= keep4(a.drop.rng, (e0 >> 2) + g, a.drop.thr) << (4 * g);
+                    for (int g = 0; g < 4; ++g) word |= keep8(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
                 }
                 bits_s[q][w] = word;
             }

@@ -264,26 +264,32 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* in, int ro
     Vec4<float>::store(part + (size_t)blockIdx.y * N + n4, s);
 }
 
+// Elementwise dropout, 8 elements (one Philox block) per thread; n % 4 == 0.
 template <typename T>
 __global__ __launch_bounds__(256) void dropout_apply_kernel(const T* in, T* out, size_t n, Drop d) {
-    const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (i4 >= n) return;
-    float v[4];
-    Vec4<T>::load(in + i4, v);
+    const size_t i8 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (i8 >= n) return;
+    const bool two = i8 + 4 < n;
+    float v[8];
+    Vec4<T>::load(in + i8, v);
+    if (two) Vec4<T>::load(in + i8 + 4, v + 4);
     if (d.thr) {
-        const uint32_t k = keep4(d.rng, i4 >> 2, d.thr);
+        const uint32_t k = keep8(d.rng, i8 >> 3, d.thr);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * d.scale : 0.0f;
+        for (int i = 0; i < 8; ++i) v[i] = ((k >> i) & 1u) ? v[i] * d.scale : 0.0f;
     }
-    Vec4<T>::store(out + i4, v);
+    Vec4<T>::store(out + i8, v);
+    if (two) Vec4<T>::store(out + i8 + 4, v + 4);
 }
 
 __global__ __launch_bounds__(256) void mask_dump_kernel(Drop d, uint8_t* out, size_t n) {
-    const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
-    if (i4 >= n) return;
-    const uint32_t k = d.thr ? keep4(d.rng, i4 >> 2, d.thr) : 0xFu;
-    uchar4 v = make_uchar4(k & 1u, (k >> 1) & 1u, (k >> 2) & 1u, (k >> 3) & 1u);
-    *reinterpret_cast<uchar4*>(out + i4) = v;
+    const size_t i8 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (i8 >= n) return;
+    const uint32_t k = d.thr ? keep8(d.rng, i8 >> 3, d.thr) : 0xFFu;
+    *reinterpret_cast<uchar4*>(out + i8) = make_uchar4(k & 1u, (k >> 1) & 1u, (k >> 2) & 1u, (k >> 3) & 1u);
+    if (i8 + 4 < n)
+        *reinterpret_cast<uchar4*>(out + i8 + 4) =
+            make_uchar4((k >> 4) & 1u, (k >> 5) & 1u, (k >> 6) & 1u, (k >> 7) & 1u);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -397,7 +403,7 @@ hipError_t colsum_partial(int dtype, const void* in, int rows, int N, float* par
 }
 
 hipError_t dropout_apply(int dtype, const void* in, void* out, size_t n, const Drop& d, hipStream_t st) {
-    dim3 grid((unsigned)((n / 4 + 255) / 256));
+    dim3 grid((unsigned)(((n + 7) / 8 + 255) / 256));
     switch (dtype) {
         case 0: hipLaunchKernelGGL(dropout_apply_kernel<float>, grid, dim3(256), 0, st, (const float*)in, (float*)out, n, d); break;
         case 1: hipLaunchKernelGGL(dropout_apply_kernel<f16>, grid, dim3(256), 0, st, (const f16*)in, (f16*)out, n, d); break;
@@ -408,7 +414,7 @@ hipError_t dropout_apply(int dtype, const void* in, void* out, size_t n, const D
 }
 
 hipError_t dropout_mask_dump(const Drop& d, uint8_t* out, size_t n, hipStream_t st) {
-    dim3 grid((unsigned)((n / 4 + 255) / 256));
+    dim3 grid((unsigned)(((n + 7) / 8 + 255) / 256));
     hipLaunchKernelGGL(mask_dump_kernel, grid, dim3(256), 0, st, d, out, n);
     return hipGetLastError();
 }

@@ -219,7 +219,7 @@ static Drop make_drop(const tel_layer* L, float p, uint32_t site, uint64_t step,
     d.thr = 0;
     d.scale = 1.0f;
     if (training && p > 0.0f) {
-        const double t = floor((double)p * 4294967296.0);
+        const double t = floor((double)p * 65536.0);
         d.thr = (uint32_t)t;
         d.scale = (float)(1.0 / (1.0 - (double)p));
     }

@@ -92,18 +92,34 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
     return make_uint4(c0, c1, c2, c3);
 }
 
-// Keep bits of the four elements 4g .. 4g+3 of one dropout site: bit i set
-// iff element 4g+i is kept, i.e. its 32-bit word >= thr.
-__device__ __forceinline__ uint32_t keep4(const Rng& r, uint64_t g, uint32_t thr) {
+// Dropout decisions: one Philox call (block g, counter (g low, g high,
+// site, step), key (seed, layer)) serves the 8 elements 8g .. 8g+7; element
+// e uses the 16-bit half (e mod 2) of word (e/2 mod 4) and is kept iff that
+// value >= thr = floor(p * 2^16).
+// Keep bits of the 8 elements of block g: bit j set iff element 8g+j is kept.
+__device__ __forceinline__ uint32_t keep8(const Rng& r, uint64_t g, uint32_t thr) {
     const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), r.site, r.step, r.key0, r.key1);
-    return (uint32_t)(w.x >= thr) | ((uint32_t)(w.y >= thr) << 1) | ((uint32_t)(w.z >= thr) << 2) |
-           ((uint32_t)(w.w >= thr) << 3);
+    const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+    uint32_t k = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) k |= (uint32_t)(((ws[j >> 1] >> (16 * (j & 1))) & 0xFFFFu) >= thr) << j;
+    return k;
+}
+// Keep bits of the four elements 4q .. 4q+3 (half of block q/2): bit i set
+// iff element 4q+i is kept.  Costs a whole Philox call; kernels that can
+// use all 8 decisions of a block call keep8 instead.
+__device__ __forceinline__ uint32_t keep4(const Rng& r, uint64_t q, uint32_t thr) {
+    const uint64_t g = q >> 1;
+    const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), r.site, r.step, r.key0, r.key1);
+    const uint32_t a = (q & 1) ? w.z : w.x, b = (q & 1) ? w.w : w.y;
+    return (uint32_t)((a & 0xFFFFu) >= thr) | ((uint32_t)((a >> 16) >= thr) << 1) |
+           ((uint32_t)((b & 0xFFFFu) >= thr) << 2) | ((uint32_t)((b >> 16) >= thr) << 3);
 }
 
 // Dropout description passed to kernels: thr == 0 means "no dropout".
 struct Drop {
     Rng rng;
-    uint32_t thr;
+    uint32_t thr;   // floor(p * 2^16)
     float scale;  // 1/(1-p) rounded to fp32
 };
 
