@@ -22,13 +22,20 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-fno-gpu-rdc",
          "-Wno-unused-result", "-I", os.path.join(ROOT, "include")]
 
 
+# Per-source extra flags.  gemm.hip: the epilogues fully unroll a loop over
+# the accumulator blocks around a large per-row body (dropout, GELU); below
+# this threshold the unroller gives up and the accumulators are indexed
+# dynamically, i.e. moved to scratch memory.
+EXTRA = {"gemm.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src)[:-4] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

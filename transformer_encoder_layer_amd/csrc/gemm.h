@@ -17,10 +17,11 @@ enum EpiKind {
     EPI_STORE = 0,         // out = v                               (T, or f32 if out_f32)
     EPI_QKV = 1,           // v + bias, scattered to [3][B][N][S][d]
     EPI_BIAS_DROP_RES = 2, // out = res + drop(v + bias)            (res T|f32, out T|f32)
-    EPI_BIAS_GELU = 3,     // u = v + bias -> out; GELU(u) -> out2 (if non-null)
-    EPI_GELU_BWD = 4,      // out = v * GELU'(aux)
+    EPI_BIAS_GELU = 3,     // u = v + bias -> out (or GELU'(u) if gelu_grad_out); GELU(u) -> out2 (if non-null)
+    EPI_GELU_BWD = 4,      // out = v * round_T(GELU'(aux))
     EPI_HEADSPLIT = 5,     // v scattered to [B][N][S][d]
     EPI_ADD_RES = 6,       // out = v + res(f32)
+    EPI_MUL_AUX = 7,       // out = v * aux                         (aux T)
 };
 
 struct EpiArgs {
@@ -31,6 +32,7 @@ struct EpiArgs {
     const void* res = nullptr;
     int res_f32 = 0;
     void* out2 = nullptr;
+    int gelu_grad_out = 0;  // EPI_BIAS_GELU: out receives GELU'(u) instead of u
     const void* aux = nullptr;
     int B = 0, S = 0, H = 0, NH = 0, d = 0;  // head-split geometry
     Drop drop{};                              // thr == 0: no dropout

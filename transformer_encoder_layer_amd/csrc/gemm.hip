@@ -30,7 +30,8 @@ namespace tel {
 template <typename T, int EPI>
 struct Epi {
     static constexpr bool kBias = EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES || EPI == EPI_BIAS_GELU;
-    static constexpr bool kElem = EPI == EPI_BIAS_DROP_RES || EPI == EPI_GELU_BWD || EPI == EPI_ADD_RES;
+    static constexpr bool kElem =
+        EPI == EPI_BIAS_DROP_RES || EPI == EPI_GELU_BWD || EPI == EPI_ADD_RES || EPI == EPI_MUL_AUX;
 
     static __device__ __forceinline__ void load_bias(const EpiArgs& e, int n, float b[4]) {
         if constexpr (kBias) Vec4<T>::load((const T*)e.bias + n, b);
@@ -40,10 +41,43 @@ struct Epi {
         if constexpr (EPI == EPI_BIAS_DROP_RES) {
             if (e.res_f32) Vec4<float>::load((const float*)e.res + off, r);
             else Vec4<T>::load((const T*)e.res + off, r);
-        } else if constexpr (EPI == EPI_GELU_BWD) {
+        } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_MUL_AUX) {
             Vec4<T>::load((const T*)e.aux + off, r);
         } else if constexpr (EPI == EPI_ADD_RES) {
             Vec4<float>::load((const float*)e.res + off, r);
+        }
+    }
+    // The same element inputs as raw bits, so that many loads can be in flight
+    // before any is converted: a 16-byte load of fp32 sources; for dtype
+    // sources the 8 bytes are loaded twice (low and high halves alike) so
+    // that the source type, a runtime flag, selects an address, not a branch.
+    static __device__ __forceinline__ uint4 load_elem_raw(const EpiArgs& e, int m, int n) {
+        const size_t off = (size_t)m * e.ldo + n;
+        const void* src = nullptr;
+        bool f32 = false;
+        if constexpr (EPI == EPI_BIAS_DROP_RES) {
+            f32 = e.res_f32 != 0;
+            src = f32 ? (const void*)((const float*)e.res + off) : (const void*)((const T*)e.res + off);
+        } else if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_MUL_AUX) {
+            src = (const T*)e.aux + off;
+        } else if constexpr (EPI == EPI_ADD_RES) {
+            f32 = true;
+            src = (const float*)e.res + off;
+        }
+        const uint2* q = reinterpret_cast<const uint2*>(src);
+        const uint2 lo = q[0];
+        const uint2 hi = q[f32 ? 1 : 0];
+        return make_uint4(lo.x, lo.y, hi.x, hi.y);
+    }
+    static __device__ __forceinline__ void elem_from_raw(const EpiArgs& e, uint4 raw, float r[4]) {
+        bool f32 = false;
+        if constexpr (EPI == EPI_BIAS_DROP_RES) f32 = e.res_f32 != 0;
+        if constexpr (EPI == EPI_ADD_RES) f32 = true;
+        if (f32) {
+            r[0] = __uint_as_float(raw.x); r[1] = __uint_as_float(raw.y);
+            r[2] = __uint_as_float(raw.z); r[3] = __uint_as_float(raw.w);
+        } else {
+            Vec4<T>::load(reinterpret_cast<const T*>(&raw), r);
         }
     }
     static __device__ __forceinline__ void finish(const EpiArgs& e, int m, int n, float v[4], const float b[4],
@@ -73,18 +107,28 @@ struct Epi {
             if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
             else Vec4<T>::store((T*)e.out + off, v);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
+            // u is rounded to the storage type first, so GELU(u) and GELU'(u)
+            // are those of the stored u (what a recompute from u would give)
+            float g[4], d[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] += b[i];
-            Vec4<T>::store((T*)e.out + off, v);
-            if (e.out2) {
-                float g[4];
-#pragma unroll
-                for (int i = 0; i < 4; ++i) g[i] = gelu_f(round_through<T>(v[i]));
-                Vec4<T>::store((T*)e.out2 + off, g);
+            for (int i = 0; i < 4; ++i) {
+                const float u = round_through<T>(v[i] + b[i]);
+                float cdf, pdf;
+                normal_cdf_pdf(u, cdf, pdf);
+                g[i] = __fmul_rn(u, cdf);               // gelu_f(u)
+                d[i] = e.gelu_grad_out ? __fmaf_rn(u, pdf, cdf) : u;  // gelu_grad_f(u) or u
             }
+            Vec4<T>::store((T*)e.out + off, d);
+            if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
         } else if constexpr (EPI == EPI_GELU_BWD) {
+            // GELU'(u) rounded to the storage type, exactly as the forward
+            // stores it when GELU is not checkpointed (EPI_MUL_AUX path)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] *= gelu_grad_f(r[i]);
+            for (int i = 0; i < 4; ++i) v[i] *= round_through<T>(gelu_grad_f(r[i]));
+            Vec4<T>::store((T*)e.out + off, v);
+        } else if constexpr (EPI == EPI_MUL_AUX) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] *= r[i];
             Vec4<T>::store((T*)e.out + off, v);
         } else if constexpr (EPI == EPI_HEADSPLIT) {
             const int bb = m / e.S, s = m - bb * e.S, h = n / e.d, c = n - h * e.d;
@@ -259,12 +303,30 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
     // region in the accumulator layout, then reads it back with each lane
     // holding 4 consecutive columns and consecutive lanes consecutive column
     // groups, so global loads (residual, GELU input) and stores run over
-    // contiguous rows.
+    // contiguous rows.  Element inputs are loaded PB blocks ahead, all rows of
+    // a block at once, so that a wave keeps up to 128 registers' worth of
+    // loads in flight instead of waiting out each load's latency.
     typedef Epi<T, EPI> E;
     constexpr int ELD = WN + 4;  // fp32 row stride: 16 rows of a column group hit distinct banks
     float* est = reinterpret_cast<float*>(smem_raw) + wave * 32 * ELD;
     constexpr int GPR = WN / 4;           // 4-column groups per row
     constexpr int RPI = 64 / GPR;         // rows per lane-iteration
+    constexpr int NIT = 32 / RPI;         // lane-iterations per block
+    constexpr int BUDGET = EPI == EPI_BIAS_DROP_RES ? 64 : 128;  // dropout's Philox needs registers too
+    constexpr int PBMAX = BUDGET / (NIT * 4) < 1 ? 1 : BUDGET / (NIT * 4);
+    constexpr int PB = E::kElem ? (MI < PBMAX ? MI : PBMAX) : 1;
+    const int cg = lane % GPR, r0 = lane / GPR;
+    const int n = n0 + wn * WN + cg * 4;
+    const int mrow0 = m0 + wm * WM + r0;  // this lane's first row of block 0
+    float b[4] = {0, 0, 0, 0};
+    E::load_bias(p.ea, n, b);
+    uint4 el[PB][NIT];
+    if constexpr (E::kElem) {
+#pragma unroll
+        for (int pb = 0; pb < PB; ++pb)
+#pragma unroll
+            for (int it = 0; it < NIT; ++it) el[pb][it] = E::load_elem_raw(p.ea, mrow0 + pb * 32 + it * RPI, n);
+    }
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
@@ -277,29 +339,20 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
             }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
-        const int cg = lane % GPR, r0 = lane / GPR;
-        const int n = n0 + wn * WN + cg * 4;
-        float b[4] = {0, 0, 0, 0};
-        E::load_bias(p.ea, n, b);
-        // rows in chunks of CH: the chunk's element loads are issued together,
-        // then finished; the chunk loop stays rolled so that this block loop
-        // (which indexes acc) can be fully unrolled even with a large finish
-        constexpr int NIT = 32 / RPI, CH = NIT < 4 ? NIT : 4;
-#pragma unroll 1
-        for (int c0 = 0; c0 < NIT; c0 += CH) {
-            float el[CH][4];
 #pragma unroll
-            for (int it = 0; it < CH; ++it) {
+        for (int it = 0; it < NIT; ++it) {
+            const int rr = it * RPI + r0;
+            const float4 q = *reinterpret_cast<const float4*>(est + rr * ELD + cg * 4);
+            float v[4] = {q.x, q.y, q.z, q.w};
+            float r[4] = {0, 0, 0, 0};
+            if constexpr (E::kElem) E::elem_from_raw(p.ea, el[i % PB][it], r);
+            E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
+        }
+        if constexpr (E::kElem) {
+            if (i + PB < MI) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) el[it][t] = 0.0f;
-                E::load_elem(p.ea, m0 + wm * WM + i * 32 + (c0 + it) * RPI + r0, n, el[it]);
-            }
-#pragma unroll
-            for (int it = 0; it < CH; ++it) {
-                const int rr = (c0 + it) * RPI + r0;
-                const float4 q = *reinterpret_cast<const float4*>(est + rr * ELD + cg * 4);
-                float v[4] = {q.x, q.y, q.z, q.w};
-                E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, el[it]);
+                for (int it = 0; it < NIT; ++it)
+                    el[i % PB][it] = E::load_elem_raw(p.ea, mrow0 + (i + PB) * 32 + it * RPI, n);
             }
         }
         __builtin_amdgcn_wave_barrier();
@@ -487,7 +540,10 @@ struct DlPlan {
     // tile whose origin is at byte address `origin`, into LDS bytes lds_bytes
     __device__ __forceinline__ void issue(const char* origin, uint32_t lds_bytes, int wave) const {
 #pragma unroll
-        for (int j = 0; j < PER; ++j) dl_load16(origin, voff[j], lds_bytes + (uint32_t)(wave + j * NW) * 1024u);
+        for (int j = 0; j < PER; ++j) issue_one(origin, lds_bytes, wave, j);
+    }
+    __device__ __forceinline__ void issue_one(const char* origin, uint32_t lds_bytes, int wave, int j) const {
+        dl_load16(origin, voff[j], lds_bytes + (uint32_t)(wave + j * NW) * 1024u);
     }
 };
 
@@ -687,6 +743,225 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
     }
 }
 
+// ------------------------------------------------- 256x256 tiles, one wave per SIMD
+// Four waves in a 2 x 2 grid of 128x128 wave tiles; k tiles 64 deep in two
+// LDS stages of 64 KB.  Compared with two waves per SIMD on 128x64 wave
+// tiles: 8 fragment reads feed 16 MFMAs (a third fewer LDS bytes per MFMA,
+// and LDS traffic is what bounds the loop), k-major rows are 128 bytes so
+// every direct load fetches whole cache lines, and there is one barrier per
+// 64 k instead of per 32.  No second wave on a SIMD covers waits, so the k
+// loop is software pipelined by hand: each MFMA is paired with at most two
+// memory instructions (a fragment read for the next k-step, a direct load of
+// the tile after next), fenced so that the pairing survives scheduling.
+constexpr int QKT = 64;  // k per stage
+constexpr int QNS = 2;   // stages
+
+// k-major rows of 64 k (128 bytes): 16-byte chunk c of row r is stored at
+// chunk c ^ ((r >> 1) & 7), so the 16 rows read by each quarter of a wave's
+// 128-bit fragment load fall in 16 distinct 16-byte bank groups.
+__device__ __forceinline__ int kmaj64_off(int row, int k) {
+    return row * 64 + (((k >> 3) ^ ((row >> 1) & 7)) << 3) + (k & 7);
+}
+
+// Direct-load plan of one 256-row operand tile, 64 k deep, for one of four
+// waves: PER wave-loads each (q = wave + 4 j); voff[j] is this lane's
+// source byte offset from the tile origin.
+template <typename T, bool KMAJ, int R>
+struct Dl4Plan {
+    static constexpr int NQ = R * QKT * (int)sizeof(T) / 1024;
+    static constexpr int PER = NQ / 4;
+    uint32_t voff[PER];
+    __device__ __forceinline__ Dl4Plan(int ld, int wave, int lane) {
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+            const int slot = (wave + j * 4) * 64 + lane;
+            if constexpr (KMAJ) {
+                const int row = slot >> 3, c = (slot & 7) ^ ((row >> 1) & 7);
+                voff[j] = (uint32_t)((row * ld + c * 8) * (int)sizeof(T));
+            } else {
+                constexpr int CPR = R / 8;
+                const int k = slot / CPR, ch = (slot % CPR) ^ (4 * (k & 3));
+                voff[j] = (uint32_t)((k * ld + ch * 8) * (int)sizeof(T));
+            }
+        }
+    }
+    __device__ __forceinline__ void issue_one(const char* origin, uint32_t lds_bytes, int wave, int j) const {
+        dl_load16(origin, voff[j], lds_bytes + (uint32_t)(wave + j * 4) * 1024u);
+    }
+};
+
+template <typename T, bool KMAJ, int R>
+__device__ __forceinline__ typename MfmaOp<T>::v8 dl4_frag(const T* lds, int rb, int ks, int lane) {
+    if constexpr (KMAJ) {
+        typedef typename MfmaOp<T>::v8 v8;
+        const int row = rb + (lane & 31);
+        return *reinterpret_cast<const v8*>(lds + kmaj64_off(row, ks * 16 + (lane >> 5) * 8));
+    } else {
+        return dl_frag<T, false, R>(lds, rb, ks, lane);  // [k][R] layout, any k depth
+    }
+}
+
+// acc + the sum of the 8 elements of an operand fragment: packed dot
+// products against (1, 1), exact products summed in fp32.
+__device__ __forceinline__ float frag_sum8(f16x8 x, float acc) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2) acc = __builtin_amdgcn_fdot2((h2){x[e], x[e + 1]}, (h2){1, 1}, acc, false);
+    return acc;
+}
+__device__ __forceinline__ float frag_sum8(bf16x8 x, float acc) {
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+    for (int e = 0; e < 8; e += 2)
+        acc = __builtin_amdgcn_fdot2_f32_bf16((b2){x[e], x[e + 1]}, (b2){1, 1}, acc, false);
+    return acc;
+}
+
+template <typename T, bool AK, bool BKM, int EPI>
+__global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
+    constexpr int BM = 256, BN = 256, NT = 256, WM = 128, WN = 128;
+    constexpr int AEL = BM * QKT, STAGE = (BM + BN) * QKT;
+    typedef typename MfmaOp<T>::v8 v8;
+
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T* smem = reinterpret_cast<T*>(smem_raw);
+    // The 256 accumulators per lane must live in the accumulation registers;
+    // the compiler gives MFMAs that operand form only in kernels that it
+    // sees using those registers.
+    asm volatile("; accumulation registers in use" ::: "a0");
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int tm = p.M / BM, tn = p.N / BN;
+    const int wave_s = __builtin_amdgcn_readfirstlane(wave);
+    const Dl4Plan<T, AK, BM> pa(p.lda, wave_s, lane);
+    const Dl4Plan<T, BKM, BN> pb(p.ldb, wave_s, lane);
+    const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem_raw;
+    for (int pid = blockIdx.x; pid < tm * tn; pid += gridDim.x) {
+        if (pid != (int)blockIdx.x) __syncthreads();  // the last epilogue is done with LDS
+        int im, in_;
+        tile_of(pid, tm, tn, im, in_);
+        const int m0 = im * BM, n0 = in_ * BN;
+        const int kbeg = blockIdx.z * p.k_per_split;
+        const int kend = min(p.K, kbeg + p.k_per_split);
+        const int nk = (kend - kbeg) / QKT;
+        const T* A = (const T*)p.A;
+        const T* B = (const T*)p.B;
+        // bias gradient fused into a weight gradient: every lane sums the A
+        // (= dY^T) fragments it feeds to the MFMAs, row (lane & 31) of each
+        // 32-row block over its half of each k-step; tile column 0 stores.
+        float rsa[4] = {0, 0, 0, 0};
+
+        f32x16 acc[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+        const char* oa = reinterpret_cast<const char*>(A + (AK ? (size_t)m0 * p.lda + kbeg : (size_t)kbeg * p.lda + m0));
+        const char* ob = reinterpret_cast<const char*>(B + (BKM ? (size_t)n0 * p.ldb + kbeg : (size_t)kbeg * p.ldb + n0));
+        const size_t sta = (size_t)(AK ? QKT : QKT * p.lda) * sizeof(T);
+        const size_t stb = (size_t)(BKM ? QKT : QKT * p.ldb) * sizeof(T);
+        // direct load q of the current origins (0..7 A, 8..15 B) into stage st
+        auto load_q = [&](int st, int q) {
+            const uint32_t base = lds0 + (uint32_t)(st * STAGE * (int)sizeof(T));
+            if (q < 8) pa.issue_one(oa, base, wave_s, q);
+            else pb.issue_one(ob, base + AEL * (uint32_t)sizeof(T), wave_s, q - 8);
+        };
+        auto frag = [&](const T* st, int ks, int q) -> v8 {
+            if (q < 4) return dl4_frag<T, AK, BM>(st, wm * WM + q * 32, ks, lane);
+            return dl4_frag<T, BKM, BN>(st + AEL, wn * WN + (q - 4) * 32, ks, lane);
+        };
+        v8 fr[2][8];  // fragment sets: [0..3] A, [4..7] B
+        // 16 MFMAs on fragment set S, paired with reads of k-step RKS of stage
+        // RST into set S^1 (if RD) and direct loads into stage LST (if LD);
+        // RD and LD are literal 0 or 1
+#define TEL_DL4_BLOCK(S, RD, RST, RKS, LD, LST)                                                          \
+    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                     \
+        acc[q >> 2][q & 3] = MfmaOp<T>::mma(fr[S][4 + (q & 3)], fr[S][q >> 2], acc[q >> 2][q & 3]);      \
+        if (!AK && q < 4) rsa[q] = frag_sum8(fr[S][q], rsa[q]);                                          \
+        if (RD && q < 8) fr[(S) ^ 1][q] = frag((RST), (RKS), q);                                          \
+        if (LD) load_q((LST), q);                                                                        \
+        __builtin_amdgcn_sched_barrier(0);                                                               \
+    }
+
+#pragma unroll
+        for (int q = 0; q < 16; ++q) load_q(0, q);
+        oa += sta;
+        ob += stb;
+        if (nk > 1) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) load_q(1, q);
+            oa += sta;
+            ob += stb;
+            wait_vmcnt<16>();  // tile 0 landed, tile 1 may be in flight
+        } else {
+            wait_vmcnt<0>();
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 8; ++q) fr[0][q] = frag(smem, 0, q);
+        // Per k tile kt (stage kt & 1; k-step 0 fragments already in set 0):
+        // k-steps 0..2 each read the next k-step of the stage; then tile kt+1
+        // is made visible (its loads landed on every wave, and every wave has
+        // read all of tile kt, whose stage tile kt+2 now overwrites), and
+        // k-step 3 reads tile kt+1's first k-step.  The steady state (a tile
+        // still to load) is one branch-free block; the last two tiles are
+        // peeled.
+        int kt = 0;
+        for (; kt < nk - 2; ++kt) {
+            const T* cur = smem + (kt & 1) * STAGE;
+            const T* nxt = smem + ((kt + 1) & 1) * STAGE;
+            __builtin_amdgcn_sched_barrier(0);
+            TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0)
+            TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0)
+            TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0)
+            wait_vmcnt<0>();
+            __syncthreads();
+            TEL_DL4_BLOCK(1, 1, nxt, 0, 1, (kt & 1))
+            oa += sta;
+            ob += stb;
+        }
+        for (; kt < nk; ++kt) {
+            const T* cur = smem + (kt & 1) * STAGE;
+            const T* nxt = smem + ((kt + 1) & 1) * STAGE;
+            __builtin_amdgcn_sched_barrier(0);
+            TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0)
+            TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0)
+            TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0)
+            if (kt + 1 < nk) {
+                wait_vmcnt<0>();
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 8; ++q) fr[0][q] = frag(nxt, 0, q);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            TEL_DL4_BLOCK(1, 0, cur, 0, 0, 0)
+        }
+#undef TEL_DL4_BLOCK
+        __syncthreads();
+
+        if constexpr (!AK) {
+            if (p.rsum != nullptr && in_ == 0) {
+                // lanes l and l + 32 hold the two k halves of row l; waves with
+                // wn = 1 computed the same sums
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float t = rsa[i] + __shfl_xor(rsa[i], 32, 64);
+                    if (wn == 0 && lane < 32) {
+                        const int mrow = m0 + wm * WM + i * 32 + lane;
+                        if (gridDim.z > 1) reinterpret_cast<float*>(p.rsum)[(size_t)blockIdx.z * p.M + mrow] = t;
+                        else reinterpret_cast<T*>(p.rsum)[mrow] = from_f<T>(t);
+                    }
+                }
+            }
+        }
+        gemm_epilogue<T, EPI, BM, BN, 2, 2>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
+    }
+}
+
 // Deterministic split-K reduction: out[m][n] = sum_z ws[z][m][n] in z order.
 // The first M/4 threads also add the per-split row sums (bias gradients).
 template <typename T>
@@ -877,11 +1152,48 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
+template <typename T, bool AK, bool BKM, int EPI>
+static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
+    float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
+    void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
+    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
+    auto kern = gemm_dl4_kernel<T, AK, BKM, EPI>;
+    size_t lds = (size_t)QNS * 512 * QKT * sizeof(T);
+    lds = std::max(lds, epilogue_lds_bytes<256, 256, 2, 2>());
+    lds = std::max(lds, (size_t)256 * 8 * 4);
+    static int slots = 0;  // workgroups of this kernel resident on the whole device
+    if (!slots) {
+        hipError_t e = set_lds(kern, lds);
+        if (e != hipSuccess) return e;
+        int per_cu = 0, dev = 0, cus = 0;
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds);
+        if (e != hipSuccess) return e;
+        e = hipGetDevice(&dev);
+        if (e != hipSuccess) return e;
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        slots = std::max(1, per_cu) * std::max(1, cus);
+    }
+    const int tiles = (g.M / 256) * (g.N / 256);
+    int gx = std::min(tiles, std::max(8, slots / splits / 8 * 8));
+    hipLaunchKernelGGL(kern, dim3(gx, 1, splits), dim3(256), lds, st, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    const size_t n4 = (size_t)g.M * g.N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
+                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea, rs_part,
+                       rsum ? reinterpret_cast<T*>(g.rowsum_out) : (T*)nullptr);
+    return hipGetLastError();
+}
+
 // 256x256 tiles run 8 waves (2 per SIMD) in a 2 x 4 grid of 128x64 wave
 // tiles: the second wave of each SIMD issues its MFMAs while the first waits
 // on LDS or the barrier, which more than pays for the 1.5x LDS fragment
 // reads of the narrower wave tile.
-constexpr int W256N = 4;
+#ifndef GEMM_W256N
+#define GEMM_W256N 2
+#endif
+constexpr int W256N = GEMM_W256N;
 // 256x128 tiles likewise run 8 waves, in a 4 x 2 grid of 64x64 wave tiles.
 constexpr int W128M = 4;
 template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
@@ -890,20 +1202,27 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
         // operands stream straight into LDS; only the GELU-on-load variant
         // (weight gradient under GELU checkpointing) uses the register-staged
         // kernel, which can transform B on its way to LDS
-        if (c.BM == 256 && c.BN == 256) return launch_dl<T, 256, 256, 2, W256N, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+        if (c.BM == 256 && c.BN == 256) {
+            // the GELU epilogue's VALU work runs better with two waves per SIMD
+            if constexpr (W256N == 2 && EPI != EPI_BIAS_GELU)
+                return launch_dl4<T, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+            else
+                return launch_dl<T, 256, 256, 2, 4, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+        }
         if (c.BM == 256 && c.BN == 128) return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
         return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
+    } else {
+        if (c.BM == 256 && c.BN == 256) {
+            int s = splitk_for(g, 256, 256);
+            return launch_mfma<T, 256, 256, 2, 4, AK, BKM, EPI, BGELU>(g, st, s);
+        }
+        if (c.BM == 256 && c.BN == 128) {
+            int s = splitk_for(g, 256, 128);
+            return launch_mfma<T, 256, 128, W128M, 2, AK, BKM, EPI, BGELU>(g, st, s);
+        }
+        int s = splitk_for(g, 128, 128);
+        return launch_mfma<T, 128, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
     }
-    if (c.BM == 256 && c.BN == 256) {
-        int s = splitk_for(g, 256, 256);
-        return launch_mfma<T, 256, 256, 2, W256N, AK, BKM, EPI, BGELU>(g, st, s);
-    }
-    if (c.BM == 256 && c.BN == 128) {
-        int s = splitk_for(g, 256, 128);
-        return launch_mfma<T, 256, 128, W128M, 2, AK, BKM, EPI, BGELU>(g, st, s);
-    }
-    int s = splitk_for(g, 128, 128);
-    return launch_mfma<T, 128, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
 }
 
 // Operand layouts the layer uses with each epilogue: projections (A, B
@@ -913,7 +1232,9 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
 template <int EPI, bool AK, bool BKM>
 constexpr bool mfma_combo() {
     if (AK && BKM) return EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES || EPI == EPI_BIAS_GELU || EPI == EPI_STORE;
-    if (AK && !BKM) return EPI == EPI_GELU_BWD || EPI == EPI_STORE || EPI == EPI_HEADSPLIT || EPI == EPI_ADD_RES;
+    if (AK && !BKM)
+        return EPI == EPI_GELU_BWD || EPI == EPI_MUL_AUX || EPI == EPI_STORE || EPI == EPI_HEADSPLIT ||
+               EPI == EPI_ADD_RES;
     if (!AK && !BKM) return EPI == EPI_STORE;
     return false;
 }
@@ -973,6 +1294,7 @@ static hipError_t dispatch_type(const GemmDesc& g, hipStream_t st, bool force_si
         case EPI_GELU_BWD: return dispatch_epi<T, EPI_GELU_BWD>(g, st, force_simt);
         case EPI_HEADSPLIT: return dispatch_epi<T, EPI_HEADSPLIT>(g, st, force_simt);
         case EPI_ADD_RES: return dispatch_epi<T, EPI_ADD_RES>(g, st, force_simt);
+        case EPI_MUL_AUX: return dispatch_epi<T, EPI_MUL_AUX>(g, st, force_simt);
     }
     return hipErrorInvalidValue;
 }

@@ -134,7 +134,7 @@ static void make_plan(tel_layer* L) {
         place(p.mu2, T * f4, true, sv, sc);
         place(p.rs2, T * f4, true, sv, sc);
         place(p.ln2_out, T * H * e, true, sv, sc);
-        place(p.u, T * F * e, true, sv, sc);
+        place(p.u, T * F * e, true, sv, sc);  // GELU input u, or GELU'(u) unless GELU is checkpointed
         place(p.g, T * F * e, !gck, sv, sc);
     } else {
         place(p.qkvh, 3 * T * H * e, true, sv, sc);
@@ -348,6 +348,7 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         TIMED(TEL_K_LN2_FWD, ln_forward(l2, st));
         g = proj(bs.of(p.ln2_out), P->w_1, F, H, EPI_BIAS_GELU);
         g.ea.out = bs.of(p.u); g.ea.ldo = F; g.ea.bias = P->b_1; g.ea.out2 = bs.of(p.g);
+        g.ea.gelu_grad_out = !c.gelu_checkpoint;
         TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
         g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
         g.ea.out = y; g.ea.ldo = H; g.ea.out_f32 = 0; g.ea.bias = P->b_2;
@@ -368,6 +369,7 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         TIMED(TEL_K_LN1_FWD, ln_forward(l1, st));
         g = proj(bs.of(p.x1e), P->w_1, F, H, EPI_BIAS_GELU);
         g.ea.out = bs.of(p.u); g.ea.ldo = F; g.ea.bias = P->b_1; g.ea.out2 = bs.of(p.g);
+        g.ea.gelu_grad_out = !c.gelu_checkpoint;
         TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
         g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
         g.ea.out = bs.of(p.res2); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_2;
@@ -462,7 +464,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     if (c.pre_ln) {
         // y = x1 + drop2(g W2^T + b2)
         HIP_TRY(dropout_apply(dt, dy, bs.of(p.df), (size_t)T * H, d2, st));
-        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, EPI_GELU_BWD);
+        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
         TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck, G->b_2));
@@ -519,7 +521,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.part_g = part_ln_g; lb.part_b = part_ln_b;
         TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
-        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, EPI_GELU_BWD);
+        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
         TIMED(TEL_K_FFN2_WGRAD, wgrad(bs.of(p.df), g_src, H, F, G->w_2, gck, G->b_2));
