@@ -817,17 +817,22 @@ __device__ __forceinline__ float frag_sum8(bf16x8 x, float acc) {
     return acc;
 }
 
-template <typename T, bool AK, bool BKM, int EPI>
+template <typename T, int BN, bool AK, bool BKM, int EPI>
 __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
-    constexpr int BM = 256, BN = 256, NT = 256, WM = 128, WN = 128;
+    constexpr int BM = 256, WM = 128, WN = BN / 2;
+    constexpr int NI = WN / 32;           // B fragments (and MFMA columns) per k-step
+    constexpr int NF = 4 + NI;            // fragments per k-step: 4 A, NI B
+    constexpr int NQ = 4 * NI;            // MFMAs per k-step
+    constexpr int LA = BM * QKT * (int)sizeof(T) / 1024 / 4;  // direct loads per wave per stage: A
+    constexpr int LPW = LA + BN * QKT * (int)sizeof(T) / 1024 / 4;  // A and B
     constexpr int AEL = BM * QKT, STAGE = (BM + BN) * QKT;
     typedef typename MfmaOp<T>::v8 v8;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T* smem = reinterpret_cast<T*>(smem_raw);
-    // The 256 accumulators per lane must live in the accumulation registers;
-    // the compiler gives MFMAs that operand form only in kernels that it
-    // sees using those registers.
+    // The accumulators (up to 256 per lane) must live in the accumulation
+    // registers; the compiler gives MFMAs that operand form only in kernels
+    // that it sees using those registers.
     asm volatile("; accumulation registers in use" ::: "a0");
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -852,11 +857,11 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
         // 32-row block over its half of each k-step; tile column 0 stores.
         float rsa[4] = {0, 0, 0, 0};
 
-        f32x16 acc[4][4];
+        f32x16 acc[4][NI];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
+            for (int j = 0; j < NI; ++j)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -864,45 +869,47 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
         const char* ob = reinterpret_cast<const char*>(B + (BKM ? (size_t)n0 * p.ldb + kbeg : (size_t)kbeg * p.ldb + n0));
         const size_t sta = (size_t)(AK ? QKT : QKT * p.lda) * sizeof(T);
         const size_t stb = (size_t)(BKM ? QKT : QKT * p.ldb) * sizeof(T);
-        // direct load q of the current origins (0..7 A, 8..15 B) into stage st
+        // direct load q of the current origins (0..LA-1 A, then B) into stage st
         auto load_q = [&](int st, int q) {
             const uint32_t base = lds0 + (uint32_t)(st * STAGE * (int)sizeof(T));
-            if (q < 8) pa.issue_one(oa, base, wave_s, q);
-            else pb.issue_one(ob, base + AEL * (uint32_t)sizeof(T), wave_s, q - 8);
+            if (q < LA) pa.issue_one(oa, base, wave_s, q);
+            else pb.issue_one(ob, base + AEL * (uint32_t)sizeof(T), wave_s, q - LA);
         };
         auto frag = [&](const T* st, int ks, int q) -> v8 {
             if (q < 4) return dl4_frag<T, AK, BM>(st, wm * WM + q * 32, ks, lane);
             return dl4_frag<T, BKM, BN>(st + AEL, wn * WN + (q - 4) * 32, ks, lane);
         };
-        v8 fr[2][8];  // fragment sets: [0..3] A, [4..7] B
-        // 16 MFMAs on fragment set S, paired with reads of k-step RKS of stage
-        // RST into set S^1 (if RD) and direct loads into stage LST (if LD);
-        // RD and LD are literal 0 or 1
+        v8 fr[2][NF];  // fragment sets: [0..3] A, [4..] B
+        // NQ MFMAs on fragment set S, paired with reads of k-step RKS of stage
+        // RST into set S^1 (if RD) and the LPW direct loads into stage LST (if
+        // LD), spread over the MFMAs; RD and LD are literal 0 or 1
 #define TEL_DL4_BLOCK(S, RD, RST, RKS, LD, LST)                                                          \
-    _Pragma("unroll") for (int q = 0; q < 16; ++q) {                                                     \
-        acc[q >> 2][q & 3] = MfmaOp<T>::mma(fr[S][4 + (q & 3)], fr[S][q >> 2], acc[q >> 2][q & 3]);      \
+    _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                     \
+        acc[q / NI][q % NI] = MfmaOp<T>::mma(fr[S][4 + q % NI], fr[S][q / NI], acc[q / NI][q % NI]);     \
         if (!AK && q < 4) rsa[q] = frag_sum8(fr[S][q], rsa[q]);                                          \
-        if (RD && q < 8) fr[(S) ^ 1][q] = frag((RST), (RKS), q);                                          \
-        if (LD) load_q((LST), q);                                                                        \
+        if (RD && q < NF) fr[(S) ^ 1][q] = frag((RST), (RKS), q);                                         \
+        if (LD) {                                                                                        \
+            _Pragma("unroll") for (int l = q * LPW / NQ; l < (q + 1) * LPW / NQ; ++l) load_q((LST), l);  \
+        }                                                                                                \
         __builtin_amdgcn_sched_barrier(0);                                                               \
     }
 
 #pragma unroll
-        for (int q = 0; q < 16; ++q) load_q(0, q);
+        for (int q = 0; q < LPW; ++q) load_q(0, q);
         oa += sta;
         ob += stb;
         if (nk > 1) {
 #pragma unroll
-            for (int q = 0; q < 16; ++q) load_q(1, q);
+            for (int q = 0; q < LPW; ++q) load_q(1, q);
             oa += sta;
             ob += stb;
-            wait_vmcnt<16>();  // tile 0 landed, tile 1 may be in flight
+            wait_vmcnt<LPW>();  // tile 0 landed, tile 1 may be in flight
         } else {
             wait_vmcnt<0>();
         }
         __syncthreads();
 #pragma unroll
-        for (int q = 0; q < 8; ++q) fr[0][q] = frag(smem, 0, q);
+        for (int q = 0; q < NF; ++q) fr[0][q] = frag(smem, 0, q);
         // Per k tile kt (stage kt & 1; k-step 0 fragments already in set 0):
         // k-steps 0..2 each read the next k-step of the stage; then tile kt+1
         // is made visible (its loads landed on every wave, and every wave has
@@ -935,7 +942,7 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
                 wait_vmcnt<0>();
                 __syncthreads();
 #pragma unroll
-                for (int q = 0; q < 8; ++q) fr[0][q] = frag(nxt, 0, q);
+                for (int q = 0; q < NF; ++q) fr[0][q] = frag(nxt, 0, q);
             }
             __builtin_amdgcn_sched_barrier(0);
             TEL_DL4_BLOCK(1, 0, cur, 0, 0, 0)
@@ -1152,14 +1159,14 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
-template <typename T, bool AK, bool BKM, int EPI>
+template <typename T, int BN, bool AK, bool BKM, int EPI>
 static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
     float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
     void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
     GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
-    auto kern = gemm_dl4_kernel<T, AK, BKM, EPI>;
-    size_t lds = (size_t)QNS * 512 * QKT * sizeof(T);
-    lds = std::max(lds, epilogue_lds_bytes<256, 256, 2, 2>());
+    auto kern = gemm_dl4_kernel<T, BN, AK, BKM, EPI>;
+    size_t lds = (size_t)QNS * (256 + BN) * QKT * sizeof(T);
+    lds = std::max(lds, epilogue_lds_bytes<256, BN, 2, 2>());
     lds = std::max(lds, (size_t)256 * 8 * 4);
     static int slots = 0;  // workgroups of this kernel resident on the whole device
     if (!slots) {
@@ -1174,7 +1181,7 @@ static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
         if (e != hipSuccess) return e;
         slots = std::max(1, per_cu) * std::max(1, cus);
     }
-    const int tiles = (g.M / 256) * (g.N / 256);
+    const int tiles = (g.M / 256) * (g.N / BN);
     int gx = std::min(tiles, std::max(8, slots / splits / 8 * 8));
     hipLaunchKernelGGL(kern, dim3(gx, 1, splits), dim3(256), lds, st, p);
     hipError_t e = hipGetLastError();
@@ -1186,15 +1193,15 @@ static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
-// 256x256 tiles run 8 waves (2 per SIMD) in a 2 x 4 grid of 128x64 wave
-// tiles: the second wave of each SIMD issues its MFMAs while the first waits
-// on LDS or the barrier, which more than pays for the 1.5x LDS fragment
-// reads of the narrower wave tile.
+// 256x256 and 256x128 tiles run the four-wave kernel (one wave per SIMD,
+// 128 x BN/2 wave tiles, 64-deep k tiles), except under the GELU forward
+// epilogue and the short-k dropout epilogue, whose VALU work hides better
+// with two waves per SIMD: the eight-wave kernel in a 2 x 4 grid of 128x64
+// wave tiles (256x256), or a 4 x 2 grid of 64x64 (256x128).
 #ifndef GEMM_W256N
 #define GEMM_W256N 2
 #endif
 constexpr int W256N = GEMM_W256N;
-// 256x128 tiles likewise run 8 waves, in a 4 x 2 grid of 64x64 wave tiles.
 constexpr int W128M = 4;
 template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
 static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
@@ -1205,11 +1212,19 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
         if (c.BM == 256 && c.BN == 256) {
             // the GELU epilogue's VALU work runs better with two waves per SIMD
             if constexpr (W256N == 2 && EPI != EPI_BIAS_GELU)
-                return launch_dl4<T, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+                return launch_dl4<T, 256, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
             else
                 return launch_dl<T, 256, 256, 2, 4, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
         }
-        if (c.BM == 256 && c.BN == 128) return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+        if (c.BM == 256 && c.BN == 128) {
+            // the dropout epilogue's Philox work, like GELU's, favours two waves
+            // per SIMD unless the k loop is long enough to dominate
+            if constexpr (EPI != EPI_BIAS_GELU) {
+                if (EPI != EPI_BIAS_DROP_RES || g.K >= 2048)
+                    return launch_dl4<T, 128, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+            }
+            return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+        }
         return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
     } else {
         if (c.BM == 256 && c.BN == 256) {
