@@ -817,12 +817,12 @@ __device__ __forceinline__ float frag_sum8(bf16x8 x, float acc) {
     return acc;
 }
 
-template <typename T, int BN, bool AK, bool BKM, int EPI>
+template <typename T, int BM, int BN, bool AK, bool BKM, int EPI>
 __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
-    constexpr int BM = 256, WM = 128, WN = BN / 2;
-    constexpr int NI = WN / 32;           // B fragments (and MFMA columns) per k-step
-    constexpr int NF = 4 + NI;            // fragments per k-step: 4 A, NI B
-    constexpr int NQ = 4 * NI;            // MFMAs per k-step
+    constexpr int WM = BM / 2, WN = BN / 2;
+    constexpr int MI = WM / 32, NI = WN / 32;  // A and B fragments per k-step
+    constexpr int NF = MI + NI;                // fragments per k-step: MI A, NI B
+    constexpr int NQ = MI * NI;                // MFMAs per k-step
     constexpr int LA = BM * QKT * (int)sizeof(T) / 1024 / 4;  // direct loads per wave per stage: A
     constexpr int LPW = LA + BN * QKT * (int)sizeof(T) / 1024 / 4;  // A and B
     constexpr int AEL = BM * QKT, STAGE = (BM + BN) * QKT;
@@ -855,11 +855,13 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
         // bias gradient fused into a weight gradient: every lane sums the A
         // (= dY^T) fragments it feeds to the MFMAs, row (lane & 31) of each
         // 32-row block over its half of each k-step; tile column 0 stores.
-        float rsa[4] = {0, 0, 0, 0};
-
-        f32x16 acc[4][NI];
+        float rsa[MI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < MI; ++i) rsa[i] = 0.0f;
+
+        f32x16 acc[MI][NI];
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
@@ -876,17 +878,17 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
             else pb.issue_one(ob, base + AEL * (uint32_t)sizeof(T), wave_s, q - LA);
         };
         auto frag = [&](const T* st, int ks, int q) -> v8 {
-            if (q < 4) return dl4_frag<T, AK, BM>(st, wm * WM + q * 32, ks, lane);
-            return dl4_frag<T, BKM, BN>(st + AEL, wn * WN + (q - 4) * 32, ks, lane);
+            if (q < MI) return dl4_frag<T, AK, BM>(st, wm * WM + q * 32, ks, lane);
+            return dl4_frag<T, BKM, BN>(st + AEL, wn * WN + (q - MI) * 32, ks, lane);
         };
-        v8 fr[2][NF];  // fragment sets: [0..3] A, [4..] B
+        v8 fr[2][NF];  // fragment sets: [0..MI-1] A, [MI..] B
         // NQ MFMAs on fragment set S, paired with reads of k-step RKS of stage
         // RST into set S^1 (if RD) and the LPW direct loads into stage LST (if
         // LD), spread over the MFMAs; RD and LD are literal 0 or 1
 #define TEL_DL4_BLOCK(S, RD, RST, RKS, LD, LST)                                                          \
     _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                     \
-        acc[q / NI][q % NI] = MfmaOp<T>::mma(fr[S][4 + q % NI], fr[S][q / NI], acc[q / NI][q % NI]);     \
-        if (!AK && q < 4) rsa[q] = frag_sum8(fr[S][q], rsa[q]);                                          \
+        acc[q / NI][q % NI] = MfmaOp<T>::mma(fr[S][MI + q % NI], fr[S][q / NI], acc[q / NI][q % NI]);    \
+        if (!AK && q < MI) rsa[q] = frag_sum8(fr[S][q], rsa[q]);                                         \
         if (RD && q < NF) fr[(S) ^ 1][q] = frag((RST), (RKS), q);                                         \
         if (LD) {                                                                                        \
             _Pragma("unroll") for (int l = q * LPW / NQ; l < (q + 1) * LPW / NQ; ++l) load_q((LST), l);  \
@@ -955,7 +957,7 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
                 // lanes l and l + 32 hold the two k halves of row l; waves with
                 // wn = 1 computed the same sums
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < MI; ++i) {
                     const float t = rsa[i] + __shfl_xor(rsa[i], 32, 64);
                     if (wn == 0 && lane < 32) {
                         const int mrow = m0 + wm * WM + i * 32 + lane;
@@ -1159,14 +1161,14 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
-template <typename T, int BN, bool AK, bool BKM, int EPI>
+template <typename T, int BM, int BN, bool AK, bool BKM, int EPI>
 static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
     float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
     void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
     GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
-    auto kern = gemm_dl4_kernel<T, BN, AK, BKM, EPI>;
-    size_t lds = (size_t)QNS * (256 + BN) * QKT * sizeof(T);
-    lds = std::max(lds, epilogue_lds_bytes<256, BN, 2, 2>());
+    auto kern = gemm_dl4_kernel<T, BM, BN, AK, BKM, EPI>;
+    size_t lds = (size_t)QNS * (BM + BN) * QKT * sizeof(T);
+    lds = std::max(lds, epilogue_lds_bytes<BM, BN, 2, 2>());
     lds = std::max(lds, (size_t)256 * 8 * 4);
     static int slots = 0;  // workgroups of this kernel resident on the whole device
     if (!slots) {
@@ -1181,7 +1183,7 @@ static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
         if (e != hipSuccess) return e;
         slots = std::max(1, per_cu) * std::max(1, cus);
     }
-    const int tiles = (g.M / 256) * (g.N / BN);
+    const int tiles = (g.M / BM) * (g.N / BN);
     int gx = std::min(tiles, std::max(8, slots / splits / 8 * 8));
     hipLaunchKernelGGL(kern, dim3(gx, 1, splits), dim3(256), lds, st, p);
     hipError_t e = hipGetLastError();
@@ -1193,11 +1195,12 @@ static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
-// 256x256 and 256x128 tiles run the four-wave kernel (one wave per SIMD,
-// 128 x BN/2 wave tiles, 64-deep k tiles), except under the GELU forward
-// epilogue and the short-k dropout epilogue, whose VALU work hides better
-// with two waves per SIMD: the eight-wave kernel in a 2 x 4 grid of 128x64
-// wave tiles (256x256), or a 4 x 2 grid of 64x64 (256x128).
+// Tiles run the four-wave kernel (2 x 2 waves of BM/2 x BN/2, 64-deep k
+// tiles), except under the GELU forward epilogue and the short-k dropout
+// epilogue, whose VALU work hides better with two waves per SIMD: the
+// eight-wave kernel in a 2 x 4 grid of 128x64 wave tiles (256x256), a 4 x 2
+// grid of 64x64 (256x128), or the four-wave 2 x 2 grid of 64x64 with 32-deep
+// k tiles (128x128).
 #ifndef GEMM_W256N
 #define GEMM_W256N 2
 #endif
@@ -1212,7 +1215,7 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
         if (c.BM == 256 && c.BN == 256) {
             // the GELU epilogue's VALU work runs better with two waves per SIMD
             if constexpr (W256N == 2 && EPI != EPI_BIAS_GELU)
-                return launch_dl4<T, 256, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+                return launch_dl4<T, 256, 256, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
             else
                 return launch_dl<T, 256, 256, 2, 4, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
         }
@@ -1221,9 +1224,13 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
             // per SIMD unless the k loop is long enough to dominate
             if constexpr (EPI != EPI_BIAS_GELU) {
                 if (EPI != EPI_BIAS_DROP_RES || g.K >= 2048)
-                    return launch_dl4<T, 128, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+                    return launch_dl4<T, 256, 128, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
             }
             return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
+        }
+        if constexpr (EPI != EPI_BIAS_GELU) {
+            if (EPI != EPI_BIAS_DROP_RES || g.K >= 2048)
+                return launch_dl4<T, 128, 128, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
         }
         return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
     } else {
