@@ -1081,6 +1081,13 @@ static TileCfg pick_tiles(const GemmDesc& g) {
     for (const TileCfg& c : cands) {
         if (!mfma_ok(g, c.BM, c.BN)) continue;
         const int tiles = (g.M / c.BM) * (g.N / c.BN);
+        if (c.BM == 256 && c.BN == 256 && tiles >= 256 && tiles % 256 != 0 && mfma_ok(g, 256, 128)) {
+            // one workgroup per CU: a partly filled last wave of 256x256
+            // tiles idles CUs; half-width tiles (about 12 % slower per flop)
+            // take over when their whole waves finish clearly sooner
+            const int w256 = (tiles + 255) / 256, w128 = (2 * tiles + 255) / 256;
+            if (w128 * 1.12 < 0.9 * 2 * w256) return {256, 128};
+        }
         if (tiles >= 256 || (c.BM == 128 && c.BN == 128)) return c;
     }
     return {0, 0};
