@@ -56,7 +56,7 @@ __device__ __forceinline__ uint32_t keep_word32(const Rng& r, uint64_t e0, uint3
 // of K and V flow through two LDS buffers, the next block fetched into
 // registers before the MFMAs of the current one (one barrier per block).
 template <typename T>
-__global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnArgs a) {
     constexpr int D = 64, KB = 64, VLD = D + 32;  // V rows 192 B apart: conflict-free transposing reads
     typedef typename MfmaOp<T>::v8 v8;
     __shared__ __align__(16) T Ks[2][KB * D];
@@ -113,48 +113,68 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks[buf], kt * 32, ks, lane), qf[ks], s[kt]);
             }
-            // s[kt][r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
+            // s[kt][r]: raw score q.k of key kb*64 + kt*32 + 8*(r>>2) +
+            // 4*(lane>>5) + (r&3) and query ql; keys at or beyond L only
+            // occur in the last block
+            if (kb * KB + KB > L) {
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = kb * KB + kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                        if (key >= L) s[kt][r] = -INFINITY;
+                    }
+            }
             float mloc = -INFINITY;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kb * KB + kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const float v = key < L ? s[kt][r] * c : -INFINITY;
-                    s[kt][r] = v;
-                    mloc = fmaxf(mloc, v);
-                }
+                for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, s[kt][r]);
             mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-            const float m_new = fmaxf(m_run, mloc);
-            const float alpha = exp2f(m_run - m_new);
-            m_run = m_new;
-            float lsum = 0.0f;
+            // Lazy rescaling: the reference maximum m_run (raw units) moves
+            // only when a block's maximum exceeds it by more than 8 / c, so
+            // the unnormalised probabilities stay <= 2^8 and O and l are
+            // rescaled only on those (rare, after the first block) blocks.
+            // The result is the same softmax up to rounding: l and O share
+            // the reference, and the log-sum-exp is m_run * c + log2(l).
+            if (__any(mloc > m_run + 8.0f / c)) {
+                const float m_new = mloc > m_run + 8.0f / c ? mloc : m_run;
+                const float alpha = __builtin_amdgcn_exp2f((m_run - m_new) * c);  // 0 on the first block
+                m_run = m_new;
+                l_run *= alpha;
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
+            }
+            const float mc = m_run * c;
 #pragma unroll
             for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = exp2f(s[kt][r] - m_new);
+                    const float p = __builtin_amdgcn_exp2f(__fmaf_rn(s[kt][r], c, -mc));
                     s[kt][r] = p;
-                    lsum += p;
+                    l_run += p;
                 }
-            l_run = l_run * alpha + lsum;
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[ct][r] *= alpha;
             if (a.drop.thr) {
 #pragma unroll
                 for (int kt = 0; kt < 2; ++kt) {
-                    // keep bits of keys kb*64 + kt*32 + 0..31
+                    // keep bits of keys kb*64 + kt*32 + 0..31; this lane's
+                    // keys 8g + 4*(lane>>5) + i are bits 8g + i of kbits
                     const uint32_t word = keep_word32(a.drop.rng, rowbase + kb * KB + kt * 32, a.drop.thr, lane);
-#pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const uint32_t kbits = word >> (g * 8 + (lane >> 5) * 4);
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
-                    }
                     if (a.bits && lane < 32) a.bits[(rowbase >> 5) + kb * 2 + kt] = word;
+                    const uint32_t kbits = word >> ((lane >> 5) * 4);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            // all ones if the bit is set, else zero (written
+                            // out: the compiler turns the C form into a
+                            // compare and a select)
+                            uint32_t m;
+                            asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(kbits), "s"(g * 8 + i));
+                            s[kt][g * 4 + i] = __uint_as_float(__float_as_uint(s[kt][g * 4 + i]) & m);
+                        }
                 }
             }
 #pragma unroll
@@ -186,7 +206,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(AttnArgs a) {
                 for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
                 Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
             }
-        if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = m_run + log2f(l);
+        if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = m_run * c + log2f(l);
     }
 }
 
@@ -330,7 +350,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
 // buffers, the next block (and this lane's two keep words of it) fetched into
 // registers before the MFMAs of the current one, one barrier per block.
 template <typename T>
-__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
     constexpr int D = 64, KB = 64;
     typedef typename MfmaOp<T>::v8 v8;
     __shared__ __align__(16) T Ks[2][KB * D];
@@ -539,7 +559,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
                 const uint64_t e0 = (bhbase + qb * QB + wq) * (uint64_t)S + kwi * 32;
                 word = 0;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) word |= keep8(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
+                for (int g = 0; g < 4; ++g) word |= keep8_cmp(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
             }
         }
         bits_s[buf][wq][ww] = word;

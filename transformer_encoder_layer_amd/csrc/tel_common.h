@@ -73,6 +73,17 @@ struct Rng {
     uint32_t site, step;  // counter words 2 and 3
 };
 
+// a ^ b ^ k as one gfx950 three-input logic instruction (truth table 0x96:
+// bit set iff an odd number of inputs are set).  k is read from a scalar
+// register, so it must be wave-uniform -- the Philox key words are (seed,
+// layer id) and their Weyl increments.
+__device__ __forceinline__ uint32_t xor3_uniform(uint32_t a, uint32_t b, uint32_t k) {
+    uint32_t r;
+    asm("v_bitop3_b32 %0, %1, %2, %3 bitop3:0x96" : "=v"(r) : "v"(a), "v"(b), "s"(k));
+    return r;
+}
+
+// k0 and k1 must be wave-uniform (see xor3_uniform).
 __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
                                                uint32_t k0, uint32_t k1) {
 #pragma unroll
@@ -83,8 +94,16 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
         const uint64_t p2 = (uint64_t)0xCD9E8D57u * c2;
         const uint32_t a0 = (uint32_t)p0, b0 = (uint32_t)(p0 >> 32);
         const uint32_t a2 = (uint32_t)p2, b2 = (uint32_t)(p2 >> 32);
-        const uint32_t n0 = b2 ^ c1 ^ k0;
-        const uint32_t n2 = b0 ^ c3 ^ k1;
+        uint32_t n0, n2;
+        if (round == 0) {
+            // counter words 1 and 3 (block high word, step) are often
+            // uniform too: plain xors let their key mix stay scalar
+            n0 = b2 ^ (c1 ^ k0);
+            n2 = b0 ^ (c3 ^ k1);
+        } else {
+            n0 = xor3_uniform(b2, c1, k0);
+            n2 = xor3_uniform(b0, c3, k1);
+        }
         c0 = n0; c1 = a2; c2 = n2; c3 = a0;
         k0 += 0x9E3779B9u;
         k1 += 0xBB67AE85u;
@@ -97,7 +116,29 @@ __device__ __forceinline__ uint4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
 // e uses the 16-bit half (e mod 2) of word (e/2 mod 4) and is kept iff that
 // value >= thr = floor(p * 2^16).
 // Keep bits of the 8 elements of block g: bit j set iff element 8g+j is kept.
+// Per 16-bit half of w: 1 if the half is below thr (element dropped), else
+// 0 -- a saturating packed subtract thr - half (zero iff half >= thr)
+// clamped to 1.  thr2 = thr in both halves, wave-uniform.
+__device__ __forceinline__ uint32_t dropped2(uint32_t w, uint32_t thr2) {
+    uint32_t d, r;
+    asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "s"(thr2), "v"(w));
+    asm("v_pk_min_u16 %0, %1, %2" : "=v"(r) : "v"(d), "s"(0x00010001u));
+    return r;  // bit 0: low half, bit 16: high half
+}
+// Bits 0..7 of the keep mask from the four words' dropped2 results
+// (element 2j at bit 2j of x, element 2j+1 at bit 2j+16).
+__device__ __forceinline__ uint32_t keep_bits8(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3) {
+    const uint32_t x = d0 | (d1 << 2) | (d2 << 4) | (d3 << 6);
+    return ~(x | (x >> 15)) & 0xFFu;
+}
 __device__ __forceinline__ uint32_t keep8(const Rng& r, uint64_t g, uint32_t thr) {
+    const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), r.site, r.step, r.key0, r.key1);
+    const uint32_t t2 = thr * 0x00010001u;
+    return keep_bits8(dropped2(w.x, t2), dropped2(w.y, t2), dropped2(w.z, t2), dropped2(w.w, t2));
+}
+// The same bits as keep8 from per-half compares: more instructions, fewer
+// registers live at once (for kernels at the edge of their register budget).
+__device__ __forceinline__ uint32_t keep8_cmp(const Rng& r, uint64_t g, uint32_t thr) {
     const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), r.site, r.step, r.key0, r.key1);
     const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
     uint32_t k = 0;
@@ -112,8 +153,9 @@ __device__ __forceinline__ uint32_t keep4(const Rng& r, uint64_t q, uint32_t thr
     const uint64_t g = q >> 1;
     const uint4 w = philox4x32_10((uint32_t)g, (uint32_t)(g >> 32), r.site, r.step, r.key0, r.key1);
     const uint32_t a = (q & 1) ? w.z : w.x, b = (q & 1) ? w.w : w.y;
-    return (uint32_t)((a & 0xFFFFu) >= thr) | ((uint32_t)((a >> 16) >= thr) << 1) |
-           ((uint32_t)((b & 0xFFFFu) >= thr) << 2) | ((uint32_t)((b >> 16) >= thr) << 3);
+    const uint32_t t2 = thr * 0x00010001u;
+    const uint32_t x = dropped2(a, t2) | (dropped2(b, t2) << 2);  // a: bits 0, 16; b: bits 2, 18
+    return ~(x | (x >> 15)) & 0xFu;
 }
 
 // Dropout description passed to kernels: thr == 0 means "no dropout".
