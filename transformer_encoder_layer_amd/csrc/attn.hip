@@ -431,23 +431,31 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
                     sc = MfmaOp<T>::mma(frag_kmaj<T>(Ks[buf], kt * 32, ks, lane), qf[ks], sc);
                     dp = MfmaOp<T>::mma(frag_kmaj<T>(Vs[buf], kt * 32, ks, lane), df[ks], dp);
                 }
-                // sc[r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
+                // sc[r]: key kb*64 + kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql;
+                // keys at or beyond L only occur in the last block
+                if (kb * KB + KB > L) {
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (kb * KB + kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) >= L) sc[r] = -INFINITY;
+                }
                 uint32_t word = 0xFFFFFFFFu;
                 if (a.drop.thr)
                     word = stored_bits ? (kt ? w1 : w0)
                                        : keep_word32(a.drop.rng, rowbase + kb * KB + kt * 32, a.drop.thr, lane);
+                const uint32_t kbits = word >> ((lane >> 5) * 4);  // key 8g + 4*(lane>>5) + i -> bit 8g + i
+                const uint32_t scale_bits = __float_as_uint(a.drop.scale);
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int key4 = kb * KB + kt * 32 + g * 8 + (lane >> 5) * 4;
-                    const uint32_t kbits = (word >> (key4 & 31)) & 0xFu;
+                for (int g = 0; g < 4; ++g)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = g * 4 + i;
-                        const float p = exp2f(key4 + i < L ? sc[r] * c - lse2 : -INFINITY);
-                        const float f = ((kbits >> i) & 1u) ? a.drop.scale : 0.0f;
-                        sc[r] = p * (dp[r] * f - Dq);
+                        const float p = __builtin_amdgcn_exp2f(__fmaf_rn(sc[r], c, -lse2));
+                        // dropout factor: 1/(1-p) if kept, else 0
+                        uint32_t m;
+                        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(kbits), "s"(g * 8 + i));
+                        const float f = __uint_as_float(m & scale_bits);
+                        sc[r] = p * __fmaf_rn(dp[r], f, -Dq);
                     }
-                }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     v8 pf;
@@ -493,7 +501,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
     __shared__ __align__(16) T Qs[2][QB * D];
     __shared__ __align__(16) T Os[2][QB * D];
     __shared__ float lse_s[2][QB], D_s[2][QB];
-    __shared__ uint32_t bits_s[2][QB][4];  // keep words of this block's 128 keys for 64 queries
+    __shared__ uint32_t bits_s[2][4][QB];  // keep words [32-key word][query] of this block's 128 keys
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
@@ -562,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
                 for (int g = 0; g < 4; ++g) word |= keep8_cmp(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
             }
         }
-        bits_s[buf][wq][ww] = word;
+        bits_s[buf][ww][wq] = word;
     };
 
     const int nqb = S / QB;
@@ -584,19 +592,28 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
                     sc = MfmaOp<T>::mma(frag_kmaj<T>(Qs[buf], qt * 32, ks, lane), kf[ks], sc);
                     dp = MfmaOp<T>::mma(frag_kmaj<T>(Os[buf], qt * 32, ks, lane), vf[ks], dp);
                 }
-                // sc[r]: query qb*64 + qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl
+                // sc[r]: query qb*64 + qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl.
+                // Keys at or beyond L are not masked here: a lane's P and dS
+                // only reach its own key's rows of dK and dV, which are
+                // written as zero instead.
+                const uint32_t scale_bits = __float_as_uint(a.drop.scale);
 #pragma unroll
                 for (int g = 0; g < 4; ++g) {
                     const int qi0 = qt * 32 + 8 * g + 4 * (lane >> 5);
                     const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[buf][qi0]);
                     const float4 d4 = *reinterpret_cast<const float4*>(&D_s[buf][qi0]);
+                    const uint4 w4 = *reinterpret_cast<const uint4*>(&bits_s[buf][wave][qi0]);
                     const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const int r = g * 4 + i;
-                        const float p = exp2f(kl < L ? sc[r] * c - lv[i] : -INFINITY);
-                        const float f = (bits_s[buf][qi0 + i][wave] >> (kl & 31)) & 1u ? a.drop.scale : 0.0f;
-                        const float dsv = p * (dp[r] * f - dvv[i]);
+                        const float p = __builtin_amdgcn_exp2f(__fmaf_rn(sc[r], c, -lv[i]));
+                        // dropout factor: 1/(1-p) if key kl of this query is kept, else 0
+                        uint32_t m;
+                        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(m) : "v"(wv[i]), "v"(kl & 31));
+                        const float f = __uint_as_float(m & scale_bits);
+                        const float dsv = p * __fmaf_rn(dp[r], f, -dvv[i]);
                         sc[r] = p * f;
                         dp[r] = dsv;
                     }
@@ -631,8 +648,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
                 float vk[4], vv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    vk[i] = dk[ct][g * 4 + i] * 0.125f;
-                    vv[i] = dv[ct][g * 4 + i];
+                    // keys at or beyond L get no gradient
+                    vk[i] = kl < L ? dk[ct][g * 4 + i] * 0.125f : 0.0f;
+                    vv[i] = kl < L ? dv[ct][g * 4 + i] : 0.0f;
                 }
                 const int col = ct * 32 + g * 8 + (lane >> 5) * 4;
                 Vec4<T>::store(outk + col, vk);
