@@ -265,24 +265,26 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
             for (int r = 0; r < 16; ++r) s[kt][r] = 0.0f;
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) s[kt] = MfmaOp<T>::mma(frag_kmaj<T>(Ks, kt * 32, ks, lane), qf[ks], s[kt]);
-            // s[kt][r]: key kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), query ql
+            // s[kt][r]: raw score of key kt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3)
+            // and query ql; only a tile reaching L holds masked keys
+            if (kt * 32 + 32 > L) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int key = kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const float v = key < L ? s[kt][r] * c : -INFINITY;
-                s[kt][r] = v;
-                m = fmaxf(m, v);
+                for (int r = 0; r < 16; ++r)
+                    if (kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) >= L) s[kt][r] = -INFINITY;
             }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m = fmaxf(m, s[kt][r]);
         }
     }
     m = fmaxf(m, __shfl_xor(m, 32, 64));
+    const float mc = m * c;  // row maximum in log2 units
     float l = 0.0f;
 #pragma unroll
     for (int kt = 0; kt < SMAX / 32; ++kt) {
         if (kt * 32 < S) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const float p = exp2f(s[kt][r] - m);
+                const float p = __builtin_amdgcn_exp2f(__fmaf_rn(s[kt][r], c, -mc));
                 s[kt][r] = p;
                 l += p;
             }
@@ -296,13 +298,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
             if (kt * 32 < S) {
                 // keep bits of keys kt*32 + 0..31
                 const uint32_t word = keep_word32(a.drop.rng, rowbase + kt * 32, a.drop.thr, lane);
+                const uint32_t kbits = word >> ((lane >> 5) * 4);  // key 8g + 4*(lane>>5) + i -> bit 8g + i
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const uint32_t kbits = word >> (g * 8 + (lane >> 5) * 4);
+                for (int g = 0; g < 4; ++g)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (!((kbits >> i) & 1u)) s[kt][g * 4 + i] = 0.0f;
-                }
+                    for (int i = 0; i < 4; ++i) {
+                        uint32_t mk;  // all ones if kept, else zero
+                        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(mk) : "v"(kbits), "s"(g * 8 + i));
+                        s[kt][g * 4 + i] = __uint_as_float(__float_as_uint(s[kt][g * 4 + i]) & mk);
+                    }
                 if (a.bits && lane < 32) a.bits[(rowbase >> 5) + kt] = word;
             }
         }
@@ -341,7 +345,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
             for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
             Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
         }
-    if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = m + log2f(l);
+    if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = mc + log2f(l);
 }
 
 // ------------------------------------------------------------------ MFMA bwd: D and dQ
@@ -500,8 +504,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
     typedef typename MfmaOp<T>::v8 v8;
     __shared__ __align__(16) T Qs[2][QB * D];
     __shared__ __align__(16) T Os[2][QB * D];
-    __shared__ float lse_s[2][QB], D_s[2][QB];
-    __shared__ uint32_t bits_s[2][4][QB];  // keep words [32-key word][query] of this block's 128 keys
+    __shared__ __align__(16) float lse_s[2][QB], D_s[2][QB];
+    __shared__ __align__(16) uint32_t bits_s[2][4][QB];  // keep words [32-key word][query] of this block's 128 keys
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int b = blockIdx.z, h = blockIdx.y;
     const int S = a.S, NH = a.NH, B = a.B, H = NH * D;
@@ -678,8 +682,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
     constexpr int D = 64, SMAX = 128;
     typedef typename MfmaOp<T>::v8 v8;
     __shared__ __align__(16) T lds[3 * SMAX * D];  // Q | dO | K; dS [S][S] overlays Q and dO
-    __shared__ float lse_s[SMAX], D_s[SMAX];
-    __shared__ uint32_t bits_s[SMAX][SMAX / 32];
+    __shared__ __align__(16) float lse_s[SMAX], D_s[SMAX];
+    __shared__ __align__(16) uint32_t bits_s[SMAX / 32][SMAX];  // keep words [32-key word][query]
     T* Qs = lds;
     T* dOs = lds + SMAX * D;
     T* Ks = lds + 2 * SMAX * D;
@@ -780,7 +784,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
 #pragma unroll
                     for (int g = 0; g < 4; ++g) word |= keep8(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
                 }
-                bits_s[q][w] = word;
+                bits_s[w][q] = word;
             }
         }
     }
@@ -805,15 +809,30 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
                     sc = MfmaOp<T>::mma(frag_kmaj<T>(Qs, qt * 32, ks, lane), kf[ks], sc);
                     dp = MfmaOp<T>::mma(frag_kmaj<T>(dOs, qt * 32, ks, lane), vf[ks], dp);
                 }
-                // sc[r]: query qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl
+                // sc[r]: query qt*32 + 8*(r>>2) + 4*(lane>>5) + (r&3), key kl.
+                // A key at or beyond L is not masked per element: its dS
+                // operands are zeroed below (phase 2 reads them for dQ) and
+                // its rows of dK and dV are written as zero.
                 f32x16 ds;
+                const uint32_t scale_bits = __float_as_uint(a.drop.scale);
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int qi = qt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                    const float p = exp2f(kl < L ? sc[r] * c - lse_s[qi] : -INFINITY);
-                    const float f = (bits_s[qi][wave] >> (kl & 31)) & 1u ? a.drop.scale : 0.0f;
-                    ds[r] = p * (dp[r] * f - D_s[qi]);
-                    sc[r] = p * f;
+                for (int g = 0; g < 4; ++g) {
+                    const int qi0 = qt * 32 + 8 * g + 4 * (lane >> 5);
+                    const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[qi0]);
+                    const float4 d4 = *reinterpret_cast<const float4*>(&D_s[qi0]);
+                    const uint4 w4 = *reinterpret_cast<const uint4*>(&bits_s[wave][qi0]);
+                    const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, dvv[4] = {d4.x, d4.y, d4.z, d4.w};
+                    const uint32_t wv[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int r = g * 4 + i;
+                        const float p = __builtin_amdgcn_exp2f(__fmaf_rn(sc[r], c, -lv[i]));
+                        uint32_t mk;  // all ones if key kl of this query is kept, else zero
+                        asm("v_bfe_i32 %0, %1, %2, 1" : "=v"(mk) : "v"(wv[i]), "v"(kl & 31));
+                        const float f = __uint_as_float(mk & scale_bits);
+                        ds[r] = p * __fmaf_rn(dp[r], f, -dvv[i]);
+                        sc[r] = p * f;
+                    }
                 }
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
@@ -830,6 +849,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
                     for (int ct = 0; ct < 2; ++ct) {
                         dv[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(dOs, ct * 32, qb0, qb0 + 8, lane), pf, dv[ct]);
                         dk[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Qs, ct * 32, qb0, qb0 + 8, lane), sf, dk[ct]);
+                    }
+                    if (kl >= L) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) sf[e] = from_f<T>(0.0f);
                     }
                     dsf[qt][half] = sf;
                 }
@@ -861,8 +884,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
                 float vk[4], vv[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    vk[i] = dk[ct][g * 4 + i] * 0.125f;
-                    vv[i] = dv[ct][g * 4 + i];
+                    // keys at or beyond L get no gradient
+                    vk[i] = kl < L ? dk[ct][g * 4 + i] * 0.125f : 0.0f;
+                    vv[i] = kl < L ? dv[ct][g * 4 + i] : 0.0f;
                 }
                 const int col = ct * 32 + g * 8 + (lane >> 5) * 4;
                 Vec4<T>::store(outk + col, vk);
