@@ -37,6 +37,15 @@ def model_flops(w) -> float:
     return 3.0 * fwd
 
 
+def valid_flops(w, lengths) -> float:
+    """The same count over valid tokens only (token packing): projections and
+    FFN on sum(len) rows, attention on len_b x len_b scores per sequence."""
+    H, F = w.hidden, w.ffn
+    L = [int(v) for v in lengths]
+    fwd = 2.0 * sum(L) * (4 * H * H + 2 * H * F) + 4.0 * sum(v * v for v in L) * H
+    return 3.0 * fwd
+
+
 class Hip:
     """The few HIP runtime calls the benchmark needs for events."""
 
@@ -128,6 +137,8 @@ def main():
     ap.add_argument("--kernel", default="ffn1_fwd", help="kernel timed for the roofline")
     ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pack", action="store_true",
+                    help="token packing: run the layers on the valid tokens of a padded workload")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of 1 GiB (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -150,14 +161,18 @@ def main():
     dev = torch.device("cuda:0")
     dt = syn.torch_dtype(w.dtype)
     T, H = w.tokens, w.hidden
+    pack = bool(args.pack and w.lengths is not None)
+    valid = int(syn.seq_lengths(w).sum()) if w.lengths is not None else T
 
     # ---- layers (distinct ids, weights from the seeded generator)
     handles, params, grads, saved = [], [], [], []
     for l in range(n_layers):
         cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, float(np.float32(w.attn_p)),
                           float(np.float32(w.hidden_p)), w.pre_ln, w.seed, l, dt, 1e-12,
-                          w.attn_dropout_checkpoint, w.normalize_invertible, w.gelu_checkpoint)
+                          w.attn_dropout_checkpoint, w.normalize_invertible, w.gelu_checkpoint, pack_tokens=pack)
         h = B.tel_layer_create(cfg.to_c())
+        if pack:
+            B.tel_layer_set_valid_tokens(h, valid)
         handles.append(h)
         p64 = syn.layer_params(w, l)
         P = {n: syn.to_storage(p64[n], w.dtype).to(dev) for n in B.PARAM_NAMES}
@@ -229,25 +244,27 @@ def main():
     ms_per_step = total_ms / args.steps
     n_run = len(run)
     layer_tokens_per_s = T * n_run / (ms_per_step / 1e3)
-    tflops = model_flops(w) * n_run / (ms_per_step / 1e3) / 1e12
+    flops = valid_flops(w, syn.seq_lengths(w)) if pack else model_flops(w)
+    tflops = flops * n_run / (ms_per_step / 1e3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
 
     # roofline of the timed kernel (algorithmic work per launch)
     F = w.ffn
-    gemm_flops = {"qkv_fwd": 2.0 * T * H * 3 * H, "out_fwd": 2.0 * T * H * H, "ffn1_fwd": 2.0 * T * H * F,
-                  "ffn2_fwd": 2.0 * T * F * H, "ffn2_dgrad": 2.0 * T * H * F, "ffn2_wgrad": 2.0 * T * H * F,
-                  "ffn1_dgrad": 2.0 * T * F * H, "ffn1_wgrad": 2.0 * T * F * H, "out_dgrad": 2.0 * T * H * H,
-                  "out_wgrad": 2.0 * T * H * H, "qkv_dgrad": 2.0 * T * 3 * H * H, "qkv_wgrad": 2.0 * T * 3 * H * H}
+    Tg = (valid + 255) // 256 * 256 if pack else T  # rows the GEMMs and LayerNorms run on
+    gemm_flops = {"qkv_fwd": 2.0 * Tg * H * 3 * H, "out_fwd": 2.0 * Tg * H * H, "ffn1_fwd": 2.0 * Tg * H * F,
+                  "ffn2_fwd": 2.0 * Tg * F * H, "ffn2_dgrad": 2.0 * Tg * H * F, "ffn2_wgrad": 2.0 * Tg * H * F,
+                  "ffn1_dgrad": 2.0 * Tg * F * H, "ffn1_wgrad": 2.0 * Tg * F * H, "out_dgrad": 2.0 * Tg * H * H,
+                  "out_wgrad": 2.0 * Tg * H * H, "qkv_dgrad": 2.0 * Tg * 3 * H * H, "qkv_wgrad": 2.0 * Tg * 3 * H * H}
     if args.kernel in gemm_flops:
         ach = gemm_flops[args.kernel] / (kern_avg_ms / 1e3) / 1e12
         meas = MEASURED_TRAFFIC.get((args.kernel, w.name))
-        traffic = meas[1] if meas and meas[0] == kernel_sources_digest() else None
+        traffic = meas[1] if meas and meas[0] == kernel_sources_digest() and not pack else None
         roof = {"kernel": args.kernel, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
                 "frac": round(ach / peak, 4), "traffic": traffic, "avg_launch_us": round(kern_avg_ms * 1e3, 2),
                 "launches": len(kern_ms), "algorithmic_per_launch": gemm_flops[args.kernel]}
     else:
         e = 2 if w.dtype != "f32" else 4
-        ln_bytes = {"ln1_fwd": 2 * T * H * e + 8 * T, "ln2_fwd": T * H * (4 + e) + 8 * T}
+        ln_bytes = {"ln1_fwd": 2 * Tg * H * e + 8 * Tg, "ln2_fwd": Tg * H * (4 + e) + 8 * Tg}
         byts = ln_bytes.get(args.kernel, float("nan"))
         ach = byts / (kern_avg_ms / 1e3) / 1e9
         roof = {"kernel": args.kernel, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
@@ -271,13 +288,16 @@ def main():
         "config": {"workload": f"{w.name}: batch {w.batch}, seq {w.seq}, hidden {w.hidden}, heads {w.heads}, "
                                f"ffn {w.ffn}, {'Pre' if w.pre_ln else 'Post'}-LN, {w.dtype}, dropout "
                                f"{w.attn_p}/{w.hidden_p}, {n_layers}-layer stack"
-                               + (f", PLD theta={theta:.5f} keeps {n_run}" if w.pld else ""),
+                               + (f", PLD theta={theta:.5f} keeps {n_run}" if w.pld else "")
+                               + (f", token packing ({valid} valid of {T} tokens)" if pack else ""),
                    "batch": w.batch, "seq_len": w.seq, "hidden": w.hidden, "heads": w.heads, "ffn": w.ffn,
                    "layers": n_layers, "layers_run": n_run, "parallelism": "single GPU"},
         "tflops": round(tflops, 1),
         "pct_mfma_peak": round(100 * tflops / peak, 2),
         "stack_tokens_per_s": round(T / (ms_per_step / 1e3), 1),
         "ms_per_layer_fwd_bwd": round(ms_per_step / n_run, 4),
+        "valid_tokens_per_s": round(valid * n_run / (ms_per_step / 1e3), 1),
+        "token_packing": pack,
         "wall_s_timed": round(wall, 3),
         "roofline": roof,
     }

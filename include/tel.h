@@ -94,6 +94,8 @@ typedef struct {
                                         backward regenerates them from the RNG */
     int32_t normalize_invertible;  /* LN backward from the LN output; drops the LN inputs */
     int32_t gelu_checkpoint;       /* keep the GELU input only; recompute GELU in backward */
+    int32_t pack_tokens;           /* run the layer on the valid tokens only (see
+                                      tel_layer_set_valid_tokens) */
 } tel_config;
 
 /* The twelve parameters, nn.Linear layout, dtype cfg.dtype, device memory:
@@ -143,6 +145,25 @@ tel_status tel_layer_backward(tel_layer* layer, const tel_params* params, const 
                               const int32_t* key_lengths, int training, uint64_t step, const void* dy,
                               const void* saved, void* scratch, void* dx, const tel_grads* grads,
                               tel_stream_t stream);
+
+/* Token packing (pack_tokens = 1): work on padding tokens is skipped, the
+ * cost the AI-infra blog describes for padded batches (sections 2.1 and 4.2,
+ * dynamic padding and length bucketing).  Declares that the next forward
+ * and its backward see key_lengths summing to valid_tokens (0 or B*S: no
+ * packing).  The layer then gathers the valid tokens b*S + s (s < len[b])
+ * into consecutive rows, rounded up to a multiple of 256 with zero filler
+ * rows, and runs LayerNorm, the projections and the FFN on those rows only;
+ * attention keeps its per-sequence layout.  Results at valid tokens are the
+ * unpacked layer's (dropout masks keep their padded element index); y and dx
+ * are zero at padding tokens, and dy there is ignored (the gradient of a
+ * loss that does not read padding outputs).  Requires the MFMA attention
+ * (fp16/bf16, head width 64, S a multiple of 64).  valid_tokens must equal
+ * the sum of the device key_lengths of those calls; it is not checked on the
+ * device (a mismatch gives wrong values, never an out-of-bounds access).
+ * Returns TEL_ERR_INVALID_ARG if valid_tokens is outside [0, B*S], and
+ * TEL_ERR_UNSUPPORTED if the layer was not created with pack_tokens or its
+ * attention cannot run packed. */
+tel_status tel_layer_set_valid_tokens(tel_layer* layer, int64_t valid_tokens);
 
 /* Free the handle.  NULL is accepted. */
 tel_status tel_layer_destroy(tel_layer* layer);

@@ -32,9 +32,10 @@ def prepare(w: syn.Workload, layer=0, random_affine=False, weight_scale=1.0):
 
 
 def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=None, switches=None,
-              device="cuda", backward=True, use_lengths=True):
+              device="cuda", backward=True, use_lengths=True, pack=False):
     """Run forward (+ backward) through the C ABI.  dy_rows: optional boolean
-    mask over sequences; dy is zeroed for the others.  Returns fp64 numpy."""
+    mask over sequences; dy is zeroed for the others.  pack: token packing
+    (the valid-token count is declared from the lengths).  Returns fp64 numpy."""
     import torch
     from transformer_encoder_layer_amd import binding as B
     from transformer_encoder_layer_amd.layer import LayerConfig
@@ -44,7 +45,7 @@ def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=
                       float(np.float32(w.hidden_p)), w.pre_ln, w.seed, layer_id, syn.torch_dtype(w.dtype),
                       1e-12, bool(sw.get("attn_dropout_checkpoint", w.attn_dropout_checkpoint)),
                       bool(sw.get("normalize_invertible", w.normalize_invertible)),
-                      bool(sw.get("gelu_checkpoint", w.gelu_checkpoint)))
+                      bool(sw.get("gelu_checkpoint", w.gelu_checkpoint)), pack_tokens=pack)
     h = B.tel_layer_create(cfg.to_c())
     try:
         saved_b, scratch_b = B.tel_layer_workspace_bytes(h)
@@ -57,6 +58,8 @@ def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=
             dy[torch.from_numpy(~m)] = 0
         dy = dy.to(dev)
         lens = torch.from_numpy(data["lengths"]).to(dev) if (use_lengths and w.lengths is not None) else None
+        if pack:
+            B.tel_layer_set_valid_tokens(h, int(np.asarray(data["lengths"]).sum()))
         y = torch.empty_like(x)
         saved = torch.empty(max(saved_b, 1), dtype=torch.uint8, device=dev)
         scratch = torch.empty(max(scratch_b, 1), dtype=torch.uint8, device=dev)
@@ -139,4 +142,36 @@ def compare(w: syn.Workload, g, o, batches, tol=None, check_grads=True):
         for n in NAMES:
             report[n] = max_abs(g["g_" + n], o["grads"][n])
             assert report[n] <= 1e-5, report
+    return report
+
+
+def zero_padding_grad(w: syn.Workload, data):
+    """Zero dy at padding tokens (s >= len[b]) in both the storage and the
+    fp64 copies: the gradient of a loss that does not read padding outputs."""
+    S = w.seq
+    for b, L in enumerate(np.asarray(data["lengths"])):
+        data["dy_t"][b * S + int(L):(b + 1) * S] = 0
+        data["dy_r"][b * S + int(L):(b + 1) * S] = 0
+
+
+def compare_packed(w: syn.Workload, g, o, batches):
+    """Token packing: y and dx at valid tokens to the usual fp16/bf16
+    tolerances, exactly zero at padding tokens; gradients by relative norm."""
+    S = w.seq
+    lens = np.asarray(syn.seq_lengths(w))
+    report = {}
+    gx, ox = [], []
+    for b in batches:
+        L = int(lens[b])
+        report[f"y[{b}]"] = max_abs(g["y"][b * S:b * S + L], o["y"][b][:L])
+        assert report[f"y[{b}]"] <= 2e-2, report
+        assert not np.any(g["y"][b * S + L:(b + 1) * S]), f"y not zero at padding of sequence {b}"
+        assert not np.any(g["dx"][b * S + L:(b + 1) * S]), f"dx not zero at padding of sequence {b}"
+        gx.append(g["dx"][b * S:b * S + L])
+        ox.append(o["dx"][b][:L])
+    report["dx"] = rel_norm(np.concatenate(gx), np.concatenate(ox))
+    assert report["dx"] <= 5e-2, report
+    for n in NAMES:
+        report[n] = rel_norm(g["g_" + n], o["grads"][n])
+        assert report[n] <= 5e-2, report
     return report

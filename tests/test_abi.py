@@ -38,7 +38,7 @@ def test_library_exports_every_symbol():
 def cfg(**kw):
     base = dict(batch=2, seq=16, hidden=64, heads=4, ffn=256, attn_dropout=0.0, hidden_dropout=0.0, pre_ln=1,
                 seed=1234, layer_id=0, dtype=B.TEL_F32, ln_eps=1e-12, attn_dropout_checkpoint=0,
-                normalize_invertible=0, gelu_checkpoint=0)
+                normalize_invertible=0, gelu_checkpoint=0, pack_tokens=0)
     base.update(kw)
     return B.tel_config(*[base[f] for f, _ in B.tel_config._fields_])
 
@@ -56,12 +56,37 @@ def cfg(**kw):
     (dict(dtype=7), B.TEL_ERR_INVALID_ARG),
     (dict(ln_eps=-1.0), B.TEL_ERR_INVALID_ARG),
     (dict(ffn=24), B.TEL_ERR_INVALID_ARG),
+    (dict(pack_tokens=1), B.TEL_ERR_UNSUPPORTED),   # fp32 / d = 16: no packed attention
+    (dict(pack_tokens=1, dtype=B.TEL_F16, hidden=256, heads=4, seq=96), B.TEL_ERR_UNSUPPORTED),  # S % 64
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(B.TelError) as e:
         B.tel_layer_create(cfg(**kw))
     assert e.value.status == status
     assert B.tel_last_error()
+
+
+def test_set_valid_tokens():
+    h = B.tel_layer_create(cfg(pack_tokens=1, dtype=B.TEL_F16, hidden=256, heads=4, seq=64, batch=4))
+    try:
+        B.tel_layer_set_valid_tokens(h, 100)
+        B.tel_layer_set_valid_tokens(h, 0)
+        B.tel_layer_set_valid_tokens(h, 256)
+        for bad in (-1, 257):
+            with pytest.raises(B.TelError) as e:
+                B.tel_layer_set_valid_tokens(h, bad)
+            assert e.value.status == B.TEL_ERR_INVALID_ARG
+        # packing adds the row maps and the packed input to the saved workspace
+        plain = B.tel_layer_create(cfg(dtype=B.TEL_F16, hidden=256, heads=4, seq=64, batch=4))
+        try:
+            assert B.tel_layer_workspace_bytes(h)[0] > B.tel_layer_workspace_bytes(plain)[0]
+            with pytest.raises(B.TelError) as e:
+                B.tel_layer_set_valid_tokens(plain, 100)
+            assert e.value.status == B.TEL_ERR_UNSUPPORTED
+        finally:
+            B.tel_layer_destroy(plain)
+    finally:
+        B.tel_layer_destroy(h)
 
 
 def test_create_null_args():

@@ -10,7 +10,7 @@ import numpy as np
 import pytest
 
 import oracle
-from _harness import NAMES, compare, gpu_layer, oracle_layer, prepare
+from _harness import NAMES, compare, compare_packed, gpu_layer, oracle_layer, prepare, zero_padding_grad
 from transformer_encoder_layer_amd import synthetic as syn
 
 pytestmark = pytest.mark.gpu
@@ -149,6 +149,42 @@ def test_inference_forward_no_saved():
                                  B.make_grads(P))
     finally:
         B.tel_layer_destroy(h)
+
+
+# ------------------------------------------------------------------ token packing
+def _run_packed(w, batches=None, dy_rows=None, step=0, layer_id=0, random_affine=True):
+    data = prepare(w, layer=layer_id, random_affine=random_affine)
+    zero_padding_grad(w, data)
+    valid = int(np.asarray(data["lengths"]).sum())
+    assert (valid + 255) // 256 * 256 < w.batch * w.seq, "case must leave padding for packing to remove"
+    g = gpu_layer(w, data, step=step, layer_id=layer_id, dy_rows=dy_rows, pack=True)
+    o = oracle_layer(w, data, step=step, layer_id=layer_id, batches=batches, dy_rows=dy_rows)
+    bs = list(range(w.batch)) if batches is None else batches
+    rep = compare_packed(w, g, o, bs)
+    print(w.name, "packed", {k: f"{v:.3g}" for k, v in rep.items()})
+
+
+@pytest.mark.parametrize("dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_packed_tokens_short_seq(dtype, pre_ln):
+    # S = 128 (whole-sequence attention kernels); sum of lengths leaves >= 256 rows to skip
+    w = syn.Workload("packed128", 8, 128, 256, 4, 1024, pre_ln, dtype, 0.1, 0.1, 21, lengths=(9, 100))
+    _run_packed(w, step=4, layer_id=3)
+
+
+@pytest.mark.parametrize("pre_ln", [True, False])
+def test_packed_tokens_streaming(pre_ln):
+    # S = 256 (streaming attention kernels, partial key blocks)
+    w = syn.Workload("packed256", 4, 256, 256, 4, 1024, pre_ln, "bf16", 0.1, 0.1, 23, lengths=(30, 150))
+    _run_packed(w, step=2, layer_id=1)
+
+
+def test_packed_tokens_bert_base_postln():
+    # the padded Post-LN workload at full size, two sequences checked
+    w = syn.WORKLOADS["bert_base_postln"]
+    rows = np.zeros(w.batch, dtype=bool)
+    rows[[0, 31]] = True
+    _run_packed(w, batches=[0, 31], dy_rows=rows, random_affine=False)
 
 
 # ------------------------------------------------------------------ full-size workloads, sampled

@@ -24,7 +24,8 @@ PARAM_NAMES = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
 
 # every symbol declared in include/tel.h
 EXPORTS = ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward", "tel_layer_backward",
-           "tel_layer_destroy", "tel_last_error", "tel_debug_dropout_mask", "tel_debug_kernel_events",
+           "tel_layer_set_valid_tokens", "tel_layer_destroy", "tel_last_error", "tel_debug_dropout_mask",
+           "tel_debug_kernel_events",
            "tel_pld_theta", "tel_pld_keep")
 
 # kernel ids (TEL_K_*) of include/tel.h
@@ -46,7 +47,7 @@ class tel_config(ctypes.Structure):
                 ("pre_ln", ctypes.c_int32), ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float),
                 ("attn_dropout_checkpoint", ctypes.c_int32), ("normalize_invertible", ctypes.c_int32),
-                ("gelu_checkpoint", ctypes.c_int32)]
+                ("gelu_checkpoint", ctypes.c_int32), ("pack_tokens", ctypes.c_int32)]
 
 
 class tel_params(ctypes.Structure):
@@ -74,6 +75,7 @@ def lib():
         L.tel_layer_forward.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp, vp, vp]
         L.tel_layer_backward.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp, vp,
                                          vp, ctypes.POINTER(tel_grads), vp]
+        L.tel_layer_set_valid_tokens.argtypes = [vp, ctypes.c_int64]
         L.tel_layer_destroy.argtypes = [vp]
         L.tel_last_error.argtypes = []
         L.tel_last_error.restype = ctypes.c_char_p
@@ -85,8 +87,8 @@ def lib():
         L.tel_pld_keep.argtypes = [u64, i32, u64, ctypes.c_double]
         L.tel_pld_keep.restype = i32
         for name in ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward",
-                     "tel_layer_backward", "tel_layer_destroy", "tel_debug_dropout_mask",
-                     "tel_debug_kernel_events"):
+                     "tel_layer_backward", "tel_layer_set_valid_tokens", "tel_layer_destroy",
+                     "tel_debug_dropout_mask", "tel_debug_kernel_events"):
             getattr(L, name).restype = ctypes.c_int
         _lib = L
     return _lib
@@ -133,6 +135,10 @@ def tel_layer_workspace_bytes(handle: int):
     s, c = ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib().tel_layer_workspace_bytes(handle, ctypes.byref(s), ctypes.byref(c)))
     return s.value, c.value
+
+
+def tel_layer_set_valid_tokens(handle: int, valid_tokens: int):
+    _check(lib().tel_layer_set_valid_tokens(handle, int(valid_tokens)))
 
 
 def tel_layer_forward(handle, params: tel_params, x, key_lengths, training, step, y, saved, scratch, stream=None):

@@ -22,6 +22,10 @@ struct AttnArgs {
     const void* dout;   // [B][NH][S][d] gradient of ctx, head-split
     float* dvec;        // [B][NH][S] rowsum(dO * O) (written by the dq kernel)
     void* dqkv;         // [B*S][3H] token-major gradient of the fused projection
+    // Packed rows (optional): the rows of ctx and dqkv are packed[b*S + s]
+    // instead of b*S + s, and tokens with packed < 0 (padding) are neither
+    // written nor read.  MFMA kernels only.
+    const int32_t* packed;
 };
 
 hipError_t attn_forward(const AttnArgs& a, hipStream_t st, bool force_simt = false);

@@ -51,6 +51,9 @@ __device__ __forceinline__ uint32_t keep_word32(const Rng& r, uint64_t e0, uint3
     return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
 }
 
+// Row of token t in ctx / dqkv: t itself, or its packed row (-1: padding).
+__device__ __forceinline__ int out_row(const AttnArgs& a, int t) { return a.packed ? a.packed[t] : t; }
+
 // ------------------------------------------------------------------ MFMA fwd
 // One workgroup = 4 waves x 32 queries of one (batch, head); 64-key blocks
 // of K and V flow through two LDS buffers, the next block fetched into
@@ -196,16 +199,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_mfma(AttnArgs a) {
     if (active) {
         const float l = l_run + __shfl_xor(l_run, 32, 64);
         const float inv = a.drop.scale / l;
-        T* out = (T*)a.ctx + (size_t)(b * S + ql) * (NH * D) + h * D;
+        const int orow = out_row(a, b * S + ql);
+        T* out = (T*)a.ctx + (size_t)max(orow, 0) * (NH * D) + h * D;
+        if (orow >= 0) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
-                Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
-            }
+                    for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
+                    Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+                }
+        }
         if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = m_run * c + log2f(l);
     }
 }
@@ -335,16 +341,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_short_mfma(AttnArgs a) {
         }
     }
     const float inv = a.drop.scale / l;
-    T* out = (T*)a.ctx + (size_t)(b * S + ql) * (NH * D) + h * D;
+    const int orow = out_row(a, b * S + ql);
+    T* out = (T*)a.ctx + (size_t)max(orow, 0) * (NH * D) + h * D;
+    if (orow >= 0) {
 #pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
+        for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            float v[4];
+            for (int g = 0; g < 4; ++g) {
+                float v[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
-            Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
-        }
+                for (int i = 0; i < 4; ++i) v[i] = o[ct][g * 4 + i] * inv;
+                Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+            }
+    }
     if (lane < 32) a.lse[(size_t)(b * NH + h) * S + ql] = mc + log2f(l);
 }
 
@@ -378,7 +387,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
     v8 qf[4], df[4];
     float Dq, lse2;
     {
-        const T* O = (const T*)a.ctx + (size_t)(b * S + qlc) * H + h * D;
+        const int orow = out_row(a, b * S + qlc);  // padding (packed rows): dO is zero there
+        const T* O = (const T*)a.ctx + (size_t)max(orow, 0) * H + h * D;
         float part = 0.0f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -476,8 +486,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
             }
         }
     }
-    if (active) {
-        T* out = (T*)a.dqkv + (size_t)(b * S + ql) * (3 * H) + h * D;
+    const int drow = out_row(a, b * S + qlc);
+    if (active && drow >= 0) {
+        T* out = (T*)a.dqkv + (size_t)drow * (3 * H) + h * D;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -642,8 +653,9 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
             }
         }
     }
-    if (active) {
-        T* outk = (T*)a.dqkv + (size_t)(b * S + kl) * (3 * H) + H + h * D;
+    const int krow = active ? out_row(a, b * S + kl) : -1;
+    if (krow >= 0) {
+        T* outk = (T*)a.dqkv + (size_t)krow * (3 * H) + H + h * D;
         T* outv = outk + H;
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
@@ -719,7 +731,7 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
     const int dq_q = dq_row < S ? dq_row : 0;
     v8 ov[4], dv8[4];
     {
-        const T* orow = (const T*)a.ctx + (size_t)(b * S + dq_q) * H + h * D + dq_half * 32;
+        const T* orow = (const T*)a.ctx + (size_t)max(out_row(a, b * S + dq_q), 0) * H + h * D + dq_half * 32;
         const T* drow = dO + (size_t)dq_q * D + dq_half * 32;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
@@ -875,23 +887,26 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
                     }
             }
         }
-        T* outk = (T*)a.dqkv + (size_t)(b * S + kl) * (3 * H) + H + h * D;
+        const int krow = out_row(a, b * S + kl);
+        T* outk = (T*)a.dqkv + (size_t)max(krow, 0) * (3 * H) + H + h * D;
         T* outv = outk + H;
+        if (krow >= 0) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float vk[4], vv[4];
+                for (int g = 0; g < 4; ++g) {
+                    float vk[4], vv[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // keys at or beyond L get no gradient
-                    vk[i] = kl < L ? dk[ct][g * 4 + i] * 0.125f : 0.0f;
-                    vv[i] = kl < L ? dv[ct][g * 4 + i] : 0.0f;
+                    for (int i = 0; i < 4; ++i) {
+                        // keys at or beyond L get no gradient
+                        vk[i] = kl < L ? dk[ct][g * 4 + i] * 0.125f : 0.0f;
+                        vv[i] = kl < L ? dv[ct][g * 4 + i] : 0.0f;
+                    }
+                    const int col = ct * 32 + g * 8 + (lane >> 5) * 4;
+                    Vec4<T>::store(outk + col, vk);
+                    Vec4<T>::store(outv + col, vv);
                 }
-                const int col = ct * 32 + g * 8 + (lane >> 5) * 4;
-                Vec4<T>::store(outk + col, vk);
-                Vec4<T>::store(outv + col, vv);
-            }
+        }
     }
     __syncthreads();
 
@@ -910,16 +925,19 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_short_mfma(AttnArgs a) {
             for (int ct = 0; ct < 2; ++ct)
                 dq[ct] = MfmaOp<T>::mma(frag_tr_kmaj<T>(Ks, ct * 32, r0, r0 + 4, lane), bf, dq[ct]);
         }
-        T* out = (T*)a.dqkv + (size_t)(b * S + q) * (3 * H) + h * D;
+        const int qrow = out_row(a, b * S + q);
+        T* out = (T*)a.dqkv + (size_t)max(qrow, 0) * (3 * H) + h * D;
+        if (qrow >= 0) {
 #pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
+            for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                float v[4];
+                for (int g = 0; g < 4; ++g) {
+                    float v[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = dq[ct][g * 4 + i] * 0.125f;
-                Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
-            }
+                    for (int i = 0; i < 4; ++i) v[i] = dq[ct][g * 4 + i] * 0.125f;
+                    Vec4<T>::store(out + ct * 32 + g * 8 + (lane >> 5) * 4, v);
+                }
+        }
     }
 }
 
@@ -1095,6 +1113,7 @@ static hipError_t fwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
             return hipGetLastError();
         }
     }
+    if (a.packed) return hipErrorInvalidValue;  // packed rows: MFMA kernels only
     switch (a.d) {
         case 16: return simt_fwd<T, 16>(a, st);
         case 32: return simt_fwd<T, 32>(a, st);
@@ -1120,6 +1139,7 @@ static hipError_t bwd_t(const AttnArgs& a, hipStream_t st, bool force_simt) {
             return hipGetLastError();
         }
     }
+    if (a.packed) return hipErrorInvalidValue;  // packed rows: MFMA kernels only
     switch (a.d) {
         case 16: return simt_bwd<T, 16>(a, st);
         case 32: return simt_bwd<T, 32>(a, st);

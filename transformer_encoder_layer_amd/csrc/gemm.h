@@ -36,6 +36,11 @@ struct EpiArgs {
     const void* aux = nullptr;
     int B = 0, S = 0, H = 0, NH = 0, d = 0;  // head-split geometry
     Drop drop{};                              // thr == 0: no dropout
+    // Packed rows: row m of the GEMM holds token row_map[m] (b*S + s) of the
+    // padded batch, or no token (-1, a filler row).  The head-split scatters
+    // place a row at its token (filler rows are not stored) and the dropout
+    // element index uses the token, so masks match the padded layout.
+    const int32_t* row_map = nullptr;
 };
 
 struct GemmDesc {

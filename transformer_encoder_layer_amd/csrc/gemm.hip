@@ -89,15 +89,18 @@ struct Epi {
         } else if constexpr (EPI == EPI_QKV) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] += b[i];
+            const int t = e.row_map ? e.row_map[m] : m;
+            if (t < 0) return;
             const int which = n / e.H, rem = n - which * e.H, h = rem / e.d, c = rem - h * e.d;
-            const int bb = m / e.S, s = m - bb * e.S;
+            const int bb = t / e.S, s = t - bb * e.S;
             const size_t o = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
         } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] += b[i];
             if (e.drop.thr) {
-                const uint64_t el = (uint64_t)m * e.ldo + n;  // token * H + column, n % 4 == 0
+                const int t = e.row_map ? max(e.row_map[m], 0) : m;
+                const uint64_t el = (uint64_t)t * e.ldo + n;  // token * H + column, n % 4 == 0
                 const uint32_t k = keep4(e.drop.rng, el >> 2, e.drop.thr);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * e.drop.scale : 0.0f;
@@ -131,7 +134,9 @@ struct Epi {
             for (int i = 0; i < 4; ++i) v[i] *= r[i];
             Vec4<T>::store((T*)e.out + off, v);
         } else if constexpr (EPI == EPI_HEADSPLIT) {
-            const int bb = m / e.S, s = m - bb * e.S, h = n / e.d, c = n - h * e.d;
+            const int t = e.row_map ? e.row_map[m] : m;
+            if (t < 0) return;
+            const int bb = t / e.S, s = t - bb * e.S, h = n / e.d, c = n - h * e.d;
             const size_t o = (((size_t)bb * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
         } else if constexpr (EPI == EPI_ADD_RES) {

@@ -33,6 +33,7 @@ struct LnBwdArgs {
     void* out; int out_f32;         // input gradient
     void* drop_out;                 // optional dtype copy of drop(out) (site given by drop)
     Drop drop;
+    const int32_t* row_map;         // optional: token of each row (packed rows) for the dropout index
     float* part_g; float* part_b;   // [gridDim.x][H] partial sums of dgamma, dbeta
 };
 
@@ -51,7 +52,25 @@ int colsum_parts(int rows);
 hipError_t colsum_partial(int dtype, const void* in, int rows, int N, float* part, hipStream_t st);
 
 // out = drop(in) elementwise over n elements (index = element id), dtype.
-hipError_t dropout_apply(int dtype, const void* in, void* out, size_t n, const Drop& d, hipStream_t st);
+// With row_map (packed rows of width H, H % 8 == 0) the element id of row r,
+// column c is row_map[r] * H + c (filler rows, row_map < 0, use token 0).
+hipError_t dropout_apply(int dtype, const void* in, void* out, size_t n, const Drop& d, hipStream_t st,
+                         const int32_t* row_map = nullptr, int H = 0);
+
+// ---- token packing (rows of sequences shorter than S dropped)
+// Packed row p of a batch with lengths len[B] holds token
+// t = b*S + s (s < len[b]) in order of t; rows sum(len) .. P-1 are fillers.
+// map[p] = t or -1 (filler); inv[t] = p or -1 (padding token).
+hipError_t build_row_maps(const int32_t* len, int B, int S, int P, int32_t* map, int32_t* inv, hipStream_t st);
+// dst[p] = src[map[p]] (zero for fillers), rows of H elements of dtype.
+hipError_t gather_rows(int dtype, const void* src, void* dst, const int32_t* map, int P, int H, hipStream_t st);
+// dst[t] = src[inv[t]] (zero for padding tokens), T = B*S rows of H elements.
+hipError_t scatter_rows(int dtype, const void* src, void* dst, const int32_t* inv, int T, int H, hipStream_t st);
+// Zero the rows s >= len[b] of a head-split tensor [G][B][NH][S][d] (dtype).
+hipError_t zero_padded_heads(int dtype, void* buf, int G, int B, int NH, int S, int d, const int32_t* len,
+                             hipStream_t st);
+// Zero rows r0 .. r1-1 of a [rows][W] dtype matrix.
+hipError_t zero_rows(int dtype, void* buf, int r0, int r1, int W, hipStream_t st);
 // keep bits of n elements (n % 4 == 0) of one site, as uint8.
 hipError_t dropout_mask_dump(const Drop& d, uint8_t* out, size_t n, hipStream_t st);
 

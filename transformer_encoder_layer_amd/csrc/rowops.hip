@@ -10,6 +10,7 @@
 // adds and the next dropout are fused in.  dgamma/dbeta are reduced
 // deterministically: per-block partial rows, then a fixed-order column sum.
 #include "rowops.h"
+#include <type_traits>
 
 namespace tel {
 
@@ -191,7 +192,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
                 store4k<T, OUT_F32>(a.out, base + idx, dx);
                 if constexpr (DROP) {
                     if (a.drop.thr) {
-                        const uint32_t k = keep4(a.drop.rng, (base + idx) >> 2, a.drop.thr);
+                        const size_t tok = a.row_map ? (size_t)max(a.row_map[row], 0) : (size_t)row;
+                        const uint32_t k = keep4(a.drop.rng, (tok * H + idx) >> 2, a.drop.thr);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dx[i] = ((k >> i) & 1u) ? dx[i] * a.drop.scale : 0.0f;
                     }
@@ -266,7 +268,8 @@ __global__ __launch_bounds__(256) void colsum_partial_kernel(const T* in, int ro
 
 // Elementwise dropout, 8 elements (one Philox block) per thread; n % 4 == 0.
 template <typename T>
-__global__ __launch_bounds__(256) void dropout_apply_kernel(const T* in, T* out, size_t n, Drop d) {
+__global__ __launch_bounds__(256) void dropout_apply_kernel(const T* in, T* out, size_t n, Drop d,
+                                                            const int32_t* row_map, int H) {
     const size_t i8 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
     if (i8 >= n) return;
     const bool two = i8 + 4 < n;
@@ -274,7 +277,12 @@ __global__ __launch_bounds__(256) void dropout_apply_kernel(const T* in, T* out,
     Vec4<T>::load(in + i8, v);
     if (two) Vec4<T>::load(in + i8 + 4, v + 4);
     if (d.thr) {
-        const uint32_t k = keep8(d.rng, i8 >> 3, d.thr);
+        size_t e = i8;  // element id of the first of the 8 (a multiple of 8)
+        if (row_map) {
+            const size_t r = i8 / H;
+            e = (size_t)max(row_map[r], 0) * H + (i8 - r * H);
+        }
+        const uint32_t k = keep8(d.rng, e >> 3, d.thr);
 #pragma unroll
         for (int i = 0; i < 8; ++i) v[i] = ((k >> i) & 1u) ? v[i] * d.scale : 0.0f;
     }
@@ -402,15 +410,128 @@ hipError_t colsum_partial(int dtype, const void* in, int rows, int N, float* par
     return hipGetLastError();
 }
 
-hipError_t dropout_apply(int dtype, const void* in, void* out, size_t n, const Drop& d, hipStream_t st) {
+hipError_t dropout_apply(int dtype, const void* in, void* out, size_t n, const Drop& d, hipStream_t st,
+                         const int32_t* row_map, int H) {
+    if (row_map && (H <= 0 || H % 8 || n % H)) return hipErrorInvalidValue;
     dim3 grid((unsigned)(((n + 7) / 8 + 255) / 256));
     switch (dtype) {
-        case 0: hipLaunchKernelGGL(dropout_apply_kernel<float>, grid, dim3(256), 0, st, (const float*)in, (float*)out, n, d); break;
-        case 1: hipLaunchKernelGGL(dropout_apply_kernel<f16>, grid, dim3(256), 0, st, (const f16*)in, (f16*)out, n, d); break;
-        case 2: hipLaunchKernelGGL(dropout_apply_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)in, (bf16*)out, n, d); break;
+        case 0: hipLaunchKernelGGL(dropout_apply_kernel<float>, grid, dim3(256), 0, st, (const float*)in, (float*)out, n, d, row_map, H); break;
+        case 1: hipLaunchKernelGGL(dropout_apply_kernel<f16>, grid, dim3(256), 0, st, (const f16*)in, (f16*)out, n, d, row_map, H); break;
+        case 2: hipLaunchKernelGGL(dropout_apply_kernel<bf16>, grid, dim3(256), 0, st, (const bf16*)in, (bf16*)out, n, d, row_map, H); break;
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();
+}
+
+// ------------------------------------------------------------------ token packing
+// One thread per token t (and per filler row): the packed row of t is the
+// number of valid tokens of the sequences before b plus s.  B is small, so
+// each thread sums the lengths it needs directly.
+__global__ __launch_bounds__(256) void build_row_maps_kernel(const int32_t* len, int B, int S, int P, int32_t* map,
+                                                             int32_t* inv) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    const int T = B * S;
+    if (i < T) {
+        const int b = i / S, s = i - b * S;
+        int off = 0;
+        for (int j = 0; j < b; ++j) off += min(max(len[j], 0), S);
+        const int p = off + s;
+        const bool valid = s < min(max(len[b], 0), S) && p < P;
+        inv[i] = valid ? p : -1;
+        if (valid) map[p] = i;
+    }
+    if (i < P) {
+        int total = 0;
+        for (int j = 0; j < B; ++j) total += min(max(len[j], 0), S);
+        if (i >= total) map[i] = -1;
+    }
+}
+
+// 8 elements (16 bytes for 16-bit types) per thread; W % 8 == 0.
+template <typename T>
+__global__ __launch_bounds__(256) void move_rows_kernel(const T* src, T* dst, const int32_t* idx, int rows, int W) {
+    const size_t i8 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    if (i8 >= (size_t)rows * W) return;
+    const int r = (int)(i8 / W), c = (int)(i8 - (size_t)r * W);
+    const int from = idx ? idx[r] : -1;
+    float v[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (from >= 0) {
+        Vec4<T>::load(src + (size_t)from * W + c, v);
+        Vec4<T>::load(src + (size_t)from * W + c + 4, v + 4);
+    }
+    Vec4<T>::store(dst + i8, v);
+    Vec4<T>::store(dst + i8 + 4, v + 4);
+}
+
+// Rows s >= len[b] of [G][B][NH][S][d]: one thread per 8 elements.
+template <typename T>
+__global__ __launch_bounds__(256) void zero_padded_heads_kernel(T* buf, int G, int B, int NH, int S, int d,
+                                                                const int32_t* len) {
+    const size_t i8 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 8;
+    const size_t n = (size_t)G * B * NH * S * d;
+    if (i8 >= n) return;
+    const size_t row = i8 / d;
+    const int s = (int)(row % S);
+    const int b = (int)((row / S / NH) % B);
+    if (s < len[b]) return;
+    const float z[4] = {0, 0, 0, 0};
+    Vec4<T>::store(buf + i8, z);
+    Vec4<T>::store(buf + i8 + 4, z);
+}
+
+template <typename F>
+static hipError_t by_dtype(int dtype, F&& f) {
+    switch (dtype) {
+        case 0: return f((float*)nullptr);
+        case 1: return f((f16*)nullptr);
+        case 2: return f((bf16*)nullptr);
+    }
+    return hipErrorInvalidValue;
+}
+
+hipError_t build_row_maps(const int32_t* len, int B, int S, int P, int32_t* map, int32_t* inv, hipStream_t st) {
+    const int n = B * S > P ? B * S : P;
+    hipLaunchKernelGGL(build_row_maps_kernel, dim3((n + 255) / 256), dim3(256), 0, st, len, B, S, P, map, inv);
+    return hipGetLastError();
+}
+
+hipError_t gather_rows(int dtype, const void* src, void* dst, const int32_t* map, int P, int H, hipStream_t st) {
+    if (H % 8) return hipErrorInvalidValue;
+    const size_t n8 = (size_t)P * H / 8;
+    return by_dtype(dtype, [&](auto* tp) {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        hipLaunchKernelGGL(move_rows_kernel<T>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                           (const T*)src, (T*)dst, map, P, H);
+        return hipGetLastError();
+    });
+}
+
+hipError_t scatter_rows(int dtype, const void* src, void* dst, const int32_t* inv, int T, int H, hipStream_t st) {
+    return gather_rows(dtype, src, dst, inv, T, H, st);  // the same move with the inverse map
+}
+
+hipError_t zero_rows(int dtype, void* buf, int r0, int r1, int W, hipStream_t st) {
+    if (r1 <= r0) return hipSuccess;
+    if (W % 8) return hipErrorInvalidValue;
+    const size_t n8 = (size_t)(r1 - r0) * W / 8;
+    return by_dtype(dtype, [&](auto* tp) {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        hipLaunchKernelGGL(move_rows_kernel<T>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                           (const T*)nullptr, (T*)buf + (size_t)r0 * W, (const int32_t*)nullptr, r1 - r0, W);
+        return hipGetLastError();
+    });
+}
+
+hipError_t zero_padded_heads(int dtype, void* buf, int G, int B, int NH, int S, int d, const int32_t* len,
+                             hipStream_t st) {
+    if (d % 8) return hipErrorInvalidValue;
+    const size_t n8 = (size_t)G * B * NH * S * d / 8;
+    return by_dtype(dtype, [&](auto* tp) {
+        using T = std::remove_pointer_t<decltype(tp)>;
+        hipLaunchKernelGGL(zero_padded_heads_kernel<T>, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                           (T*)buf, G, B, NH, S, d, len);
+        return hipGetLastError();
+    });
 }
 
 hipError_t dropout_mask_dump(const Drop& d, uint8_t* out, size_t n, hipStream_t st) {

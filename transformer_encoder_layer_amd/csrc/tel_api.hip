@@ -67,6 +67,8 @@ struct Plan {
     // scratch (backward)
     Buf df, du, dgemm, dres, dz, dout, dvec, dqkv, dres2;
     Buf part_ln, part_col, splitk;
+    // token packing: row maps and x packed (saved); y, dy, dx packed (scratch)
+    Buf rmap, rinv, xp, yp, dyp, dxp;
     size_t saved_bytes = 0, scratch_bytes = 0;
 };
 
@@ -81,6 +83,7 @@ struct tel_layer {
     size_t esz;
     Plan plan;
     long pending_fwd;  // forwards with saved state not yet consumed by a backward
+    long valid_tokens = 0;  // token packing: sum of the key lengths (0: not packed)
     // optional benchmark hook: events recorded around one kernel's launches
     int prof_kernel = -1;
     hipEvent_t* prof_start = nullptr;
@@ -123,6 +126,12 @@ static void make_plan(tel_layer* L) {
                            L->d == 64 && L->S % 64 == 0 && L->cfg.dtype != TEL_F32;
     size_t sv = 0, sc = 0;
     if (keep_bits) place(p.abits, BNS * (size_t)(L->S / 32) * 4, true, sv, sc);
+    if (L->cfg.pack_tokens) {
+        place(p.rmap, T * 4, true, sv, sc);
+        place(p.rinv, T * 4, true, sv, sc);
+        place(p.xp, T * H * e, true, sv, sc);
+        place(p.yp, T * H * e, false, sv, sc);
+    }
     if (L->cfg.pre_ln) {
         place(p.ln1_out, T * H * e, true, sv, sc);
         place(p.mu1, T * f4, true, sv, sc);
@@ -164,6 +173,10 @@ static void make_plan(tel_layer* L) {
     place(p.dout, T * H * e, false, sv, sc);
     place(p.dvec, BNS * f4, false, sv, sc);
     place(p.dqkv, 3 * T * H * e, false, sv, sc);
+    if (L->cfg.pack_tokens) {
+        place(p.dyp, T * H * e, false, sv, sc);
+        place(p.dxp, T * H * e, false, sv, sc);
+    }
     const size_t maxN = 3 * H > F ? 3 * H : F;
     place(p.part_ln, 2 * (size_t)ln_backward_parts(L->T) * H * f4, false, sv, sc);
     place(p.part_col, (size_t)colsum_parts(L->T) * maxN * f4, false, sv, sc);
@@ -201,6 +214,8 @@ static tel_status validate_cfg(const tel_config* c) {
     if (c->dtype != TEL_F32 && c->dtype != TEL_F16 && c->dtype != TEL_BF16)
         return fail(TEL_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
     if (!(c->ln_eps >= 0.0f)) return fail(TEL_ERR_INVALID_ARG, "ln_eps must be >= 0");
+    if (c->pack_tokens && (c->dtype == TEL_F32 || d != 64 || c->seq % 64))
+        return fail(TEL_ERR_UNSUPPORTED, "pack_tokens needs fp16/bf16, head width 64 and seq a multiple of 64");
     const double T = (double)c->batch * c->seq;
     if (T * (double)(3 * c->hidden > F ? 3 * c->hidden : F) >= 2147483647.0 ||
         (double)c->batch * c->heads * c->seq * (double)c->seq >= 9.0e18)
@@ -258,6 +273,16 @@ tel_status tel_layer_workspace_bytes(const tel_layer* L, size_t* saved_bytes, si
     return TEL_OK;
 }
 
+tel_status tel_layer_set_valid_tokens(tel_layer* L, int64_t valid_tokens) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    if (!L->cfg.pack_tokens) return fail(TEL_ERR_UNSUPPORTED, "layer was created without pack_tokens");
+    if (valid_tokens < 0 || valid_tokens > (int64_t)L->T)
+        return fail(TEL_ERR_INVALID_ARG, "valid_tokens %lld outside [0, %d]", (long long)valid_tokens, L->T);
+    L->valid_tokens = (long)valid_tokens;
+    g_err.clear();
+    return TEL_OK;
+}
+
 tel_status tel_layer_destroy(tel_layer* L) {
     delete L;
     return TEL_OK;
@@ -285,6 +310,14 @@ static tel_status check_grads(const tel_grads* g) {
     return TEL_OK;
 }
 
+// Rows the layer runs on: the valid tokens rounded up to the 256-row GEMM
+// tile when packing pays (some padding, key lengths given), else all B*S.
+static int packed_rows(const tel_layer* L, const int32_t* key_lengths) {
+    if (!L->cfg.pack_tokens || !key_lengths || L->valid_tokens <= 0) return 0;
+    const long P = (L->valid_tokens + 255) / 256 * 256;
+    return P < L->T ? (int)P : 0;
+}
+
 struct Bases {
     void* saved;
     void* scratch;
@@ -305,12 +338,27 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     hipStream_t st = (hipStream_t)stream;
     const tel_config& c = L->cfg;
     const Plan& p = L->plan;
-    const int T = L->T, H = L->H, F = L->F, dt = c.dtype;
+    const int H = L->H, F = L->F, dt = c.dtype;
     // without a saved buffer every "saved" tensor lives in a private region of scratch
     // placed after the scratch plan: callers that pass saved = NULL must size scratch
     // as saved_bytes + scratch_bytes.
     void* sv = saved ? saved : (char*)scratch + align_up(p.scratch_bytes);
     Bases bs{sv, scratch};
+    // token packing: the layer runs on PR packed rows (x gathered, y scattered back)
+    const int PR = packed_rows(L, key_lengths);
+    const int T = PR ? PR : L->T;
+    const int32_t* rmap = PR ? (const int32_t*)bs.of(p.rmap) : nullptr;
+    const int32_t* rinv = PR ? (const int32_t*)bs.of(p.rinv) : nullptr;
+    const void* xin = x;
+    void* yout = y;
+    if (PR) {
+        HIP_TRY(build_row_maps(key_lengths, L->B, L->S, PR, (int32_t*)bs.of(p.rmap), (int32_t*)bs.of(p.rinv), st));
+        HIP_TRY(gather_rows(dt, x, bs.of(p.xp), rmap, PR, H, st));
+        // the QKV epilogue writes valid tokens only; attention reads the rest as zeros
+        HIP_TRY(zero_padded_heads(dt, bs.of(p.qkvh), 3, L->B, L->NH, L->S, L->d, key_lengths, st));
+        xin = bs.of(p.xp);
+        yout = bs.of(p.yp);
+    }
     const Drop d0 = make_drop(L, c.attn_dropout, 0, step, training);
     const Drop d1 = make_drop(L, c.hidden_dropout, 1, step, training);
     const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
@@ -320,6 +368,13 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     aa.qkvh = bs.of(p.qkvh); aa.len = key_lengths; aa.drop = d0;
     aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
     aa.bits = p.abits.used ? (uint32_t*)bs.of(p.abits) : nullptr;
+    aa.packed = rinv;
+    // attention writes the valid tokens' rows of ctx; filler rows must be finite
+    auto attn = [&]() -> hipError_t {
+        hipError_t e = attn_forward(aa, st);
+        if (e != hipSuccess || !PR) return e;
+        return zero_rows(dt, aa.ctx, (int)L->valid_tokens, PR, H, st);
+    };
 
     auto proj = [&](const void* A, const void* W, int N, int K, int epi) {
         GemmDesc g;
@@ -327,21 +382,22 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         g.A = A; g.lda = K; g.a_kmajor = true;
         g.B = W; g.ldb = K; g.b_kmajor = true;
         g.epi = epi;
+        g.ea.row_map = rmap;
         return g;
     };
 
     if (c.pre_ln) {
-        LnFwdArgs l1{dt, T, H, c.ln_eps, x, 0, P->ln1_g, P->ln1_b, bs.of(p.ln1_out), nullptr, nullptr,
+        LnFwdArgs l1{dt, T, H, c.ln_eps, xin, 0, P->ln1_g, P->ln1_b, bs.of(p.ln1_out), nullptr, nullptr,
                      (float*)bs.of(p.mu1), (float*)bs.of(p.rs1)};
         TIMED(TEL_K_LN1_FWD, ln_forward(l1, st));
         GemmDesc g = proj(bs.of(p.ln1_out), P->w_qkv, 3 * H, H, EPI_QKV);
         g.ea.out = bs.of(p.qkvh); g.ea.bias = P->b_qkv;
         g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
         TIMED(TEL_K_QKV_FWD, gemm_launch(g, st));
-        TIMED(TEL_K_ATTN_FWD, attn_forward(aa, st));
+        TIMED(TEL_K_ATTN_FWD, attn());
         g = proj(bs.of(p.ctx), P->w_o, H, H, EPI_BIAS_DROP_RES);
         g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_o;
-        g.ea.res = x; g.ea.res_f32 = 0; g.ea.drop = d1;
+        g.ea.res = xin; g.ea.res_f32 = 0; g.ea.drop = d1;
         TIMED(TEL_K_OUT_FWD, gemm_launch(g, st));
         LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res1), 1, P->ln2_g, P->ln2_b, bs.of(p.ln2_out), nullptr, nullptr,
                      (float*)bs.of(p.mu2), (float*)bs.of(p.rs2)};
@@ -351,18 +407,18 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         g.ea.gelu_grad_out = !c.gelu_checkpoint;
         TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
         g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
-        g.ea.out = y; g.ea.ldo = H; g.ea.out_f32 = 0; g.ea.bias = P->b_2;
+        g.ea.out = yout; g.ea.ldo = H; g.ea.out_f32 = 0; g.ea.bias = P->b_2;
         g.ea.res = bs.of(p.res1); g.ea.res_f32 = 1; g.ea.drop = d2;
         TIMED(TEL_K_FFN2_FWD, gemm_launch(g, st));
     } else {
-        GemmDesc g = proj(x, P->w_qkv, 3 * H, H, EPI_QKV);
+        GemmDesc g = proj(xin, P->w_qkv, 3 * H, H, EPI_QKV);
         g.ea.out = bs.of(p.qkvh); g.ea.bias = P->b_qkv;
         g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
         TIMED(TEL_K_QKV_FWD, gemm_launch(g, st));
-        TIMED(TEL_K_ATTN_FWD, attn_forward(aa, st));
+        TIMED(TEL_K_ATTN_FWD, attn());
         g = proj(bs.of(p.ctx), P->w_o, H, H, EPI_BIAS_DROP_RES);
         g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_o;
-        g.ea.res = x; g.ea.res_f32 = 0; g.ea.drop = d1;
+        g.ea.res = xin; g.ea.res_f32 = 0; g.ea.drop = d1;
         TIMED(TEL_K_OUT_FWD, gemm_launch(g, st));
         LnFwdArgs l1{dt, T, H, c.ln_eps, bs.of(p.res1), 1, P->ln1_g, P->ln1_b, bs.of(p.x1e),
                      (float*)bs.of(p.x1f), nullptr, (float*)bs.of(p.mu1), (float*)bs.of(p.rs1)};
@@ -375,10 +431,11 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         g.ea.out = bs.of(p.res2); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_2;
         g.ea.res = bs.of(p.x1f); g.ea.res_f32 = 1; g.ea.drop = d2;
         TIMED(TEL_K_FFN2_FWD, gemm_launch(g, st));
-        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res2), 1, P->ln2_g, P->ln2_b, y, nullptr,
+        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res2), 1, P->ln2_g, P->ln2_b, yout, nullptr,
                      p.ycopy.used ? bs.of(p.ycopy) : nullptr, (float*)bs.of(p.mu2), (float*)bs.of(p.rs2)};
         TIMED(TEL_K_LN2_FWD, ln_forward(l2, st));
     }
+    if (PR) HIP_TRY(scatter_rows(dt, yout, y, rinv, L->T, H, st));
     if (saved) L->pending_fwd++;
     g_err.clear();
     return TEL_OK;
@@ -402,8 +459,21 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     if (L->pending_fwd <= 0) return fail(TEL_ERR_STATE, "backward called without a preceding forward with saved state");
     hipStream_t st = (hipStream_t)stream;
     const Plan& p = L->plan;
-    const int T = L->T, H = L->H, F = L->F, dt = c.dtype;
+    const int H = L->H, F = L->F, dt = c.dtype;
     Bases bs{const_cast<void*>(saved), scratch};
+    // token packing: the forward's PR packed rows (dy gathered, dx scattered back)
+    const int PR = packed_rows(L, key_lengths);
+    const int T = PR ? PR : L->T;
+    const int32_t* rmap = PR ? (const int32_t*)bs.of(p.rmap) : nullptr;
+    const int32_t* rinv = PR ? (const int32_t*)bs.of(p.rinv) : nullptr;
+    const void* xin = PR ? bs.of(p.xp) : x;
+    const void* dyin = dy;
+    void* dxout = dx;
+    if (PR) {
+        HIP_TRY(gather_rows(dt, dy, bs.of(p.dyp), rmap, PR, H, st));
+        dyin = bs.of(p.dyp);
+        dxout = bs.of(p.dxp);
+    }
     const Drop d0 = make_drop(L, c.attn_dropout, 0, step, training);
     const Drop d1 = make_drop(L, c.hidden_dropout, 1, step, training);
     const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
@@ -424,6 +494,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g.A = dY; g.lda = out; g.a_kmajor = true;
         g.B = W; g.ldb = in; g.b_kmajor = false;
         g.epi = epi;
+        g.ea.row_map = rmap;
         return g;
     };
     // dW[out][in] = dY^T . X, written to the caller's gradient (dtype)
@@ -458,12 +529,23 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
     aa.dout = bs.of(p.dout); aa.dvec = (float*)bs.of(p.dvec); aa.dqkv = bs.of(p.dqkv);
     aa.bits = p.abits.used ? (uint32_t*)bs.of(p.abits) : nullptr;
+    aa.packed = rinv;
+    // padding tokens: their dO is zero (the head-split scatter writes valid
+    // tokens only), and the filler rows of dqkv must be finite for the GEMMs
+    auto attn = [&]() -> hipError_t {
+        hipError_t e = attn_backward(aa, st);
+        if (e != hipSuccess || !PR) return e;
+        return zero_rows(dt, aa.dqkv, (int)L->valid_tokens, PR, 3 * H, st);
+    };
+    auto zero_dout = [&]() -> hipError_t {
+        return PR ? zero_padded_heads(dt, bs.of(p.dout), 1, L->B, L->NH, L->S, L->d, key_lengths, st) : hipSuccess;
+    };
 
     const void* g_src = gck ? bs.of(p.u) : bs.of(p.g);  // FFN2 input (or GELU input to recompute it from)
 
     if (c.pre_ln) {
         // y = x1 + drop2(g W2^T + b2)
-        HIP_TRY(dropout_apply(dt, dy, bs.of(p.df), (size_t)T * H, d2, st));
+        HIP_TRY(dropout_apply(dt, dyin, bs.of(p.df), (size_t)T * H, d2, st, rmap, H));
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
@@ -479,18 +561,19 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.src = inv ? bs.of(p.ln2_out) : bs.of(p.res1); lb.src_f32 = inv ? 0 : 1; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
         lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
-        lb.res = dy; lb.res_f32 = 0;
+        lb.res = dyin; lb.res_f32 = 0;
         lb.out = bs.of(p.dres); lb.out_f32 = 1;
         lb.drop_out = bs.of(p.dz); lb.drop = d1;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
         TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
         // out-projection
         g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
         g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
+        HIP_TRY(zero_dout());
         TIMED(TEL_K_OUT_DGRAD, gemm_launch(g, st));
         TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false, G->b_o));
-        TIMED(TEL_K_ATTN_BWD, attn_backward(aa, st));
+        TIMED(TEL_K_ATTN_BWD, attn());
         // QKV projection
         g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
@@ -500,25 +583,25 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb = LnBwdArgs{};
         lb.dtype = dt; lb.T = T; lb.H = H;
         lb.dout = bs.of(p.dgemm);
-        lb.src = inv ? bs.of(p.ln1_out) : x; lb.src_f32 = 0; lb.from_output = inv;
+        lb.src = inv ? bs.of(p.ln1_out) : xin; lb.src_f32 = 0; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu1); lb.rstd = (const float*)bs.of(p.rs1);
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
         lb.res = bs.of(p.dres); lb.res_f32 = 1;
-        lb.out = dx; lb.out_f32 = 0;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        lb.out = dxout; lb.out_f32 = 0;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(G->ln1_g, G->ln1_b));
     } else {
         // y = LN2(z2): dz2 = LN2'(dy); df = drop2(dz2)
         LnBwdArgs lb{};
         lb.dtype = dt; lb.T = T; lb.H = H;
-        lb.dout = dy;
+        lb.dout = dyin;
         lb.src = inv ? bs.of(p.ycopy) : bs.of(p.res2); lb.src_f32 = inv ? 0 : 1; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
         lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
         lb.out = bs.of(p.dres2); lb.out_f32 = 1;
         lb.drop_out = bs.of(p.df); lb.drop = d2;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
         TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
@@ -538,20 +621,22 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
         lb.out = bs.of(p.dres); lb.out_f32 = 1;
         lb.drop_out = bs.of(p.dz); lb.drop = d1;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b;
+        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(G->ln1_g, G->ln1_b));
         g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
         g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
+        HIP_TRY(zero_dout());
         TIMED(TEL_K_OUT_DGRAD, gemm_launch(g, st));
         TIMED(TEL_K_OUT_WGRAD, wgrad(bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, false, G->b_o));
-        TIMED(TEL_K_ATTN_BWD, attn_backward(aa, st));
+        TIMED(TEL_K_ATTN_BWD, attn());
         // dx = dz1 + dqkv W_qkv
         g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_ADD_RES);
-        g.ea.out = dx; g.ea.ldo = H; g.ea.res = bs.of(p.dres);
+        g.ea.out = dxout; g.ea.ldo = H; g.ea.res = bs.of(p.dres);
         TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
-        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), x, 3 * H, H, G->w_qkv, false, G->b_qkv));
+        TIMED(TEL_K_QKV_WGRAD, wgrad(bs.of(p.dqkv), xin, 3 * H, H, G->w_qkv, false, G->b_qkv));
     }
+    if (PR) HIP_TRY(scatter_rows(dt, dxout, dx, rinv, L->T, H, st));
     L->pending_fwd--;
     g_err.clear();
     return TEL_OK;

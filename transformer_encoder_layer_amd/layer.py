@@ -43,12 +43,14 @@ class LayerConfig:
     attn_dropout_checkpoint: bool = False
     normalize_invertible: bool = False
     gelu_checkpoint: bool = False
+    pack_tokens: bool = False
 
     def to_c(self) -> B.tel_config:
         return B.tel_config(self.batch, self.seq, self.hidden, self.heads, self.ffn, self.attn_dropout,
                             self.hidden_dropout, int(self.pre_ln), self.seed, self.layer_id,
                             _DTYPES[self.dtype], self.ln_eps, int(self.attn_dropout_checkpoint),
-                            int(self.normalize_invertible), int(self.gelu_checkpoint))
+                            int(self.normalize_invertible), int(self.gelu_checkpoint),
+                            int(self.pack_tokens))
 
 
 _scratch = {}
@@ -70,8 +72,10 @@ def _round256(n: int) -> int:
 
 class _LayerFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, lengths, step, layer, *params):
+    def forward(ctx, x, lengths, step, valid, layer, *params):
         dev = x.device
+        if valid is not None:
+            B.tel_layer_set_valid_tokens(layer.handle, valid)
         need_grad = torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in params))
         x = x.contiguous()
         y = torch.empty_like(x)
@@ -87,6 +91,7 @@ class _LayerFn(torch.autograd.Function):
         ctx.saved_buf = saved
         ctx.save_for_backward(x, *params)
         ctx.lengths = lengths
+        ctx.valid = valid
         return y
 
     @staticmethod
@@ -97,11 +102,13 @@ class _LayerFn(torch.autograd.Function):
         dx = torch.empty_like(x)
         grads = [torch.empty_like(p) for p in params]
         scratch = scratch_buffer(x.device, layer.scratch_bytes)
+        if ctx.valid is not None:
+            B.tel_layer_set_valid_tokens(layer.handle, ctx.valid)
         B.tel_layer_backward(layer.handle, B.make_params(dict(zip(B.PARAM_NAMES, params))), x, ctx.lengths,
                              ctx.training_flag, ctx.step, dy, ctx.saved_buf, scratch, dx,
                              B.make_grads(dict(zip(B.PARAM_NAMES, grads))))
         ctx.saved_buf = None
-        return (dx, None, None, None, *grads)
+        return (dx, None, None, None, None, *grads)
 
 
 class EncoderLayer(torch.nn.Module):
@@ -123,8 +130,14 @@ class EncoderLayer(torch.nn.Module):
     def params(self):
         return [getattr(self, n) for n in B.PARAM_NAMES]
 
-    def forward(self, x: torch.Tensor, key_lengths: Optional[torch.Tensor] = None, step: int = 0):
-        return _LayerFn.apply(x, key_lengths, int(step), self, *self.params())
+    def forward(self, x: torch.Tensor, key_lengths: Optional[torch.Tensor] = None, step: int = 0,
+                valid_tokens: Optional[int] = None):
+        """valid_tokens: sum of key_lengths (token packing); computed on the
+        host from key_lengths when packing is on and it is not given."""
+        valid = None
+        if self.cfg.pack_tokens and key_lengths is not None:
+            valid = int(key_lengths.sum().item()) if valid_tokens is None else int(valid_tokens)
+        return _LayerFn.apply(x, key_lengths, int(step), valid, self, *self.params())
 
     def __del__(self):
         h = getattr(self, "handle", None)
