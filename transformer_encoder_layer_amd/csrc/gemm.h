@@ -67,6 +67,17 @@ struct GemmDesc {
 // True if gemm_launch computes rowsum_out for this GEMM inside its kernel.
 bool gemm_rowsum_fused(const GemmDesc& g);
 
+// Two weight gradients (A and B m/n-major, EPI_STORE, no GELU on load, M
+// and N multiples of 256) in one persistent launch, so that the tiles of
+// both fill the chip with fewer k-splits than either alone; a's workspace
+// (splitk_ws, splitk_ws_elems) holds the partials of both.  Row sums are
+// fused as in gemm_launch.  gemm_group_ok tells whether the pair qualifies;
+// gemm_launch_group returns hipErrorInvalidValue (launching nothing) if not.
+bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b);
+hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t stream);
+// Workspace elements gemm_launch_group needs for the pair (0: none).
+size_t gemm_splitk_group_elems(const GemmDesc& a, const GemmDesc& b);
+
 // Launch; returns hipSuccess or the launch error.  force_simt selects the
 // generic SIMT kernel regardless of shape (used by tests).
 hipError_t gemm_launch(const GemmDesc& g, hipStream_t stream, bool force_simt = false);

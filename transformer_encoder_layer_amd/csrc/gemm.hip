@@ -166,6 +166,15 @@ struct GemmParams {
     void* rsum;       // row sums of A: dtype [M] (one split) or fp32 [splits][M] after ws
 };
 
+// One or two GEMMs of the same tile shape run by one persistent launch: the
+// work units are problem 0's (split, tile) pairs, then problem 1's.
+struct GemmGroup {
+    GemmParams p[2];
+    int splits[2];
+    int units0;  // units of problem 0 (its tiles x splits)
+    int units;   // all units
+};
+
 // ------------------------------------------------------------------ MFMA path
 constexpr int KT = 64;        // k tile (elements)
 // Padding (elements) of m/n-major LDS rows: rows of 128 or 256 elements
@@ -283,12 +292,12 @@ __device__ __forceinline__ void tile_of(int pid, int tm, int tn, int& im, int& i
 template <typename T, int EPI, int BM, int BN, int WGM, int WGN>
 __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
                                               unsigned char* smem_raw, int m0, int n0, int wm, int wn, int wave,
-                                              int lane) {
+                                              int lane, int split, int nsplit) {
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
     // acc[i][j][g*4 + r]: row m = m0 + wm*WM + i*32 + (lane & 31),
     // columns n .. n+3 with n = n0 + wn*WN + j*32 + g*8 + (lane >> 5)*4.
-    if (gridDim.z > 1) {
+    if (nsplit > 1) {  // split-K partial: fp32 to the workspace slice of this split
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -299,7 +308,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
                     const int n = n0 + wn * WN + j * 32 + g * 8 + (lane >> 5) * 4;
                     float v[4] = {acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2],
                                   acc[i][j][g * 4 + 3]};
-                    Vec4<float>::store(p.ws + ((size_t)blockIdx.z * p.M + m) * p.N + n, v);
+                    Vec4<float>::store(p.ws + ((size_t)split * p.M + m) * p.N + n, v);
                 }
         return;
     }
@@ -476,7 +485,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) 
         }
     }
 
-    gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
+    gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, blockIdx.z, gridDim.z);
 }
 
 // ------------------------------------------------------------------ direct-load path
@@ -744,7 +753,7 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
                 __syncthreads();
             }
         }
-        gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
+        gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, blockIdx.z, gridDim.z);
     }
 }
 
@@ -823,7 +832,7 @@ __device__ __forceinline__ float frag_sum8(bf16x8 x, float acc) {
 }
 
 template <typename T, int BM, int BN, bool AK, bool BKM, int EPI>
-__global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
+__global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
     constexpr int WM = BM / 2, WN = BN / 2;
     constexpr int MI = WM / 32, NI = WN / 32;  // A and B fragments per k-step
     constexpr int NF = MI + NI;                // fragments per k-step: MI A, NI B
@@ -842,17 +851,22 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int tm = p.M / BM, tn = p.N / BN;
     const int wave_s = __builtin_amdgcn_readfirstlane(wave);
-    const Dl4Plan<T, AK, BM> pa(p.lda, wave_s, lane);
-    const Dl4Plan<T, BKM, BN> pb(p.ldb, wave_s, lane);
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem_raw;
-    for (int pid = blockIdx.x; pid < tm * tn; pid += gridDim.x) {
-        if (pid != (int)blockIdx.x) __syncthreads();  // the last epilogue is done with LDS
+    for (int u = blockIdx.x; u < G.units; u += gridDim.x) {
+        if (u != (int)blockIdx.x) __syncthreads();  // the last epilogue is done with LDS
+        const int g = u >= G.units0 ? 1 : 0;
+        const GemmParams& p = g ? G.p[1] : G.p[0];
+        const int nsplit = g ? G.splits[1] : G.splits[0];
+        const int tm = p.M / BM, tn = p.N / BN;
+        const int lu = u - (g ? G.units0 : 0);
+        const int split = lu / (tm * tn), pid = lu - split * (tm * tn);
+        const Dl4Plan<T, AK, BM> pa(p.lda, wave_s, lane);
+        const Dl4Plan<T, BKM, BN> pb(p.ldb, wave_s, lane);
         int im, in_;
         tile_of(pid, tm, tn, im, in_);
         const int m0 = im * BM, n0 = in_ * BN;
-        const int kbeg = blockIdx.z * p.k_per_split;
+        const int kbeg = split * p.k_per_split;
         const int kend = min(p.K, kbeg + p.k_per_split);
         const int nk = (kend - kbeg) / QKT;
         const T* A = (const T*)p.A;
@@ -966,13 +980,13 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmParams p) {
                     const float t = rsa[i] + __shfl_xor(rsa[i], 32, 64);
                     if (wn == 0 && lane < 32) {
                         const int mrow = m0 + wm * WM + i * 32 + lane;
-                        if (gridDim.z > 1) reinterpret_cast<float*>(p.rsum)[(size_t)blockIdx.z * p.M + mrow] = t;
+                        if (nsplit > 1) reinterpret_cast<float*>(p.rsum)[(size_t)split * p.M + mrow] = t;
                         else reinterpret_cast<T*>(p.rsum)[mrow] = from_f<T>(t);
                     }
                 }
             }
         }
-        gemm_epilogue<T, EPI, BM, BN, 2, 2>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane);
+        gemm_epilogue<T, EPI, BM, BN, 2, 2>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, split, nsplit);
     }
 }
 
@@ -1173,38 +1187,131 @@ static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
     return hipGetLastError();
 }
 
-template <typename T, int BM, int BN, bool AK, bool BKM, int EPI>
-static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
-    float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
+// Kernel parameters of one GEMM of a launch with `splits` k-splits whose
+// partials (and per-split row sums) go to ws.
+template <bool AK>
+static GemmParams dl4_params(const GemmDesc& g, int splits, float* ws) {
+    float* rs_part = splits > 1 ? ws + (size_t)splits * g.M * g.N : nullptr;
     void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
-    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
-    auto kern = gemm_dl4_kernel<T, BM, BN, AK, BKM, EPI>;
-    size_t lds = (size_t)QNS * (BM + BN) * QKT * sizeof(T);
-    lds = std::max(lds, epilogue_lds_bytes<BM, BN, 2, 2>());
-    lds = std::max(lds, (size_t)256 * 8 * 4);
-    static int slots = 0;  // workgroups of this kernel resident on the whole device
+    return GemmParams{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, ws, rsum};
+}
+
+// Resident workgroups of a dl4 instantiation on the device (0 on failure).
+template <typename T, int BM, int BN, bool AK, bool BKM, int EPI>
+static int dl4_slots(size_t lds) {
+    static int slots = 0;
     if (!slots) {
-        hipError_t e = set_lds(kern, lds);
-        if (e != hipSuccess) return e;
+        auto kern = gemm_dl4_kernel<T, BM, BN, AK, BKM, EPI>;
+        if (set_lds(kern, lds) != hipSuccess) return 0;
         int per_cu = 0, dev = 0, cus = 0;
-        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds);
-        if (e != hipSuccess) return e;
-        e = hipGetDevice(&dev);
-        if (e != hipSuccess) return e;
-        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-        if (e != hipSuccess) return e;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 256, lds) != hipSuccess) return 0;
+        if (hipGetDevice(&dev) != hipSuccess) return 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
         slots = std::max(1, per_cu) * std::max(1, cus);
     }
-    const int tiles = (g.M / BM) * (g.N / BN);
-    int gx = std::min(tiles, std::max(8, slots / splits / 8 * 8));
-    hipLaunchKernelGGL(kern, dim3(gx, 1, splits), dim3(256), lds, st, p);
+    return slots;
+}
+
+template <int BM, int BN>
+constexpr size_t dl4_lds_bytes(size_t esz) {
+    return std::max(std::max((size_t)QNS * (BM + BN) * QKT * esz, epilogue_lds_bytes<BM, BN, 2, 2>()),
+                    (size_t)256 * 8 * 4);
+}
+
+// Deterministic reduction of one GEMM's split-K partials (and row sums).
+template <typename T>
+static hipError_t splitk_reduce(const GemmDesc& g, int splits, const float* ws, hipStream_t st) {
+    const float* rs_part = ws + (size_t)splits * g.M * g.N;
+    const bool rsum = g.rowsum_out != nullptr && !g.a_kmajor;
+    const size_t n4 = (size_t)g.M * g.N / 4;
+    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, ws, splits,
+                       g.M, g.N, g.ea, rsum ? rs_part : nullptr, rsum ? reinterpret_cast<T*>(g.rowsum_out) : (T*)nullptr);
+    return hipGetLastError();
+}
+
+template <typename T, int BM, int BN, bool AK, bool BKM, int EPI>
+static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
+    auto kern = gemm_dl4_kernel<T, BM, BN, AK, BKM, EPI>;
+    const size_t lds = dl4_lds_bytes<BM, BN>(sizeof(T));
+    const int slots = dl4_slots<T, BM, BN, AK, BKM, EPI>(lds);  // workgroups resident on the device
+    if (!slots) return hipErrorInvalidConfiguration;
+    GemmGroup G{};
+    G.p[0] = G.p[1] = dl4_params<AK>(g, splits, g.splitk_ws);
+    G.splits[0] = G.splits[1] = splits;
+    G.units0 = G.units = (g.M / BM) * (g.N / BN) * splits;
+    // persistent grid: at most one resident wave of workgroups, a multiple of
+    // the 8 XCDs so each workgroup's tiles stay on its XCD's range
+    const int gx = std::min(G.units, std::max(8, slots / 8 * 8));
+    hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    const size_t n4 = (size_t)g.M * g.N / 4;
-    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea, rs_part,
-                       rsum ? reinterpret_cast<T*>(g.rowsum_out) : (T*)nullptr);
-    return hipGetLastError();
+    return splitk_reduce<T>(g, splits, g.splitk_ws, st);
+}
+
+// Two weight gradients in one launch (256x256 tiles, A and B m/n-major,
+// plain store with fused row sums): the split count fills the chip with the
+// tiles of both; partials of the second follow those of the first in ws.
+static int group_splits(const GemmDesc& a, const GemmDesc& b) {
+    auto ok = [](const GemmDesc& g) {
+        return g.dtype != 0 && !g.a_kmajor && !g.b_kmajor && !g.b_gelu && g.epi == EPI_STORE &&
+               g.M % 256 == 0 && g.N % 256 == 0 && g.K % QKT == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
+    };
+    if (!ok(a) || !ok(b) || a.dtype != b.dtype) return 0;
+    // one workgroup per CU: the largest split count (<= 4) whose units fit
+    // one wave of 256, and only if that wave is at least three quarters full
+    const int tiles = (a.M / 256) * (a.N / 256) + (b.M / 256) * (b.N / 256);
+    int s = 1;
+    while (tiles * s * 2 <= 256 && s < 4) s *= 2;
+    // every split keeps at least 8 k tiles
+    while (s > 1 && (a.K % (s * QKT) || b.K % (s * QKT) || a.K / (s * QKT) < 8 || b.K / (s * QKT) < 8)) s /= 2;
+    return tiles * s >= 192 && tiles * s <= 256 ? s : 0;
+}
+
+size_t gemm_splitk_group_elems(const GemmDesc& a, const GemmDesc& b) {
+    const int s = group_splits(a, b);
+    if (s <= 1) return 0;
+    return (size_t)s * ((size_t)a.M * a.N + a.M + (size_t)b.M * b.N + b.M);
+}
+
+bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b) {
+    const int s = group_splits(a, b);
+    if (s == 0) return false;
+    if (s > 1 && (a.splitk_ws == nullptr || gemm_splitk_group_elems(a, b) > a.splitk_ws_elems)) return false;
+    return true;
+}
+
+template <typename T>
+static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
+    constexpr int BM = 256, BN = 256;
+    const int splits = group_splits(a, b);
+    auto kern = gemm_dl4_kernel<T, BM, BN, false, false, EPI_STORE>;
+    const size_t lds = dl4_lds_bytes<BM, BN>(sizeof(T));
+    const int slots = dl4_slots<T, BM, BN, false, false, EPI_STORE>(lds);
+    if (!slots) return hipErrorInvalidConfiguration;
+    float* ws_a = a.splitk_ws;
+    float* ws_b = splits > 1 ? ws_a + (size_t)splits * ((size_t)a.M * a.N + a.M) : nullptr;
+    GemmGroup G{};
+    G.p[0] = dl4_params<false>(a, splits, ws_a);
+    G.p[1] = dl4_params<false>(b, splits, ws_b);
+    G.splits[0] = G.splits[1] = splits;
+    G.units0 = (a.M / BM) * (a.N / BN) * splits;
+    G.units = G.units0 + (b.M / BM) * (b.N / BN) * splits;
+    const int gx = std::min(G.units, std::max(8, slots / 8 * 8));
+    hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || splits == 1) return e;
+    e = splitk_reduce<T>(a, splits, ws_a, st);
+    if (e != hipSuccess) return e;
+    return splitk_reduce<T>(b, splits, ws_b, st);
+}
+
+hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
+    if (!gemm_group_ok(a, b)) return hipErrorInvalidValue;
+    switch (a.dtype) {
+        case 1: return launch_dl4_group<f16>(a, b, st);
+        case 2: return launch_dl4_group<bf16>(a, b, st);
+    }
+    return hipErrorInvalidValue;
 }
 
 // Tiles run the four-wave kernel (2 x 2 waves of BM/2 x BN/2, 64-deep k
