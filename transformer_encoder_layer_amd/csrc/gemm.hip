@@ -80,6 +80,27 @@ struct Epi {
             Vec4<T>::load(reinterpret_cast<const T*>(&raw), r);
         }
     }
+    // Dropout element index of (row m, column n): token * ldo + column.
+    static __device__ __forceinline__ uint64_t drop_element(const EpiArgs& e, int m, int n) {
+        const int t = e.row_map ? max(e.row_map[m], 0) : m;
+        return (uint64_t)t * e.ldo + n;
+    }
+    // EPI_BIAS_DROP_RES with the keep bits of the 4 elements given (bit i:
+    // column n + i; all set without dropout).
+    static __device__ __forceinline__ void finish_drop(const EpiArgs& e, int m, int n, float v[4], const float b[4],
+                                                       const float r[4], uint32_t k) {
+        const size_t off = (size_t)m * e.ldo + n;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += b[i];
+        if (e.drop.thr) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * e.drop.scale : 0.0f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] += r[i];
+        if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
+        else Vec4<T>::store((T*)e.out + off, v);
+    }
     static __device__ __forceinline__ void finish(const EpiArgs& e, int m, int n, float v[4], const float b[4],
                                                   const float r[4]) {
         const size_t off = (size_t)m * e.ldo + n;
@@ -96,19 +117,9 @@ struct Epi {
             const size_t o = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
         } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] += b[i];
-            if (e.drop.thr) {
-                const int t = e.row_map ? max(e.row_map[m], 0) : m;
-                const uint64_t el = (uint64_t)t * e.ldo + n;  // token * H + column, n % 4 == 0
-                const uint32_t k = keep4(e.drop.rng, el >> 2, e.drop.thr);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) v[i] = ((k >> i) & 1u) ? v[i] * e.drop.scale : 0.0f;
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] += r[i];
-            if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
-            else Vec4<T>::store((T*)e.out + off, v);
+            uint32_t k = 0xFu;
+            if (e.drop.thr) k = keep4(e.drop.rng, drop_element(e, m, n) >> 2, e.drop.thr);
+            finish_drop(e, m, n, v, b, r, k);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             // u is rounded to the storage type first, so GELU(u) and GELU'(u)
             // are those of the stored u (what a recompute from u would give)
@@ -351,6 +362,26 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
                 *reinterpret_cast<float4*>(est + (lane & 31) * ELD + col) =
                     make_float4(acc[i][j][g * 4 + 0], acc[i][j][g * 4 + 1], acc[i][j][g * 4 + 2], acc[i][j][g * 4 + 3]);
             }
+        // Dropout keep bits of this lane's rows: lanes 2c and 2c+1 hold the
+        // two halves of one 8-column Philox block, so for each pair of rows
+        // each draws the block of one row and they swap the results (half
+        // the Philox calls of one per 4 elements).
+        uint32_t kn[NIT];
+        if constexpr (EPI == EPI_BIAS_DROP_RES) {
+            static_assert(NIT % 2 == 0 && GPR % 2 == 0, "row pairs and column-group pairs");
+            const int odd = cg & 1;
+#pragma unroll
+            for (int t = 0; t < NIT / 2; ++t) {
+                uint32_t k8 = 0xFFu;
+                if (p.ea.drop.thr) {
+                    const int m = m0 + wm * WM + i * 32 + (2 * t + odd) * RPI + r0;
+                    k8 = keep8(p.ea.drop.rng, E::drop_element(p.ea, m, n - odd * 4) >> 3, p.ea.drop.thr);
+                }
+                const uint32_t o8 = __shfl_xor(k8, 1, 64);
+                kn[2 * t] = odd ? (o8 >> 4) : (k8 & 0xFu);
+                kn[2 * t + 1] = odd ? (k8 >> 4) : (o8 & 0xFu);
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -360,7 +391,8 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
             float v[4] = {q.x, q.y, q.z, q.w};
             float r[4] = {0, 0, 0, 0};
             if constexpr (E::kElem) E::elem_from_raw(p.ea, el[i % PB][it], r);
-            E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
+            if constexpr (EPI == EPI_BIAS_DROP_RES) E::finish_drop(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r, kn[it]);
+            else E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
         }
         if constexpr (E::kElem) {
             if (i + PB < MI) {
