@@ -80,9 +80,11 @@ struct Epi {
             Vec4<T>::load(reinterpret_cast<const T*>(&raw), r);
         }
     }
-    // Dropout element index of (row m, column n): token * ldo + column.
+    // Dropout element index of (row m, column n): token * ldo + column; PK:
+    // packed rows, the token comes from row_map (filler rows use token 0).
+    template <bool PK>
     static __device__ __forceinline__ uint64_t drop_element(const EpiArgs& e, int m, int n) {
-        const int t = e.row_map ? max(e.row_map[m], 0) : m;
+        const int t = PK ? max(e.row_map[m], 0) : m;
         return (uint64_t)t * e.ldo + n;
     }
     // EPI_BIAS_DROP_RES with the keep bits of the 4 elements given (bit i:
@@ -101,6 +103,7 @@ struct Epi {
         if (e.out_f32) Vec4<float>::store((float*)e.out + off, v);
         else Vec4<T>::store((T*)e.out + off, v);
     }
+    template <bool PK = false>
     static __device__ __forceinline__ void finish(const EpiArgs& e, int m, int n, float v[4], const float b[4],
                                                   const float r[4]) {
         const size_t off = (size_t)m * e.ldo + n;
@@ -110,15 +113,15 @@ struct Epi {
         } else if constexpr (EPI == EPI_QKV) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] += b[i];
-            const int t = e.row_map ? e.row_map[m] : m;
-            if (t < 0) return;
+            const int t = PK ? e.row_map[m] : m;
+            if (PK && t < 0) return;
             const int which = n / e.H, rem = n - which * e.H, h = rem / e.d, c = rem - h * e.d;
             const int bb = t / e.S, s = t - bb * e.S;
             const size_t o = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
         } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
             uint32_t k = 0xFu;
-            if (e.drop.thr) k = keep4(e.drop.rng, drop_element(e, m, n) >> 2, e.drop.thr);
+            if (e.drop.thr) k = keep4(e.drop.rng, drop_element<PK>(e, m, n) >> 2, e.drop.thr);
             finish_drop(e, m, n, v, b, r, k);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
             // u is rounded to the storage type first, so GELU(u) and GELU'(u)
@@ -145,8 +148,8 @@ struct Epi {
             for (int i = 0; i < 4; ++i) v[i] *= r[i];
             Vec4<T>::store((T*)e.out + off, v);
         } else if constexpr (EPI == EPI_HEADSPLIT) {
-            const int t = e.row_map ? e.row_map[m] : m;
-            if (t < 0) return;
+            const int t = PK ? e.row_map[m] : m;
+            if (PK && t < 0) return;
             const int bb = t / e.S, s = t - bb * e.S, h = n / e.d, c = n - h * e.d;
             const size_t o = (((size_t)bb * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
@@ -163,7 +166,8 @@ __device__ __forceinline__ void epilogue4(const EpiArgs& e, int m, int n, float 
     float b[4] = {0, 0, 0, 0}, r[4] = {0, 0, 0, 0};
     Epi<T, EPI>::load_bias(e, n, b);
     Epi<T, EPI>::load_elem(e, m, n, r);
-    Epi<T, EPI>::finish(e, m, n, v, b, r);
+    if (e.row_map) Epi<T, EPI>::template finish<true>(e, m, n, v, b, r);
+    else Epi<T, EPI>::template finish<false>(e, m, n, v, b, r);
 }
 
 struct GemmParams {
@@ -300,10 +304,10 @@ __device__ __forceinline__ void tile_of(int pid, int tm, int tn, int& im, int& i
 
 // Epilogue shared by the GEMM kernels (acc layout of the 32x32x16 MFMA with
 // the operand roles swapped: lane holds 4 consecutive columns of one row).
-template <typename T, int EPI, int BM, int BN, int WGM, int WGN>
-__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
-                                              unsigned char* smem_raw, int m0, int n0, int wm, int wn, int wave,
-                                              int lane, int split, int nsplit) {
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN, bool PK>
+__device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& p, f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                                   unsigned char* smem_raw, int m0, int n0, int wm, int wn, int wave,
+                                                   int lane, int split, int nsplit) {
     constexpr int WM = BM / WGM, WN = BN / WGN;
     constexpr int MI = WM / 32, NI = WN / 32;
     // acc[i][j][g*4 + r]: row m = m0 + wm*WM + i*32 + (lane & 31),
@@ -375,7 +379,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
                 uint32_t k8 = 0xFFu;
                 if (p.ea.drop.thr) {
                     const int m = m0 + wm * WM + i * 32 + (2 * t + odd) * RPI + r0;
-                    k8 = keep8(p.ea.drop.rng, E::drop_element(p.ea, m, n - odd * 4) >> 3, p.ea.drop.thr);
+                    k8 = keep8(p.ea.drop.rng, E::template drop_element<PK>(p.ea, m, n - odd * 4) >> 3, p.ea.drop.thr);
                 }
                 const uint32_t o8 = __shfl_xor(k8, 1, 64);
                 kn[2 * t] = odd ? (o8 >> 4) : (k8 & 0xFu);
@@ -392,7 +396,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
             float r[4] = {0, 0, 0, 0};
             if constexpr (E::kElem) E::elem_from_raw(p.ea, el[i % PB][it], r);
             if constexpr (EPI == EPI_BIAS_DROP_RES) E::finish_drop(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r, kn[it]);
-            else E::finish(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
+            else E::template finish<PK>(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
         }
         if constexpr (E::kElem) {
             if (i + PB < MI) {
@@ -403,6 +407,23 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
         }
         __builtin_amdgcn_wave_barrier();
     }
+}
+
+// Packed rows (row_map set) change only the head-split scatters and the
+// dropout element index; the choice is made once per kernel so that the
+// unpacked epilogue keeps its row arithmetic free of per-row loads.
+template <typename T, int EPI, int BM, int BN, int WGM, int WGN>
+__device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)[BM / WGM / 32][BN / WGN / 32],
+                                              unsigned char* smem_raw, int m0, int n0, int wm, int wn, int wave,
+                                              int lane, int split, int nsplit) {
+    if constexpr (EPI == EPI_QKV || EPI == EPI_HEADSPLIT || EPI == EPI_BIAS_DROP_RES) {
+        if (p.ea.row_map) {
+            gemm_epilogue_impl<T, EPI, BM, BN, WGM, WGN, true>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, split,
+                                                              nsplit);
+            return;
+        }
+    }
+    gemm_epilogue_impl<T, EPI, BM, BN, WGM, WGN, false>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, split, nsplit);
 }
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
