@@ -18,7 +18,7 @@ enum EpiKind {
     EPI_QKV = 1,           // v + bias, scattered to [3][B][N][S][d]
     EPI_BIAS_DROP_RES = 2, // out = res + drop(v + bias)            (res T|f32, out T|f32)
     EPI_BIAS_GELU = 3,     // u = v + bias -> out (or GELU'(u) if gelu_grad_out); GELU(u) -> out2 (if non-null)
-    EPI_GELU_BWD = 4,      // out = v * round_T(GELU'(aux))
+    EPI_GELU_BWD = 4,      // out = v * round_T(GELU'(aux)); out2 (optional) = GELU(aux)
     EPI_HEADSPLIT = 5,     // v scattered to [B][N][S][d]
     EPI_ADD_RES = 6,       // out = v + res(f32)
     EPI_MUL_AUX = 7,       // out = v * aux                         (aux T)

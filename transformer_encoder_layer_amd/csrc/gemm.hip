@@ -139,10 +139,19 @@ struct Epi {
             if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
         } else if constexpr (EPI == EPI_GELU_BWD) {
             // GELU'(u) rounded to the storage type, exactly as the forward
-            // stores it when GELU is not checkpointed (EPI_MUL_AUX path)
+            // stores it when GELU is not checkpointed (EPI_MUL_AUX path); with
+            // out2, also GELU(u) (the W2 weight gradient's operand), the same
+            // bits as gelu_f and as the forward's stored GELU(u)
+            float g[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] *= round_through<T>(gelu_grad_f(r[i]));
+            for (int i = 0; i < 4; ++i) {
+                float cdf, pdf;
+                normal_cdf_pdf(r[i], cdf, pdf);
+                v[i] *= round_through<T>(__fmaf_rn(r[i], pdf, cdf));  // gelu_grad_f(u)
+                g[i] = __fmul_rn(r[i], cdf);                          // gelu_f(u)
+            }
             Vec4<T>::store((T*)e.out + off, v);
+            if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
         } else if constexpr (EPI == EPI_MUL_AUX) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] *= r[i];

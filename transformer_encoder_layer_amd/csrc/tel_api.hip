@@ -67,6 +67,7 @@ struct Plan {
     Buf ycopy;    // Post-LN output copy (invertible LN2 backward)
     // scratch (backward)
     Buf df, du, dgemm, dres, dz, dout, dvec, dqkv, dres2;
+    Buf gck_g;    // GELU(u) recomputed in the backward under gelu checkpointing
     Buf part_ln, part_col, splitk;
     // token packing: row maps and x packed (saved); y, dy, dx packed (scratch)
     Buf rmap, rinv, xp, yp, dyp, dxp;
@@ -167,6 +168,7 @@ static void make_plan(tel_layer* L) {
     sc = 0;
     place(p.df, T * H * e, false, sv, sc);
     place(p.du, T * F * e, false, sv, sc);
+    if (gck) place(p.gck_g, T * F * e, false, sv, sc);
     place(p.dgemm, T * H * e, false, sv, sc);
     place(p.dres, T * H * f4, false, sv, sc);
     place(p.dres2, T * H * f4, false, sv, sc);
@@ -568,18 +570,21 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         return PR ? zero_padded_heads(dt, bs.of(p.dout), 1, L->B, L->NH, L->S, L->d, key_lengths, st) : hipSuccess;
     };
 
-    const void* g_src = gck ? bs.of(p.u) : bs.of(p.g);  // FFN2 input (or GELU input to recompute it from)
+    // FFN2 input: kept by the forward, or (gelu checkpoint) recomputed from u
+    // by the FFN2 input-gradient epilogue into scratch
+    const void* g_src = gck ? bs.of(p.gck_g) : bs.of(p.g);
 
     if (c.pre_ln) {
         // y = x1 + drop2(g W2^T + b2)
         HIP_TRY(dropout_apply(dt, dyin, bs.of(p.df), (size_t)T * H, d2, st, rmap, H));
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
+        if (gck) g.ea.out2 = bs.of(p.gck_g);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, gck},
+        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, false},
                        TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, G->b_1, false});
         if (s != TEL_OK) return s;
         // x1 -> LN2: dx1 = dy + LN2'(da2); dz = drop1(dx1)
@@ -635,11 +640,12 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
+        if (gck) g.ea.out2 = bs.of(p.gck_g);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, gck},
+        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, false},
                        TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, G->b_1, false});
         if (s != TEL_OK) return s;
         // x1 = LN1(z1): dz1 = LN1'(dgemm + dz2); dz = drop1(dz1)
