@@ -1055,9 +1055,8 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
 // Deterministic split-K reduction: out[m][n] = sum_z ws[z][m][n] in z order.
 // The first M/4 threads also add the per-split row sums (bias gradients).
 template <typename T>
-__global__ void splitk_reduce_kernel(const float* ws, int splits, int M, int N, EpiArgs ea, const float* rs_part,
-                                     T* rs_out) {
-    const size_t i4 = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+__device__ __forceinline__ void splitk_reduce_body(size_t i4, const float* ws, int splits, int M, int N,
+                                                   const EpiArgs& ea, const float* rs_part, T* rs_out) {
     const size_t MN = (size_t)M * N;
     if (rs_out && i4 < (size_t)M) {
         float r[4] = {0, 0, 0, 0};
@@ -1079,6 +1078,30 @@ __global__ void splitk_reduce_kernel(const float* ws, int splits, int M, int N, 
     }
     const int m = (int)(i4 / N), n = (int)(i4 - (size_t)m * N);
     epilogue4<T, EPI_STORE>(ea, m, n, v);
+}
+
+template <typename T>
+__global__ void splitk_reduce_kernel(const float* ws, int splits, int M, int N, EpiArgs ea, const float* rs_part,
+                                     T* rs_out) {
+    splitk_reduce_body<T>(((size_t)blockIdx.x * blockDim.x + threadIdx.x) * 4, ws, splits, M, N, ea, rs_part, rs_out);
+}
+
+// The reductions of a weight-gradient pair in one launch (a launch of this
+// size costs about its own fixed overhead): blocks below `blocks0` reduce the
+// first GEMM, the rest the second.
+struct ReduceJob {
+    const float* ws;
+    int M, N;
+    EpiArgs ea;
+    const float* rs_part;
+    void* rs_out;
+};
+template <typename T>
+__global__ void splitk_reduce_pair_kernel(ReduceJob a, ReduceJob b, int splits, unsigned blocks0) {
+    const bool second = blockIdx.x >= blocks0;
+    const ReduceJob& j = second ? b : a;
+    const size_t i4 = ((size_t)(blockIdx.x - (second ? blocks0 : 0u)) * blockDim.x + threadIdx.x) * 4;
+    splitk_reduce_body<T>(i4, j.ws, splits, j.M, j.N, j.ea, j.rs_part, reinterpret_cast<T*>(j.rs_out));
 }
 
 // ------------------------------------------------------------------ SIMT path
@@ -1362,9 +1385,16 @@ static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStre
     hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || splits == 1) return e;
-    e = splitk_reduce<T>(a, splits, ws_a, st);
-    if (e != hipSuccess) return e;
-    return splitk_reduce<T>(b, splits, ws_b, st);
+    auto job = [&](const GemmDesc& g, const float* ws) {
+        const bool rsum = g.rowsum_out != nullptr;  // fused row sums (A is m-major here)
+        return ReduceJob{ws, g.M, g.N, g.ea, rsum ? ws + (size_t)splits * g.M * g.N : nullptr,
+                         rsum ? g.rowsum_out : nullptr};
+    };
+    const unsigned blocks0 = (unsigned)(((size_t)a.M * a.N / 4 + 255) / 256);
+    const unsigned blocks1 = (unsigned)(((size_t)b.M * b.N / 4 + 255) / 256);
+    hipLaunchKernelGGL(splitk_reduce_pair_kernel<T>, dim3(blocks0 + blocks1), dim3(256), 0, st, job(a, ws_a),
+                       job(b, ws_b), splits, blocks0);
+    return hipGetLastError();
 }
 
 hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
