@@ -172,6 +172,25 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
                 }
             }
         }
+        // Dropout keep bits: lanes 2j and 2j+1 hold the two halves of one
+        // 8-column Philox block of each of the two rows, so each draws the
+        // block of one row and they swap halves (one Philox call per 8
+        // elements).  Every lane draws, before any row or column is skipped.
+        uint32_t kn[2][NC];
+        if constexpr (DROP) {
+            if (a.drop.thr) {
+                const int odd = lane & 1;
+                const int urow = min(row0 + rr + odd, a.T - 1);  // the row this lane draws for
+                const size_t tok = a.row_map ? (size_t)max(a.row_map[urow], 0) : (size_t)urow;
+#pragma unroll
+                for (int c = 0; c < NC; ++c) {
+                    const uint32_t k8 = keep8(a.drop.rng, (tok * H + c * 256 + (lane & ~1) * 4) >> 3, a.drop.thr);
+                    const uint32_t o8 = __shfl_xor(k8, 1, 64);
+                    kn[0][c] = odd ? (o8 >> 4) : (k8 & 0xFu);
+                    kn[1][c] = odd ? (k8 >> 4) : (o8 & 0xFu);
+                }
+            }
+        }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int row = row0 + rr + u;
@@ -192,8 +211,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
                 store4k<T, OUT_F32>(a.out, base + idx, dx);
                 if constexpr (DROP) {
                     if (a.drop.thr) {
-                        const size_t tok = a.row_map ? (size_t)max(a.row_map[row], 0) : (size_t)row;
-                        const uint32_t k = keep4(a.drop.rng, (tok * H + idx) >> 2, a.drop.thr);
+                        const uint32_t k = kn[u][c];
 #pragma unroll
                         for (int i = 0; i < 4; ++i) dx[i] = ((k >> i) & 1u) ? dx[i] * a.drop.scale : 0.0f;
                     }
