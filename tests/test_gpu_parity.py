@@ -74,6 +74,22 @@ def test_small_lowp_d32_simt_attention(dtype):
     _run(w)
 
 
+def test_max_hidden_head128():
+    # the largest hidden width the layer accepts (2048: eight 256-column
+    # groups per LayerNorm lane) with 128-wide heads (generic attention
+    # kernel at its largest head width).  fp16: in bf16 the output error at
+    # this width is bf16's rounding (8x fp16's, 3 fewer mantissa bits) and
+    # reaches the 2e-2 output bound itself.
+    w = syn.Workload("h2048", 2, 64, 2048, 16, 4096, True, "f16", 0.1, 0.1, 17, lengths=(20, 64))
+    _run(w, step=2)
+
+
+def test_hidden1536_postln():
+    # hidden 1536: six 256-column groups per LayerNorm lane; 24 heads of 64
+    w = syn.Workload("h1536", 2, 128, 1536, 24, 2048, False, "bf16", 0.1, 0.1, 19, lengths=(40, 128))
+    _run(w)
+
+
 # ------------------------------------------------------------------ masks
 @pytest.mark.parametrize("site", [0, 1, 2])
 def test_dropout_masks_bitexact(site):
