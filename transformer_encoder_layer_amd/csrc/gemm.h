@@ -73,8 +73,23 @@ bool gemm_rowsum_fused(const GemmDesc& g);
 // (splitk_ws, splitk_ws_elems) holds the partials of both.  Row sums are
 // fused as in gemm_launch.  gemm_group_ok tells whether the pair qualifies;
 // gemm_launch_group returns hipErrorInvalidValue (launching nothing) if not.
+//
+// Column sums that only need to be done by the end of the launch (the
+// LayerNorm gamma/beta gradients: out[n] = sum_p part[p][n] of fp32 [P][N]
+// partial rows, out in the GEMM dtype) can ride along: they run as extra
+// workgroups of the launch that reduces the split-K partials (or of a launch
+// of their own when the pair needs no reduction), summed in the same fixed
+// order as the standalone LayerNorm finalize, so the results are the same
+// bits either way.
+struct ColsumJob {
+    const float* part;
+    int P, N;
+    void* out;
+};
+constexpr int kMaxColsumJobs = 4;
 bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b);
-hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t stream);
+hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t stream,
+                             const ColsumJob* colsums = nullptr, int n_colsums = 0);
 // Workspace elements gemm_launch_group needs for the pair (0: none).
 size_t gemm_splitk_group_elems(const GemmDesc& a, const GemmDesc& b);
 

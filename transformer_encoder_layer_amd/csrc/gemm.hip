@@ -1096,11 +1096,29 @@ struct ReduceJob {
     const float* rs_part;
     void* rs_out;
 };
+struct ColsumJobs {
+    ColsumJob j[kMaxColsumJobs];
+    int n;
+    int blocks;  // workgroups per job: (N + 7) / 8 of the widest job
+};
+// The first cs.n * cs.blocks workgroups each sum 8 columns of one
+// column-sum job (first, so that their latency-bound loads overlap the
+// reduction); then blocks0 workgroups reduce problem a and the rest problem b.
 template <typename T>
-__global__ void splitk_reduce_pair_kernel(ReduceJob a, ReduceJob b, int splits, unsigned blocks0) {
-    const bool second = blockIdx.x >= blocks0;
+__global__ __launch_bounds__(256) void splitk_reduce_pair_kernel(ReduceJob a, ReduceJob b, int splits,
+                                                                 unsigned blocks0, ColsumJobs cs) {
+    const unsigned extra = (unsigned)(cs.n * cs.blocks);
+    if (blockIdx.x < extra) {
+        __shared__ float red[32][9];
+        const int job = (int)(blockIdx.x / (unsigned)cs.blocks), n0 = (int)(blockIdx.x % (unsigned)cs.blocks) * 8;
+        const ColsumJob& c = cs.j[job];
+        if (n0 < c.N) colsum8_block<T>(c.part, c.P, c.N, reinterpret_cast<T*>(c.out), n0, red);  // block-uniform
+        return;
+    }
+    const unsigned bid = blockIdx.x - extra;
+    const bool second = bid >= blocks0;
     const ReduceJob& j = second ? b : a;
-    const size_t i4 = ((size_t)(blockIdx.x - (second ? blocks0 : 0u)) * blockDim.x + threadIdx.x) * 4;
+    const size_t i4 = ((size_t)(bid - (second ? blocks0 : 0u)) * blockDim.x + threadIdx.x) * 4;
     splitk_reduce_body<T>(i4, j.ws, splits, j.M, j.N, j.ea, j.rs_part, reinterpret_cast<T*>(j.rs_out));
 }
 
@@ -1366,7 +1384,7 @@ bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b) {
 }
 
 template <typename T>
-static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
+static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJobs& cs) {
     constexpr int BM = 256, BN = 256;
     const int splits = group_splits(a, b);
     auto kern = gemm_dl4_kernel<T, BM, BN, false, false, EPI_STORE>;
@@ -1384,7 +1402,13 @@ static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStre
     const int gx = std::min(G.units, std::max(8, slots / 8 * 8));
     hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
+    if (e != hipSuccess || (splits == 1 && cs.n == 0)) return e;
+    const unsigned extra = (unsigned)(cs.n * cs.blocks);
+    if (splits == 1) {  // no partials to reduce: the column sums alone
+        hipLaunchKernelGGL(splitk_reduce_pair_kernel<T>, dim3(extra), dim3(256), 0, st, ReduceJob{}, ReduceJob{}, 1,
+                           0u, cs);
+        return hipGetLastError();
+    }
     auto job = [&](const GemmDesc& g, const float* ws) {
         const bool rsum = g.rowsum_out != nullptr;  // fused row sums (A is m-major here)
         return ReduceJob{ws, g.M, g.N, g.ea, rsum ? ws + (size_t)splits * g.M * g.N : nullptr,
@@ -1392,16 +1416,26 @@ static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStre
     };
     const unsigned blocks0 = (unsigned)(((size_t)a.M * a.N / 4 + 255) / 256);
     const unsigned blocks1 = (unsigned)(((size_t)b.M * b.N / 4 + 255) / 256);
-    hipLaunchKernelGGL(splitk_reduce_pair_kernel<T>, dim3(blocks0 + blocks1), dim3(256), 0, st, job(a, ws_a),
-                       job(b, ws_b), splits, blocks0);
+    hipLaunchKernelGGL(splitk_reduce_pair_kernel<T>, dim3(extra + blocks0 + blocks1), dim3(256), 0, st, job(a, ws_a),
+                       job(b, ws_b), splits, blocks0, cs);
     return hipGetLastError();
 }
 
-hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st) {
-    if (!gemm_group_ok(a, b)) return hipErrorInvalidValue;
+hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJob* colsums,
+                             int n_colsums) {
+    if (!gemm_group_ok(a, b) || n_colsums < 0 || n_colsums > kMaxColsumJobs || (n_colsums && !colsums))
+        return hipErrorInvalidValue;
+    ColsumJobs cs{};
+    cs.n = n_colsums;
+    for (int i = 0; i < n_colsums; ++i) {
+        const ColsumJob& c = colsums[i];
+        if (!c.part || !c.out || c.P <= 0 || c.N <= 0) return hipErrorInvalidValue;
+        cs.j[i] = c;
+        cs.blocks = std::max(cs.blocks, (c.N + 7) / 8);
+    }
     switch (a.dtype) {
-        case 1: return launch_dl4_group<f16>(a, b, st);
-        case 2: return launch_dl4_group<bf16>(a, b, st);
+        case 1: return launch_dl4_group<f16>(a, b, st, cs);
+        case 2: return launch_dl4_group<bf16>(a, b, st, cs);
     }
     return hipErrorInvalidValue;
 }

@@ -234,36 +234,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
     }
 }
 
-// out_v[n] = sum_p part_v[p][n] for up to two vectors v (blockIdx.y): 8
-// columns x 32 row phases per workgroup; phase j sums rows j, j+32, ... in
-// order, then the 32 phase sums are added in order -- a fixed summation
-// order, independent of scheduling, with only P/32 dependent load rounds.
+// out_v[n] = sum_p part_v[p][n] for up to two vectors v (blockIdx.y), 8
+// columns per workgroup, in the fixed order of colsum8_block.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* part0, const float* part1, int P, int N,
                                                               T* out0, T* out1) {
     __shared__ float red[32][9];
-    const float* part = blockIdx.y ? part1 : part0;
-    T* out = blockIdx.y ? out1 : out0;
-    const int cl = threadIdx.x & 7, ph = threadIdx.x >> 3;
-    const int n = blockIdx.x * 8 + cl;
-    float s = 0.0f;
-    if (n < N) {
-        int p = ph;
-        for (; p + 96 < P; p += 128) {
-            const float a0 = part[(size_t)p * N + n], a1 = part[(size_t)(p + 32) * N + n];
-            const float a2 = part[(size_t)(p + 64) * N + n], a3 = part[(size_t)(p + 96) * N + n];
-            s += a0; s += a1; s += a2; s += a3;
-        }
-        for (; p < P; p += 32) s += part[(size_t)p * N + n];
-    }
-    red[ph][cl] = s;
-    __syncthreads();
-    if (ph == 0 && n < N) {
-        float t = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) t += red[j][cl];
-        out[n] = from_f<T>(t);
-    }
+    colsum8_block<T>(blockIdx.y ? part1 : part0, P, N, blockIdx.y ? out1 : out0, blockIdx.x * 8, red);
 }
 
 constexpr int CS_ROWS = 64;  // rows per partial in colsum_partial

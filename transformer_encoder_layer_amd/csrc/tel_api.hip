@@ -68,7 +68,7 @@ struct Plan {
     // scratch (backward)
     Buf df, du, dgemm, dres, dz, dout, dvec, dqkv, dres2;
     Buf gck_g;    // GELU(u) recomputed in the backward under gelu checkpointing
-    Buf part_ln, part_col, splitk;
+    Buf part_ln, part_ln2, part_col, splitk;
     // token packing: row maps and x packed (saved); y, dy, dx packed (scratch)
     Buf rmap, rinv, xp, yp, dyp, dxp;
     size_t saved_bytes = 0, scratch_bytes = 0;
@@ -181,7 +181,9 @@ static void make_plan(tel_layer* L) {
         place(p.dxp, T * H * e, false, sv, sc);
     }
     const size_t maxN = 3 * H > F ? 3 * H : F;
+    // gamma/beta partial rows of LN1 and LN2 (both are finalized at the end)
     place(p.part_ln, 2 * (size_t)ln_backward_parts(L->T) * H * f4, false, sv, sc);
+    place(p.part_ln2, 2 * (size_t)ln_backward_parts(L->T) * H * f4, false, sv, sc);
     place(p.part_col, (size_t)colsum_parts(L->T) * maxN * f4, false, sv, sc);
     // split-K partials of the four weight-gradient GEMMs
     size_t sk = 0;
@@ -485,9 +487,13 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
     const bool inv = c.normalize_invertible != 0;
     const bool gck = c.gelu_checkpoint != 0;
-    float* part_ln_g = (float*)bs.of(p.part_ln);
+    // LN1's and LN2's gamma/beta partial rows (separate buffers: both are
+    // finalized at the end, with the last weight-gradient pair when it runs)
     const int lnP = ln_backward_parts(T);
-    float* part_ln_b = part_ln_g + (size_t)lnP * H;
+    float* part_ln1_g = (float*)bs.of(p.part_ln);
+    float* part_ln1_b = part_ln1_g + (size_t)lnP * H;
+    float* part_ln2_g = (float*)bs.of(p.part_ln2);
+    float* part_ln2_b = part_ln2_g + (size_t)lnP * H;
     float* part_col = (float*)bs.of(p.part_col);
     const int colP = colsum_parts(T);
     float* skws = p.splitk.used ? (float*)bs.of(p.splitk) : nullptr;
@@ -537,19 +543,46 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     // Two weight gradients: one grouped launch when both qualify (the tiles
     // of both fill the chip with fewer k-splits), else one after the other.
     // A profiled kernel id always runs alone, so its events cover only it.
-    auto wgrad_pair = [&](int ka, const Wg& a, int kb, const Wg& b) -> tel_status {
+    // Two weight gradients run as one grouped launch when both qualify (the
+    // tiles of both fill the chip with fewer k-splits), else one after the
+    // other.  A profiled kernel id always runs alone, so its events cover
+    // only it.
+    auto grouped = [&](int ka, const Wg& a, int kb, const Wg& b) {
         const GemmDesc ga = wdesc(a), gb = wdesc(b);
         const bool alone = L->prof_kernel == ka || L->prof_kernel == kb;
-        if (!alone && ga.rowsum_out && gb.rowsum_out && gemm_group_ok(ga, gb)) {
-            HIP_TRY(gemm_launch_group(ga, gb, st));
-            return TEL_OK;
-        }
-        TIMED(ka, wgrad1(a));
-        TIMED(kb, wgrad1(b));
-        return TEL_OK;
+        return !alone && ga.rowsum_out && gb.rowsum_out && gemm_group_ok(ga, gb);
     };
-    auto ln_grads = [&](void* gg, void* gb) -> hipError_t {
-        return colsum_finalize2(dt, part_ln_g, part_ln_b, lnP, H, gg, gb, st);
+    // The LayerNorm gamma/beta finalizes (fixed-order column sums of the
+    // partial rows): when the last pair (W_o with W_qkv, the end of the
+    // backward) runs grouped, they wait for it and ride with its reduction
+    // launch; otherwise each runs right after its LayerNorm backward.
+    const bool fold_ln = grouped(TEL_K_OUT_WGRAD, Wg{nullptr, nullptr, H, H, G->w_o, G->b_o, false},
+                                 TEL_K_QKV_WGRAD, Wg{nullptr, nullptr, 3 * H, H, G->w_qkv, G->b_qkv, false});
+    ColsumJob ln_fin[kMaxColsumJobs];
+    int n_ln_fin = 0;
+    auto ln_grads = [&](const float* pg, const float* pb, void* gg, void* gb) -> hipError_t {
+        if (!fold_ln) return colsum_finalize2(dt, pg, pb, lnP, H, gg, gb, st);
+        ln_fin[n_ln_fin++] = ColsumJob{pg, lnP, H, gg};
+        ln_fin[n_ln_fin++] = ColsumJob{pb, lnP, H, gb};
+        return hipSuccess;
+    };
+    // with_ln: the last pair, which takes the pending LayerNorm finalizes
+    auto wgrad_pair = [&](int ka, const Wg& a, int kb, const Wg& b, bool with_ln) -> tel_status {
+        const GemmDesc ga = wdesc(a), gb = wdesc(b);
+        if (grouped(ka, a, kb, b)) {
+            HIP_TRY(gemm_launch_group(ga, gb, st, with_ln ? ln_fin : nullptr, with_ln ? n_ln_fin : 0));
+            if (with_ln) n_ln_fin = 0;
+        } else {
+            TIMED(ka, wgrad1(a));
+            TIMED(kb, wgrad1(b));
+        }
+        if (with_ln) {
+            for (int i = 0; i < n_ln_fin; i += 2)
+                HIP_TRY(colsum_finalize2(dt, ln_fin[i].part, ln_fin[i + 1].part, lnP, H, ln_fin[i].out,
+                                         ln_fin[i + 1].out, st));
+            n_ln_fin = 0;
+        }
+        return TEL_OK;
     };
 
     AttnArgs aa{};
@@ -585,7 +618,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
         s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, false},
-                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, G->b_1, false});
+                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, G->b_1, false}, false);
         if (s != TEL_OK) return s;
         // x1 -> LN2: dx1 = dy + LN2'(da2); dz = drop1(dx1)
         LnBwdArgs lb{};
@@ -597,9 +630,9 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.res = dyin; lb.res_f32 = 0;
         lb.out = bs.of(p.dres); lb.out_f32 = 1;
         lb.drop_out = bs.of(p.dz); lb.drop = d1;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
+        lb.part_g = part_ln2_g; lb.part_b = part_ln2_b; lb.row_map = rmap;
         TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
-        HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
+        HIP_TRY(ln_grads(part_ln2_g, part_ln2_b, G->ln2_g, G->ln2_b));
         // out-projection
         g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
         g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
@@ -610,10 +643,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o, false},
-                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, G->b_qkv, false});
-        if (s != TEL_OK) return s;
-        // x -> LN1: dx = dx1 + LN1'(da1)
+        // x -> LN1: dx = dx1 + LN1'(da1) (ahead of the weight gradients, which
+        // do not need it, so that its finalize can ride with their reduction)
         lb = LnBwdArgs{};
         lb.dtype = dt; lb.T = T; lb.H = H;
         lb.dout = bs.of(p.dgemm);
@@ -622,9 +653,13 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
         lb.res = bs.of(p.dres); lb.res_f32 = 1;
         lb.out = dxout; lb.out_f32 = 0;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
+        lb.part_g = part_ln1_g; lb.part_b = part_ln1_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
-        HIP_TRY(ln_grads(G->ln1_g, G->ln1_b));
+        HIP_TRY(ln_grads(part_ln1_g, part_ln1_b, G->ln1_g, G->ln1_b));
+        s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o, false},
+                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, G->b_qkv, false},
+                       true);
+        if (s != TEL_OK) return s;
     } else {
         // y = LN2(z2): dz2 = LN2'(dy); df = drop2(dz2)
         LnBwdArgs lb{};
@@ -635,9 +670,9 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
         lb.out = bs.of(p.dres2); lb.out_f32 = 1;
         lb.drop_out = bs.of(p.df); lb.drop = d2;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
+        lb.part_g = part_ln2_g; lb.part_b = part_ln2_b; lb.row_map = rmap;
         TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
-        HIP_TRY(ln_grads(G->ln2_g, G->ln2_b));
+        HIP_TRY(ln_grads(part_ln2_g, part_ln2_b, G->ln2_g, G->ln2_b));
         GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         if (gck) g.ea.out2 = bs.of(p.gck_g);
@@ -646,7 +681,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
         s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, false},
-                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, G->b_1, false});
+                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, G->b_1, false}, false);
         if (s != TEL_OK) return s;
         // x1 = LN1(z1): dz1 = LN1'(dgemm + dz2); dz = drop1(dz1)
         lb = LnBwdArgs{};
@@ -657,9 +692,9 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
         lb.out = bs.of(p.dres); lb.out_f32 = 1;
         lb.drop_out = bs.of(p.dz); lb.drop = d1;
-        lb.part_g = part_ln_g; lb.part_b = part_ln_b; lb.row_map = rmap;
+        lb.part_g = part_ln1_g; lb.part_b = part_ln1_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
-        HIP_TRY(ln_grads(G->ln1_g, G->ln1_b));
+        HIP_TRY(ln_grads(part_ln1_g, part_ln1_b, G->ln1_g, G->ln1_b));
         g = dgrad(bs.of(p.dz), P->w_o, H, H, EPI_HEADSPLIT);
         g.ea.out = bs.of(p.dout); g.ea.B = L->B; g.ea.S = L->S; g.ea.H = H; g.ea.NH = L->NH; g.ea.d = L->d;
         HIP_TRY(zero_dout());
@@ -670,7 +705,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g.ea.out = dxout; g.ea.ldo = H; g.ea.res = bs.of(p.dres);
         TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
         s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o, false},
-                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), xin, 3 * H, H, G->w_qkv, G->b_qkv, false});
+                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), xin, 3 * H, H, G->w_qkv, G->b_qkv, false}, true);
         if (s != TEL_OK) return s;
     }
     if (PR) HIP_TRY(scatter_rows(dt, dxout, dx, rinv, L->T, H, st));

@@ -165,6 +165,37 @@ struct Drop {
     float scale;  // 1/(1-p) rounded to fp32
 };
 
+// ---------------------------------------------------------------- column sums
+// out[n] = sum_p part[p][n] (fp32 [P][N] partial rows) for the 8 columns
+// n0 .. n0+7, by one 256-thread block: thread (phase j = tid / 8, column
+// tid % 8) adds rows j, j+32, ... in order, then the 32 phase sums are added
+// in order -- a fixed summation order, independent of scheduling, with only
+// P/128 dependent load rounds.  red: 32 x 9 floats of LDS; every thread of
+// the block must call it.
+template <typename T>
+__device__ __forceinline__ void colsum8_block(const float* part, int P, int N, T* out, int n0, float (*red)[9]) {
+    const int cl = threadIdx.x & 7, ph = threadIdx.x >> 3;
+    const int n = n0 + cl;
+    float s = 0.0f;
+    if (n < N) {
+        int p = ph;
+        for (; p + 96 < P; p += 128) {
+            const float a0 = part[(size_t)p * N + n], a1 = part[(size_t)(p + 32) * N + n];
+            const float a2 = part[(size_t)(p + 64) * N + n], a3 = part[(size_t)(p + 96) * N + n];
+            s += a0; s += a1; s += a2; s += a3;
+        }
+        for (; p < P; p += 32) s += part[(size_t)p * N + n];
+    }
+    red[ph][cl] = s;
+    __syncthreads();
+    if (ph == 0 && n < N) {
+        float t = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) t += red[j][cl];
+        out[n] = from_f<T>(t);
+    }
+}
+
 // ---------------------------------------------------------------- GELU
 // Exact GELU u*Phi(u) and its derivative Phi(u) + u*phi(u) (AI-infra blog,
 // section 2.3: the erf form, not the tanh approximation).  Phi comes from
