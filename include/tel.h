@@ -192,7 +192,10 @@ enum {
  * start_events[i % count] and stop_events[i % count] (hipEvent_t handles the
  * caller created), i counting the launches since this call.  The arrays are
  * borrowed until the hook is disabled with kernel_id < 0.  Results are
- * unchanged. */
+ * unchanged, except that a weight-gradient pair that otherwise runs as one
+ * grouped launch runs as two launches while one of its ids is profiled: those
+ * two weight gradients and their bias gradients may then take another k-split
+ * and round differently (every other output keeps its bits). */
 tel_status tel_debug_kernel_events(tel_layer* layer, int kernel_id, void** start_events, void** stop_events,
                                    int count);
 

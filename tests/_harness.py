@@ -31,11 +31,27 @@ def prepare(w: syn.Workload, layer=0, random_affine=False, weight_scale=1.0):
     return dict(params_t=params_t, params_r=params_r, x_t=x_t, x_r=x_r, dy_t=dy_t, dy_r=dy_r, lengths=lengths)
 
 
+def _hip_events(n):
+    """n HIP events (handles) from the runtime, for the kernel-event hook."""
+    import ctypes
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    out = []
+    for _ in range(n):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        out.append(e.value)
+    return hip, out
+
+
 def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=None, switches=None,
-              device="cuda", backward=True, use_lengths=True, pack=False):
+              device="cuda", backward=True, use_lengths=True, pack=False, prof_kernel=None):
     """Run forward (+ backward) through the C ABI.  dy_rows: optional boolean
     mask over sequences; dy is zeroed for the others.  pack: token packing
-    (the valid-token count is declared from the lengths).  Returns fp64 numpy."""
+    (the valid-token count is declared from the lengths).  prof_kernel: a
+    kernel id whose launches the kernel-event hook brackets during the
+    backward.  Returns fp64 numpy."""
     import torch
     from transformer_encoder_layer_amd import binding as B
     from transformer_encoder_layer_amd.layer import LayerConfig
@@ -68,8 +84,17 @@ def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=
         if backward:
             dx = torch.empty_like(x)
             G = {n: torch.empty_like(P[n]) for n in NAMES}
+            hook = None
+            if prof_kernel is not None:
+                hip, ev = _hip_events(2)
+                hook = B.tel_debug_kernel_events(h, prof_kernel, ev[:1], ev[1:])
             B.tel_layer_backward(h, B.make_params(P), x, lens, training, step, dy, saved, scratch, dx,
                                  B.make_grads(G))
+            torch.cuda.synchronize()
+            if hook is not None:
+                B.tel_debug_kernel_events(h, -1, None, None)
+                for e in ev:
+                    hip.hipEventDestroy(e)
             out["dx"] = dx
             out.update({"g_" + n: G[n] for n in NAMES})
         torch.cuda.synchronize()
