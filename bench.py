@@ -135,7 +135,7 @@ def main():
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--layers", type=int, default=0, help="override the stack depth")
     ap.add_argument("--kernel", default="ffn1_fwd", help="kernel timed for the roofline")
-    ap.add_argument("--cpu-seqs", type=int, default=16, help="sequences in the oracle sample")
+    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle sample (BERT-Large: the whole batch, about 10 s on 16 host threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pack", action="store_true",
                     help="token packing: run the layers on the valid tokens of a padded workload")
