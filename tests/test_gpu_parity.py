@@ -215,6 +215,16 @@ def test_full_bert_large_layer():
     _sampled("bert_large", [0, 63])
 
 
+def test_full_bert_large_shape_postln():
+    # Post-LN at the BERT-Large shapes, where the last weight-gradient pair
+    # runs grouped and both LayerNorm gamma/beta sums (LN2's from the first
+    # backward kernel on) ride with its reduction
+    w = syn.WORKLOADS["bert_large"].with_(pre_ln=False)
+    rows = np.zeros(w.batch, dtype=bool)
+    rows[[9, 40]] = True
+    _run(w, batches=[9, 40], dy_rows=rows, layer_id=5, step=3, random_affine=True)
+
+
 def test_full_bert_large_layer23():
     w = syn.WORKLOADS["bert_large"]
     rows = np.zeros(w.batch, dtype=bool)
