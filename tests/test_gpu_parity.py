@@ -203,6 +203,16 @@ def test_packed_tokens_bert_base_postln():
     _run_packed(w, batches=[0, 31], dy_rows=rows, random_affine=False)
 
 
+def test_packed_tokens_bert_large_shape():
+    # BERT-Large shapes with padding: the packed rows (valid tokens rounded up
+    # to 256) are the k of the weight gradients, which still run as grouped
+    # pairs, the last one also summing the LayerNorm gamma/beta partials
+    w = syn.WORKLOADS["bert_large"].with_(lengths=(64, 128))
+    rows = np.zeros(w.batch, dtype=bool)
+    rows[[3, 50]] = True
+    _run_packed(w, batches=[3, 50], dy_rows=rows, step=1, layer_id=2)
+
+
 # ------------------------------------------------------------------ full-size workloads, sampled
 def _sampled(name, batches, **over):
     w = syn.WORKLOADS[name].with_(**over)
