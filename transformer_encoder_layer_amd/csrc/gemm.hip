@@ -1296,7 +1296,9 @@ template <bool AK>
 static GemmParams dl4_params(const GemmDesc& g, int splits, float* ws) {
     float* rs_part = splits > 1 ? ws + (size_t)splits * g.M * g.N : nullptr;
     void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
-    return GemmParams{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, ws, rsum};
+    // k tiles per split rounded up: the last split may be shorter
+    const int kps = (g.K / QKT + splits - 1) / splits * QKT;
+    return GemmParams{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, kps, g.ea, ws, rsum};
 }
 
 // Resident workgroups of a dl4 instantiation on the device (0 on failure).
@@ -1354,20 +1356,41 @@ static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
 // Two weight gradients in one launch (256x256 tiles, A and B m/n-major,
 // plain store with fused row sums): the split count fills the chip with the
 // tiles of both; partials of the second follow those of the first in ws.
+// Split count of a pair on 256x256 tiles, one workgroup per CU.  Its cost is
+// modelled as the waves of 256 units times the k tiles of the longest unit
+// (the critical path), plus the split-K partials the reduction reads (one
+// 256x256x64 k tile, ~2 us at the sustained rate, against ~0.7 ps per fp32
+// partial element): the cheapest count in 1..8 wins.  Splits may be unequal
+// (k tiles rounded up per split) so that shapes in multiples of 768 fill
+// whole waves (BERT-Base: 72 tiles x 7 splits = 504 units); every split
+// keeps at least 8 k tiles.  0: the pair does not fit.
 static int group_splits(const GemmDesc& a, const GemmDesc& b) {
     auto ok = [](const GemmDesc& g) {
         return g.dtype != 0 && !g.a_kmajor && !g.b_kmajor && !g.b_gelu && g.epi == EPI_STORE &&
                g.M % 256 == 0 && g.N % 256 == 0 && g.K % QKT == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
     };
     if (!ok(a) || !ok(b) || a.dtype != b.dtype) return 0;
-    // one workgroup per CU: the largest split count (<= 4) whose units fit
-    // one wave of 256, and only if that wave is at least three quarters full
     const int tiles = (a.M / 256) * (a.N / 256) + (b.M / 256) * (b.N / 256);
-    int s = 1;
-    while (tiles * s * 2 <= 256 && s < 4) s *= 2;
-    // every split keeps at least 8 k tiles
-    while (s > 1 && (a.K % (s * QKT) || b.K % (s * QKT) || a.K / (s * QKT) < 8 || b.K / (s * QKT) < 8)) s /= 2;
-    return tiles * s >= 192 && tiles * s <= 256 ? s : 0;
+    const double elems = (double)a.M * a.N + (double)b.M * b.N;
+    auto splits_fit = [](int K, int s) {  // every split of K gets >= 8 k tiles
+        const int kt = K / QKT, per = (kt + s - 1) / s;
+        return per >= 8 && kt - (s - 1) * per >= 8;
+    };
+    int best = 0;
+    double best_cost = 0.0;
+    for (int s = 1; s <= 8; ++s) {
+        if (!splits_fit(a.K, s) || !splits_fit(b.K, s)) continue;
+        const int waves = (tiles * s + 255) / 256;
+        const int per = (std::max(a.K, b.K) / QKT + s - 1) / s;
+        const double cost = (double)waves * per + (s > 1 ? s * elems * 3.2e-7 : 0.0);
+        if (!best || cost < best_cost) {
+            best = s;
+            best_cost = cost;
+        }
+    }
+    // a pair that would leave over a quarter of the chip idle runs apart
+    if (!best || (double)tiles * best / (((tiles * best + 255) / 256) * 256) < 0.75) return 0;
+    return best;
 }
 
 size_t gemm_splitk_group_elems(const GemmDesc& a, const GemmDesc& b) {
