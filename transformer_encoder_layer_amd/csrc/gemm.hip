@@ -350,10 +350,16 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& p, f32x16 (
     constexpr int GPR = WN / 4;           // 4-column groups per row
     constexpr int RPI = 64 / GPR;         // rows per lane-iteration
     constexpr int NIT = 32 / RPI;         // lane-iterations per block
+    // lanes in use: all 64 unless GPR does not divide 64 (WN = 96: 48 lanes
+    // cover two rows of 24 groups; the other 16 follow row 0's addresses and
+    // store nothing)
+    constexpr int LANES = RPI * GPR;
+    static_assert(32 % RPI == 0, "whole lane-iterations per 32-row block");
     constexpr int BUDGET = EPI == EPI_BIAS_DROP_RES ? 64 : 128;  // dropout's Philox needs registers too
     constexpr int PBMAX = BUDGET / (NIT * 4) < 1 ? 1 : BUDGET / (NIT * 4);
     constexpr int PB = E::kElem ? (MI < PBMAX ? MI : PBMAX) : 1;
-    const int cg = lane % GPR, r0 = lane / GPR;
+    const bool lane_on = LANES == 64 || lane < LANES;
+    const int cg = lane % GPR, r0 = lane_on ? lane / GPR : 0;
     const int n = n0 + wn * WN + cg * 4;
     const int mrow0 = m0 + wm * WM + r0;  // this lane's first row of block 0
     float b[4] = {0, 0, 0, 0};
@@ -404,8 +410,12 @@ __device__ __forceinline__ void gemm_epilogue_impl(const GemmParams& p, f32x16 (
             float v[4] = {q.x, q.y, q.z, q.w};
             float r[4] = {0, 0, 0, 0};
             if constexpr (E::kElem) E::elem_from_raw(p.ea, el[i % PB][it], r);
-            if constexpr (EPI == EPI_BIAS_DROP_RES) E::finish_drop(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r, kn[it]);
-            else E::template finish<PK>(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
+            if (lane_on) {
+                if constexpr (EPI == EPI_BIAS_DROP_RES)
+                    E::finish_drop(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r, kn[it]);
+                else
+                    E::template finish<PK>(p.ea, m0 + wm * WM + i * 32 + rr, n, v, b, r);
+            }
         }
         if constexpr (E::kElem) {
             if (i + PB < MI) {
@@ -1200,6 +1210,16 @@ static TileCfg pick_tiles(const GemmDesc& g) {
     if (!g.a_kmajor && !g.b_kmajor && g.epi == EPI_STORE && g.splitk_ws && mfma_ok(g, 256, 256) &&
         (g.M / 256) * (g.N / 256) >= 64)
         return {256, 256};
+    // Forward projections (QKV head split, bias + dropout + residual):
+    // 256x192 tiles when their whole waves of 256 finish sooner than those of
+    // 256x128 tiles (a 256x192 tile is 1.5 times the work) -- widths in
+    // multiples of 768 (768 = 4 x 192, a 1.5-wave grid on 256x128 tiles)
+    if ((g.epi == EPI_QKV || g.epi == EPI_BIAS_DROP_RES) && g.a_kmajor && g.b_kmajor && mfma_ok(g, 256, 192) &&
+        mfma_ok(g, 256, 128)) {
+        const int w192 = ((g.M / 256) * (g.N / 192) + 255) / 256;
+        const int w128 = ((g.M / 256) * (g.N / 128) + 255) / 256;
+        if (3 * w192 < 2 * w128) return {256, 192};
+    }
     for (const TileCfg& c : cands) {
         if (!mfma_ok(g, c.BM, c.BN)) continue;
         const int tiles = (g.M / c.BM) * (g.N / c.BN);
@@ -1486,6 +1506,11 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
                 return launch_dl4<T, 256, 256, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
             else
                 return launch_dl<T, 256, 256, 2, 4, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+        }
+        if (c.BM == 256 && c.BN == 192) {
+            if constexpr ((EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES) && AK && BKM)
+                return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
+            return hipErrorNotSupported;
         }
         if (c.BM == 256 && c.BN == 128) {
             // the dropout epilogue's Philox work, like GELU's, favours two waves
