@@ -575,9 +575,20 @@ constexpr int DNS = 4;     // stages
 __device__ __forceinline__ int kmaj32_off(int row, int k) {
     return row * 32 + (((k >> 3) ^ ((row >> 2) & 3)) << 3) + (k & 7);
 }
+// Chunk swizzle of an m/n-major row k of R elements.  R a multiple of 128:
+// chunk ^ 4 (k & 3), so the four k rows of a transposing read (whose bases
+// fall on one bank) take four distinct 16-dword windows.  R = 192 (24 chunks,
+// rows 96 dwords apart: rows k and k+2 share banks): chunk ^ 4 ((k >> 1) & 1),
+// which keeps every chunk inside its aligned group of 8 and moves rows k+2
+// and k+3 16 dwords away from rows k and k+1.
+template <int R>
+__device__ __forceinline__ int mn_swz(int k) {
+    static_assert(R % 128 == 0 || R == 192, "m/n-major tile width");
+    return R % 128 == 0 ? 4 * (k & 3) : 4 * ((k >> 1) & 1);
+}
 template <int R>
 __device__ __forceinline__ int mn32_off(int k, int col) {
-    return k * R + (((col >> 3) ^ (4 * (k & 3))) << 3) + (col & 7);
+    return k * R + (((col >> 3) ^ mn_swz<R>(k)) << 3) + (col & 7);
 }
 
 // One wave-wide direct load: lane i copies the 16 bytes at sbase + voff to
@@ -618,7 +629,7 @@ struct DlPlan {
             } else {
                 constexpr int CPR = R / 8;
                 const int k = slot / CPR, p = slot % CPR;
-                const int ch = p ^ (4 * (k & 3));
+                const int ch = p ^ mn_swz<R>(k);
                 voff[j] = (uint32_t)((k * ld + ch * 8) * (int)sizeof(T));
             }
         }
@@ -866,7 +877,7 @@ struct Dl4Plan {
                 voff[j] = (uint32_t)((row * ld + c * 8) * (int)sizeof(T));
             } else {
                 constexpr int CPR = R / 8;
-                const int k = slot / CPR, ch = (slot % CPR) ^ (4 * (k & 3));
+                const int k = slot / CPR, ch = (slot % CPR) ^ mn_swz<R>(k);
                 voff[j] = (uint32_t)((k * ld + ch * 8) * (int)sizeof(T));
             }
         }
@@ -1210,12 +1221,14 @@ static TileCfg pick_tiles(const GemmDesc& g) {
     if (!g.a_kmajor && !g.b_kmajor && g.epi == EPI_STORE && g.splitk_ws && mfma_ok(g, 256, 256) &&
         (g.M / 256) * (g.N / 256) >= 64)
         return {256, 256};
-    // Forward projections (QKV head split, bias + dropout + residual):
-    // 256x192 tiles when their whole waves of 256 finish sooner than those of
-    // 256x128 tiles (a 256x192 tile is 1.5 times the work) -- widths in
-    // multiples of 768 (768 = 4 x 192, a 1.5-wave grid on 256x128 tiles)
-    if ((g.epi == EPI_QKV || g.epi == EPI_BIAS_DROP_RES) && g.a_kmajor && g.b_kmajor && mfma_ok(g, 256, 192) &&
-        mfma_ok(g, 256, 128)) {
+    // Projections (QKV head split, bias + dropout + residual) and input
+    // gradients (store, head split, residual add): 256x192 tiles when their
+    // whole waves of 256 finish sooner than those of 256x128 tiles (a 256x192
+    // tile is 1.5 times the work) -- widths in multiples of 768 (768 = 4 x
+    // 192, a 1.5-wave grid on 256x128 tiles)
+    const bool fwd192 = (g.epi == EPI_QKV || g.epi == EPI_BIAS_DROP_RES) && g.b_kmajor;
+    const bool dgrad192 = (g.epi == EPI_STORE || g.epi == EPI_HEADSPLIT || g.epi == EPI_ADD_RES) && !g.b_kmajor;
+    if ((fwd192 || dgrad192) && g.a_kmajor && mfma_ok(g, 256, 192) && mfma_ok(g, 256, 128)) {
         const int w192 = ((g.M / 256) * (g.N / 192) + 255) / 256;
         const int w128 = ((g.M / 256) * (g.N / 128) + 255) / 256;
         if (3 * w192 < 2 * w128) return {256, 192};
@@ -1509,6 +1522,8 @@ static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
         }
         if (c.BM == 256 && c.BN == 192) {
             if constexpr ((EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES) && AK && BKM)
+                return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
+            if constexpr ((EPI == EPI_STORE || EPI == EPI_HEADSPLIT || EPI == EPI_ADD_RES) && AK && !BKM)
                 return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
             return hipErrorNotSupported;
         }
