@@ -8,9 +8,12 @@ inputs, weights and workspaces are resident in HBM before timing starts.
 
 Reported: value = tokens/s of one layer's forward+backward (stack tokens/s
 times the number of layers run), model TFLOP/s and its fraction of the dense
-fp16 MFMA peak, the roofline of the dominant kernel (timed live with HIP
-events around each of its launches inside the timed steps), and the fp64
-CPU oracle's throughput on a bounded sample of the same workload.
+fp16 MFMA peak, per-step time percentiles, the roofline of the dominant
+kernel call site (the grouped W_2 + W_1 weight-gradient launch with its
+split-K reduction; timed live with HIP events around each of its launches
+inside the timed steps) and of the next two call sites by time (each timed on
+its own third of the layers), and the fp64 CPU oracle's throughput on a
+bounded sample of the same workload.
 """
 from __future__ import annotations
 
@@ -69,8 +72,20 @@ class Hip:
         self.h.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, n_seq: int):
-    """Oracle forward + backward of n_seq sequences of the workload (fp64, host cores)."""
+    """Oracle forward + backward of n_seq sequences of the workload (fp64, host
+    cores): one call that runs the forward and then the backward."""
     import oracle
     from transformer_encoder_layer_amd import synthetic as syn
     sub = w.with_(batch=n_seq)
@@ -81,16 +96,15 @@ def cpu_baseline(w, n_seq: int):
     cfg = oracle.LayerCfg(n_seq, w.seq, w.hidden, w.heads, w.ffn, pre_ln=w.pre_ln, training=True,
                           attn_p=float(np.float32(w.attn_p)), hidden_p=float(np.float32(w.hidden_p)),
                           seed=w.seed, step=0, layer_id=0)
-    oracle.lib()
+    threads = oracle.omp_threads()
     t0 = time.perf_counter()
-    oracle.layer_forward(cfg, p, x, lengths)
-    oracle.layer_backward(cfg, p, x, lengths, dy, ln_invertible=w.normalize_invertible)
+    oracle.layer_backward(cfg, p, x, lengths, dy, ln_invertible=w.normalize_invertible, want_y=True)
     dt = time.perf_counter() - t0
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": n_seq * w.seq / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+    return {"value": n_seq * w.seq / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"{n_seq} of {w.batch} sequences ({n_seq * w.seq} tokens), one layer forward+backward, "
                       f"fp64, {dt:.2f} s", "seconds": dt,
-            "model_gflops": model_flops(sub) / dt / 1e9}
+            "model_gflops": model_flops(sub) / dt / 1e9, "cpu_model": cpu_model(), "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)), "omp_threads": threads}
 
 
 COPY_BYTES = 1 << 30
@@ -134,7 +148,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--layers", type=int, default=0, help="override the stack depth")
-    ap.add_argument("--kernel", default="ffn1_fwd", help="kernel timed for the roofline")
+    ap.add_argument("--kernel", default="ffn_wgrad_pair", help="call site whose roofline is reported")
+    ap.add_argument("--also", default="ffn1_fwd,attn_wgrad_pair",
+                    help="further call sites timed (comma-separated), each on its own share of the layers")
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle sample (BERT-Large: the whole batch, about 10 s on 16 host threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pack", action="store_true",
@@ -154,7 +170,7 @@ def main():
         return
     from transformer_encoder_layer_amd import binding as B
     from transformer_encoder_layer_amd import synthetic as syn
-    from transformer_encoder_layer_amd.layer import LayerConfig
+    from transformer_encoder_layer_amd.layer import LayerConfig, pld_gates
 
     w = syn.WORKLOADS[args.workload]
     n_layers = args.layers or w.layers
@@ -194,7 +210,7 @@ def main():
     step_id = w.pld[2] if w.pld else 0
     if w.pld:
         theta = B.tel_pld_theta(step_id, w.pld[0], w.pld[1])
-        gates = [B.tel_pld_keep(w.seed, l, step_id, theta) for l in range(n_layers)]
+        gates = pld_gates(w.seed, n_layers, step_id, w.pld[0], w.pld[1])
     else:
         theta, gates = 1.0, [True] * n_layers
     run = [l for l in range(n_layers) if gates[l]]
@@ -219,27 +235,36 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    # live per-kernel timing of the dominant kernel during the timed steps
+    # live per-kernel timing during the timed steps: the roofline call site on
+    # every layer when it is the only one, else each timed call site on its
+    # own share of the layers (every layer has the same shapes)
     hip = Hip()
-    kid = B.KERNELS[args.kernel]
+    sites = [args.kernel] + [k for k in args.also.split(",") if k and k != args.kernel]
+    site_of = {l: sites[i * len(sites) // len(run)] for i, l in enumerate(run)}
     ev = {l: ([hip.event() for _ in range(args.steps)], [hip.event() for _ in range(args.steps)]) for l in run}
-    keep_alive = [B.tel_debug_kernel_events(handles[l], kid, ev[l][0], ev[l][1]) for l in run]
+    keep_alive = [B.tel_debug_kernel_events(handles[l], B.KERNELS[site_of[l]], ev[l][0], ev[l][1]) for l in run]
     t_start, t_stop = hip.event(), hip.event()
+    step_ev = [hip.event() for _ in range(args.steps + 1)]
 
     torch.cuda.synchronize()
     hip.h.hipEventRecord(ctypes.c_void_p(t_start), ctypes.c_void_p(stream))
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for i in range(args.steps):
+        hip.h.hipEventRecord(ctypes.c_void_p(step_ev[i]), ctypes.c_void_p(stream))
         step()
+    hip.h.hipEventRecord(ctypes.c_void_p(step_ev[-1]), ctypes.c_void_p(stream))
     hip.h.hipEventRecord(ctypes.c_void_p(t_stop), ctypes.c_void_p(stream))
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = hip.elapsed_ms(t_start, t_stop)
+    step_ms = np.array([hip.elapsed_ms(step_ev[i], step_ev[i + 1]) for i in range(args.steps)])
     for l in run:
         B.tel_debug_kernel_events(handles[l], -1, None, None)
     del keep_alive
-    kern_ms = [hip.elapsed_ms(a, b) for l in run for a, b in zip(*ev[l])]
-    kern_avg_ms = float(np.mean(kern_ms))
+    site_ms = {k: [] for k in sites}
+    for l in run:
+        for a, b in zip(*ev[l]):
+            site_ms[site_of[l]].append(hip.elapsed_ms(a, b))
 
     ms_per_step = total_ms / args.steps
     n_run = len(run)
@@ -248,32 +273,43 @@ def main():
     tflops = flops * n_run / (ms_per_step / 1e3) / 1e12
     peak = PEAK_MFMA_TFLOPS[w.dtype]
 
-    # roofline of the timed kernel (algorithmic work per launch)
+    # roofline of each timed call site (algorithmic work per launch)
     F = w.ffn
     Tg = (valid + 255) // 256 * 256 if pack else T  # rows the GEMMs and LayerNorms run on
     gemm_flops = {"qkv_fwd": 2.0 * Tg * H * 3 * H, "out_fwd": 2.0 * Tg * H * H, "ffn1_fwd": 2.0 * Tg * H * F,
                   "ffn2_fwd": 2.0 * Tg * F * H, "ffn2_dgrad": 2.0 * Tg * H * F, "ffn2_wgrad": 2.0 * Tg * H * F,
                   "ffn1_dgrad": 2.0 * Tg * F * H, "ffn1_wgrad": 2.0 * Tg * F * H, "out_dgrad": 2.0 * Tg * H * H,
-                  "out_wgrad": 2.0 * Tg * H * H, "qkv_dgrad": 2.0 * Tg * 3 * H * H, "qkv_wgrad": 2.0 * Tg * 3 * H * H}
-    if args.kernel in gemm_flops:
-        ach = gemm_flops[args.kernel] / (kern_avg_ms / 1e3) / 1e12
-        meas = MEASURED_TRAFFIC.get((args.kernel, w.name))
-        traffic = meas[1] if meas and meas[0] == kernel_sources_digest() and not pack else None
-        roof = {"kernel": args.kernel, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(ach / peak, 4), "traffic": traffic, "avg_launch_us": round(kern_avg_ms * 1e3, 2),
-                "launches": len(kern_ms), "algorithmic_per_launch": gemm_flops[args.kernel]}
-    else:
+                  "out_wgrad": 2.0 * Tg * H * H, "qkv_dgrad": 2.0 * Tg * 3 * H * H, "qkv_wgrad": 2.0 * Tg * 3 * H * H,
+                  "ffn_wgrad_pair": 4.0 * Tg * H * F, "attn_wgrad_pair": 2.0 * Tg * H * H + 2.0 * Tg * 3 * H * H}
+    digest = kernel_sources_digest()
+
+    def roofline(site):
+        ms = site_ms[site]
+        if not ms:
+            return {"kernel": site, "launches": 0}
+        avg_ms = float(np.mean(ms))
+        if site in gemm_flops:
+            ach = gemm_flops[site] / (avg_ms / 1e3) / 1e12
+            meas = MEASURED_TRAFFIC.get((site, w.name))
+            traffic = meas[1] if meas and meas[0] == digest and not pack else None
+            return {"kernel": site, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": traffic, "avg_launch_us": round(avg_ms * 1e3, 2),
+                    "launches": len(ms), "algorithmic_per_launch": gemm_flops[site]}
         e = 2 if w.dtype != "f32" else 4
         ln_bytes = {"ln1_fwd": 2 * Tg * H * e + 8 * Tg, "ln2_fwd": Tg * H * (4 + e) + 8 * Tg}
-        byts = ln_bytes.get(args.kernel, float("nan"))
-        ach = byts / (kern_avg_ms / 1e3) / 1e9
-        roof = {"kernel": args.kernel, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
+        byts = ln_bytes.get(site, float("nan"))
+        ach = byts / (avg_ms / 1e3) / 1e9
+        return {"kernel": site, "bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBS,
                 "unit": "GB/s", "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": None,
-                "avg_launch_us": round(kern_avg_ms * 1e3, 2), "launches": len(kern_ms),
-                "algorithmic_per_launch": byts}
+                "avg_launch_us": round(avg_ms * 1e3, 2), "launches": len(ms), "algorithmic_per_launch": byts}
+
+    roof = roofline(sites[0])
+    others = [roofline(k) for k in sites[1:]]
+    shape = (f"{'BERT-Large' if w.name == 'bert_large' else w.name} layer B{w.batch} S{w.seq} H{w.hidden} "
+             f"{w.dtype.replace('f16', 'fp16')}{', token packing' if pack else ''}")
 
     out = {
-        "metric": "fwd+bwd tokens/sec and TFLOP/s (% MFMA peak), BERT-Large layer B64 S128 fp16",
+        "metric": f"fwd+bwd tokens/sec and TFLOP/s (% MFMA peak), {shape}",
         "value": round(layer_tokens_per_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -299,11 +335,14 @@ def main():
         "valid_tokens_per_s": round(valid * n_run / (ms_per_step / 1e3), 1),
         "token_packing": pack,
         "wall_s_timed": round(wall, 3),
+        "step_ms": {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
+                    "p90": round(float(np.percentile(step_ms, 90)), 4)},
         "roofline": roof,
+        "kernels": [roof] + others,
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, min(args.cpu_seqs, w.batch))
-    for e in [t_start, t_stop] + [x for l in run for x in ev[l][0] + ev[l][1]]:
+    for e in [t_start, t_stop] + step_ev + [x for l in run for x in ev[l][0] + ev[l][1]]:
         hip.destroy(e)
     for h in handles:
         B.tel_layer_destroy(h)

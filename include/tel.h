@@ -28,15 +28,22 @@
  * counter = (floor(e/8) low, floor(e/8) high, site, step mod 2^32); one
  * call serves the 8 elements 8g .. 8g+7, element e taking the 16-bit half
  * (e mod 2) of output word (e/2 mod 4), and it is dropped iff that value
- * < floor(p * 2^16) with p the fp32 value in tel_config.  Sites: 0 attention
+ * < floor(p * 2^16) with p the fp32 value in tel_config.  The realised drop
+ * probability is therefore q = floor(p * 2^16) / 2^16 (q <= p < q + 2^-16;
+ * p = 0.1f gives q = 6553/65536 = 0.0999908), and a kept value times 1/(1-p)
+ * has mean (1-q)/(1-p) = 1 + (p-q)/(1-p) times the input (1.00001 at
+ * p = 0.1f).  Probabilities in (0, 2^-16), which would realise q = 0, are
+ * rejected with TEL_ERR_UNSUPPORTED.  Sites: 0 attention
  * probabilities, element e = ((b*N + h)*S + i)*S + j; 1 attention-branch
  * output, 2 FFN-branch output, element e = t*H + c with token t = b*S + s;
  * 3 the progressive layer-drop gate (output word 0 of block 0, compared as
  * a 32-bit value with floor(theta * 2^32)).  Masks are a pure function of
- * (seed, layer_id, site, step, e).  The forward keeps the attention keep
- * bits (1 bit per score, in saved) unless attn_dropout_checkpoint is set, in
- * which case the backward regenerates them; hidden-dropout bits are always
- * regenerated.  Every switch setting therefore sees identical masks.
+ * (seed, layer_id, site, step, e).  For seq <= 128 the forward keeps the
+ * attention keep bits (1 bit per score, in saved) unless
+ * attn_dropout_checkpoint is set; longer sequences, and that switch, make
+ * the backward regenerate them, so nothing kept grows with seq^2.
+ * Hidden-dropout bits are always regenerated.  Every switch setting
+ * therefore sees identical masks.
  *
  * Data layout: row-major, token-major activations [B*S, H] with t = b*S+s;
  * weights in nn.Linear layout W[out, in].  Params, activations and grads
@@ -53,7 +60,18 @@
  * invalid input returns TEL_ERR_INVALID_ARG / TEL_ERR_UNSUPPORTED without
  * touching the GPU.  A failed kernel launch returns TEL_ERR_HIP.  The message
  * for the last non-OK status of the calling thread is tel_last_error().
- * Nothing aborts or throws across this interface.
+ * Nothing aborts or throws across this interface.  The device key_lengths
+ * are not read on the host: values outside [1, seq] give wrong results (but
+ * no out-of-bounds access) in the release library; the debug library
+ * (built with TEL_DEBUG_CHECKS, libtel_debug.so) copies them to the host at
+ * every forward and backward and returns TEL_ERR_INVALID_ARG instead.
+ *
+ * Differences from the interface first planned for this layer: the backward
+ * takes x, key_lengths, training and step again (the forward keeps no
+ * pointers, and dropout masks are regenerated from them); tel_pld_keep
+ * returns int32_t; tel_config orders its fields as below and adds
+ * pack_tokens; token packing, the kernel-event hook, the debug buffer hooks
+ * and tel_check_key_lengths are additions.
  */
 #ifndef TEL_H
 #define TEL_H
@@ -184,7 +202,11 @@ enum {
     TEL_K_FFN1_FWD = 5, TEL_K_FFN2_FWD = 6,
     TEL_K_FFN2_DGRAD = 10, TEL_K_FFN2_WGRAD = 11, TEL_K_FFN1_DGRAD = 12, TEL_K_FFN1_WGRAD = 13,
     TEL_K_LN2_BWD = 14, TEL_K_OUT_DGRAD = 15, TEL_K_OUT_WGRAD = 16, TEL_K_ATTN_BWD = 17,
-    TEL_K_QKV_DGRAD = 18, TEL_K_QKV_WGRAD = 19, TEL_K_LN1_BWD = 20
+    TEL_K_QKV_DGRAD = 18, TEL_K_QKV_WGRAD = 19, TEL_K_LN1_BWD = 20,
+    /* the grouped weight-gradient launches (W_2 with W_1, W_o with W_qkv),
+       each with its split-K reduction and, for the last, the LayerNorm
+       gamma/beta sums; only where the pair runs grouped */
+    TEL_K_FFN_WGRAD_PAIR = 21, TEL_K_ATTN_WGRAD_PAIR = 22
 };
 
 /* Benchmark hook: from now on, every launch of kernel kernel_id (a TEL_K_*
@@ -193,11 +215,49 @@ enum {
  * caller created), i counting the launches since this call.  The arrays are
  * borrowed until the hook is disabled with kernel_id < 0.  Results are
  * unchanged, except that a weight-gradient pair that otherwise runs as one
- * grouped launch runs as two launches while one of its ids is profiled: those
- * two weight gradients and their bias gradients may then take another k-split
- * and round differently (every other output keeps its bits). */
+ * grouped launch runs as two launches while one of its single ids
+ * (TEL_K_*_WGRAD) is profiled: those two weight gradients and their bias
+ * gradients may then take another k-split and round differently (every other
+ * output keeps its bits).  The pair ids time the grouped launch as it runs. */
 tel_status tel_debug_kernel_events(tel_layer* layer, int kernel_id, void** start_events, void** stop_events,
                                    int count);
+
+/* Test hook: the next training forward of this layer (with attention
+ * dropout on) also writes the attention keep bits it applies to out_dev:
+ * device uint32 [B][N][S][S/32], bit j%32 of word j/32 of query row
+ * (b, h, i) set iff key j is kept; words of 32-key groups at or beyond
+ * len[b] are not written.  One-shot; out_dev NULL disarms it.  The bits are
+ * written by the attention kernel itself (copied from saved where the layer
+ * keeps them), so they are the mask the forward applied.
+ * TEL_ERR_UNSUPPORTED unless the MFMA attention runs (fp16/bf16, head width
+ * 64, seq a multiple of 64). */
+tel_status tel_debug_attn_keep_bits(tel_layer* layer, uint32_t* out_dev);
+
+/* Internal buffers a test may read after a call (their contents last until
+ * the next call that uses the same saved / scratch buffer).  Rows are the
+ * layer's rows: tokens, or packed rows under token packing. */
+enum {
+    TEL_BUF_DROP1_IN = 0,   /* scratch, fp32 [T,H]: gradient reaching dropout site 1 in the backward
+                               (Pre-LN dx1, Post-LN dz1) */
+    TEL_BUF_DROP1_OUT = 1,  /* scratch, dtype [T,H]: the same after site 1's mask and 1/(1-p) */
+    TEL_BUF_DROP2_IN = 2,   /* scratch, fp32 [T,H]: Post-LN dz2 reaching site 2 (Pre-LN: it is dy,
+                               TEL_ERR_UNSUPPORTED) */
+    TEL_BUF_DROP2_OUT = 3,  /* scratch, dtype [T,H]: gradient after site 2's mask and 1/(1-p) */
+    TEL_BUF_ATTN_KEEP_BITS = 4 /* saved: the forward's attention keep bits (layout as in
+                               tel_debug_attn_keep_bits), where the layer keeps them */
+};
+/* Offset (bytes) and size of buffer `which` within saved (*in_saved = 1) or
+ * scratch (*in_saved = 0).  TEL_ERR_UNSUPPORTED if this layer has no such
+ * buffer. */
+tel_status tel_debug_buffer(const tel_layer* layer, int which, size_t* offset, size_t* bytes, int* in_saved);
+
+/* Host-side check that host_lengths[0..batch-1] all lie in [1, seq]:
+ * TEL_OK or TEL_ERR_INVALID_ARG naming the first bad entry.  The debug
+ * library runs it on a host copy of the device key_lengths. */
+tel_status tel_check_key_lengths(const int32_t* host_lengths, int32_t batch, int32_t seq);
+
+/* 1 in the debug library (TEL_DEBUG_CHECKS), else 0. */
+int32_t tel_debug_checks_enabled(void);
 
 /* Progressive layer dropping (PLD page, "core mechanism": theta(t) =
  * (1 - theta_bar) exp(-gamma t) + theta_bar).  Host-only, pure functions.

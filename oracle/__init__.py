@@ -74,6 +74,8 @@ def lib():
                                        ctypes.POINTER(ctypes.c_uint8)]
         L.orc_drop_threshold.argtypes = [ctypes.c_double]
         L.orc_drop_threshold.restype = ctypes.c_uint64
+        L.orc_omp_threads.argtypes = []
+        L.orc_omp_threads.restype = ctypes.c_int
         L.orc_pld_theta.argtypes = [ctypes.c_double] * 3
         L.orc_pld_theta.restype = ctypes.c_double
         L.orc_pld_keep.argtypes = [ctypes.c_uint64, ctypes.c_int32, ctypes.c_uint64, ctypes.c_double]
@@ -91,7 +93,7 @@ def lib():
                                         ctypes.POINTER(ctypes.c_int32), _DP, ctypes.POINTER(_Acts)]
         L.orc_layer_backward.argtypes = [ctypes.POINTER(_Cfg), ctypes.POINTER(_Params), _DP,
                                          ctypes.POINTER(ctypes.c_int32), _DP, ctypes.c_int, _DP,
-                                         ctypes.POINTER(_Params)]
+                                         ctypes.POINTER(_Params), _DP]
         _lib = L
     return _lib
 
@@ -147,6 +149,11 @@ def dropout_mask(seed, layer, site, step, p, e0, n):
 
 def drop_threshold(p):
     return int(lib().orc_drop_threshold(float(p)))
+
+
+def omp_threads():
+    """Threads the oracle's OpenMP regions run with."""
+    return int(lib().orc_omp_threads())
 
 
 def pld_theta(t, theta_bar=0.5, gamma=0.001):
@@ -230,8 +237,9 @@ def layer_forward(cfg: LayerCfg, params: dict, x, lengths, want_acts=False):
     return y, acts
 
 
-def layer_backward(cfg: LayerCfg, params: dict, x, lengths, dy, ln_invertible=False):
-    """Returns (dx, grads) in fp64; grads keyed like params."""
+def layer_backward(cfg: LayerCfg, params: dict, x, lengths, dy, ln_invertible=False, want_y=False):
+    """Returns (dx, grads) in fp64; grads keyed like params.  With want_y,
+    returns (dx, grads, y): the forward output it recomputes on the way."""
     keep = []
     P = _params_struct(params, keep)
     x = _f64(x).reshape(cfg.batch * cfg.seq, cfg.hidden)
@@ -240,10 +248,11 @@ def layer_backward(cfg: LayerCfg, params: dict, x, lengths, dy, ln_invertible=Fa
     grads = {n: np.empty(np.shape(params[n])) for n in PARAM_NAMES}
     G = _Params(*[_dp(grads[n]) for n in PARAM_NAMES])
     dx = np.empty_like(x)
+    y = np.empty_like(x) if want_y else None
     c = cfg.c()
     rc = lib().orc_layer_backward(ctypes.byref(c), ctypes.byref(P), _dp(x),
                                   ln.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)), _dp(dy),
-                                  int(ln_invertible), _dp(dx), ctypes.byref(G))
+                                  int(ln_invertible), _dp(dx), ctypes.byref(G), _dp(y))
     if rc != 0:
         raise ValueError("oracle rejected the configuration")
-    return dx, grads
+    return (dx, grads, y) if want_y else (dx, grads)

@@ -47,6 +47,11 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#else
+static int omp_get_num_threads(void) { return 1; }
+#endif
 
 #define ORC_OK 0
 #define ORC_ERR (-1)
@@ -138,7 +143,9 @@ static uint32_t rng_half(uint64_t seed, int32_t layer, uint32_t site, uint64_t s
     return (e & 1) ? (w >> 16) : (w & 0xFFFFu);
 }
 
-/* An element is dropped iff its 16-bit value < floor(p * 2^16). */
+/* An element is dropped iff its 16-bit value < floor(p * 2^16), so the
+ * realised drop probability is floor(p * 2^16) / 2^16; a p in (0, 2^-16)
+ * would realise none and is rejected by check_cfg. */
 static uint64_t drop_threshold(double p)
 {
     if (!(p > 0.0)) return 0;
@@ -146,6 +153,18 @@ static uint64_t drop_threshold(double p)
 }
 
 uint64_t orc_drop_threshold(double p) { return drop_threshold(p); }
+
+/* Threads an OpenMP parallel region of this library runs with. */
+int orc_omp_threads(void)
+{
+    int n = 1;
+    #pragma omp parallel
+    {
+        #pragma omp single
+        n = omp_get_num_threads();
+    }
+    return n;
+}
 
 static int keep_elem(uint64_t seed, int32_t layer, uint32_t site, uint64_t step, uint64_t e, uint64_t thr)
 {
@@ -470,6 +489,8 @@ static int check_cfg(const orc_cfg *c)
     if (c->batch <= 0 || c->seq <= 0 || c->hidden <= 0 || c->heads <= 0 || c->ffn <= 0) return ORC_ERR;
     if (c->hidden % c->heads) return ORC_ERR;
     if (c->attn_p < 0 || c->attn_p >= 1 || c->hidden_p < 0 || c->hidden_p >= 1) return ORC_ERR;
+    if ((c->attn_p > 0 && drop_threshold(c->attn_p) == 0) || (c->hidden_p > 0 && drop_threshold(c->hidden_p) == 0))
+        return ORC_ERR;
     return ORC_OK;
 }
 
@@ -571,9 +592,10 @@ int orc_layer_forward(const orc_cfg *cfg, const orc_params *p, const double *x, 
 
 /* Backward by the chain rule through the forward above (recomputed here).
  * dy [T,H] upstream gradient; dx [T,H] and all 12 grads OVERWRITTEN.
- * ln_invertible selects the LayerNorm backward from the LN output. */
+ * ln_invertible selects the LayerNorm backward from the LN output.  y_out
+ * (may be NULL) receives the recomputed forward output. */
 int orc_layer_backward(const orc_cfg *cfg, const orc_params *p, const double *x, const int32_t *len,
-                       const double *dy, int ln_invertible, double *dx, orc_grads *gr)
+                       const double *dy, int ln_invertible, double *dx, orc_grads *gr, double *y_out)
 {
     if (check_cfg(cfg)) return ORC_ERR;
     const int B = cfg->batch, S = cfg->seq, H = cfg->hidden, N = cfg->heads, F = cfg->ffn;
@@ -582,6 +604,7 @@ int orc_layer_backward(const orc_cfg *cfg, const orc_params *p, const double *x,
     fwd_state st;
     memset(&st, 0, sizeof(st));
     layer_fwd(cfg, p, x, len, &st);
+    copy_out(y_out, st.y, TH);
     attn_ctx a = { B, S, H, N, H / N, len, cfg->training, cfg->batch_offset, cfg->attn_p,
                    cfg->seed, cfg->step, cfg->layer_id };
 

@@ -200,3 +200,90 @@ def compare_packed(w: syn.Workload, g, o, batches):
         report[n] = rel_norm(g["g_" + n], o["grads"][n])
         assert report[n] <= 5e-2, report
     return report
+
+
+def oracle_full(w: syn.Workload, params_r, x_r, dy_r, lengths, training=True, step=0, layer_id=0,
+                invertible=False):
+    """Oracle forward + backward of the whole batch in one call (element
+    indices are global because the batch starts at sequence 0).  Returns
+    (y, dx, grads), fp64."""
+    cfg = oracle.LayerCfg(w.batch, w.seq, w.hidden, w.heads, w.ffn, pre_ln=w.pre_ln, training=training,
+                          attn_p=float(np.float32(w.attn_p)), hidden_p=float(np.float32(w.hidden_p)),
+                          seed=w.seed, step=step, layer_id=layer_id)
+    dx, g, y = oracle.layer_backward(cfg, params_r, x_r, lengths, dy_r, ln_invertible=invertible, want_y=True)
+    return y, dx, g
+
+
+def compare_full(w: syn.Workload, y, dx, grads, o_y, o_dx, o_grads, tag=""):
+    """fp16/bf16 tolerances on every element of y, dx and all twelve gradients."""
+    rep = {"y": max_abs(y, o_y), "dx": rel_norm(dx, o_dx)}
+    for n in NAMES:
+        rep[n] = rel_norm(grads[n], o_grads[n])
+    print(tag, {k: f"{v:.3g}" for k, v in rep.items()})
+    assert rep["y"] <= 2e-2, rep
+    for k, v in rep.items():
+        if k != "y":
+            assert v <= 5e-2, (k, rep)
+    return rep
+
+
+def keep_bits_of_words(words):
+    """uint32 keep words (numpy) -> one uint8 keep flag per score, in element
+    order: bit j of word k is score 32k + j."""
+    return np.unpackbits(np.ascontiguousarray(words).view(np.uint8), bitorder="little")
+
+
+class GpuRun:
+    """One layer on the GPU through the C ABI whose saved and scratch buffers
+    stay readable after each call (for the in-situ mask checks)."""
+
+    def __init__(self, w: syn.Workload, params_t, switches=None, layer_id=0, ln_eps=1e-12):
+        import torch
+        from transformer_encoder_layer_amd import binding as B
+        from transformer_encoder_layer_amd.layer import LayerConfig
+        self.B, self.torch, self.w = B, torch, w
+        sw = dict(switches or {})
+        cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, float(np.float32(w.attn_p)),
+                          float(np.float32(w.hidden_p)), w.pre_ln, w.seed, layer_id, syn.torch_dtype(w.dtype),
+                          ln_eps, bool(sw.get("attn_dropout_checkpoint", w.attn_dropout_checkpoint)),
+                          bool(sw.get("normalize_invertible", w.normalize_invertible)),
+                          bool(sw.get("gelu_checkpoint", w.gelu_checkpoint)))
+        self.h = B.tel_layer_create(cfg.to_c())
+        sv, sc = B.tel_layer_workspace_bytes(self.h)
+        self.saved = torch.empty(max(sv, 1), dtype=torch.uint8, device="cuda")
+        self.scratch = torch.empty(max(sc, 1), dtype=torch.uint8, device="cuda")
+        self.P = {n: params_t[n].cuda() for n in NAMES}
+
+    def forward(self, x, lengths=None, step=0, capture_bits=False):
+        torch, B = self.torch, self.B
+        self.x = x.cuda()
+        self.lens = None if lengths is None else torch.from_numpy(np.asarray(lengths, dtype=np.int32)).cuda()
+        self.step = step
+        self.bits = None
+        if capture_bits:
+            w = self.w
+            # zero first: words of key groups the kernel does not visit stay 0
+            self.bits = torch.zeros(w.batch * w.heads * w.seq * w.seq // 32, dtype=torch.int32, device="cuda")
+            B.tel_debug_attn_keep_bits(self.h, self.bits)
+        y = torch.empty_like(self.x)
+        B.tel_layer_forward(self.h, B.make_params(self.P), self.x, self.lens, 1, step, y, self.saved, self.scratch)
+        torch.cuda.synchronize()
+        return y
+
+    def backward(self, dy):
+        torch, B = self.torch, self.B
+        dx = torch.empty_like(self.x)
+        G = {n: torch.empty_like(self.P[n]) for n in NAMES}
+        B.tel_layer_backward(self.h, B.make_params(self.P), self.x, self.lens, 1, self.step, dy.cuda(), self.saved,
+                             self.scratch, dx, B.make_grads(G))
+        torch.cuda.synchronize()
+        return dx, G
+
+    def buffer(self, name, dtype):
+        """Copy of an internal buffer (TEL_BUF_* name) as a CPU tensor of dtype."""
+        off, n, in_saved = self.B.tel_debug_buffer(self.h, name)
+        base = self.saved if in_saved else self.scratch
+        return base[off:off + n].view(dtype).cpu()
+
+    def close(self):
+        self.B.tel_layer_destroy(self.h)

@@ -58,6 +58,9 @@ def cfg(**kw):
     (dict(ffn=24), B.TEL_ERR_INVALID_ARG),
     (dict(pack_tokens=1), B.TEL_ERR_UNSUPPORTED),   # fp32 / d = 16: no packed attention
     (dict(pack_tokens=1, dtype=B.TEL_F16, hidden=256, heads=4, seq=96), B.TEL_ERR_UNSUPPORTED),  # S % 64
+    # 16-bit draws cannot realise a drop probability in (0, 2^-16)
+    (dict(attn_dropout=1e-6), B.TEL_ERR_UNSUPPORTED),
+    (dict(hidden_dropout=float(np.float32(2.0 ** -16 * 0.999))), B.TEL_ERR_UNSUPPORTED),
 ])
 def test_create_rejects(kw, status):
     with pytest.raises(B.TelError) as e:
@@ -176,3 +179,87 @@ def test_pld_memsave_stack_gates():
     gates = [B.tel_pld_keep(7, l, 5000, theta) for l in range(24)]
     assert gates == [oracle.pld_keep(7, l, 5000, theta) for l in range(24)]
     assert 0 < sum(gates) < 24
+
+
+def test_smallest_realisable_dropout_accepted():
+    # p = 2^-16 realises exactly one dropped value in 2^16 (threshold 1)
+    for kw in (dict(attn_dropout=2.0 ** -16), dict(hidden_dropout=2.0 ** -16), dict(attn_dropout=0.0)):
+        B.tel_layer_destroy(B.tel_layer_create(cfg(**kw)))
+
+
+def _saved(**kw):
+    h = B.tel_layer_create(cfg(**kw))
+    try:
+        return B.tel_layer_workspace_bytes(h)[0]
+    finally:
+        B.tel_layer_destroy(h)
+
+
+def test_long_sequences_keep_nothing_quadratic():
+    # S <= 128: the forward keeps 1 keep bit per attention score (B*N*S*S/8
+    # bytes); longer sequences regenerate them, so attention dropout adds
+    # nothing to the saved workspace (the long-sequence workload's shape)
+    short = dict(dtype=B.TEL_F16, batch=4, seq=128, hidden=256, heads=4, ffn=1024)
+    assert _saved(**short, attn_dropout=0.1) - _saved(**short) == 4 * 4 * 128 * 128 // 8
+    long = dict(dtype=B.TEL_BF16, batch=8, seq=2048, hidden=1024, heads=16, ffn=4096)
+    assert _saved(**long, attn_dropout=0.1) == _saved(**long)
+    # and what is kept grows linearly in S at fixed tokens
+    a = _saved(dtype=B.TEL_BF16, batch=16, seq=1024, hidden=1024, heads=16, ffn=4096, attn_dropout=0.1)
+    b = _saved(**long, attn_dropout=0.1)
+    # the only S-dependent term left is the [B,N,S] fp32 log-sum-exp (same B*S here)
+    assert a == b
+
+
+def test_debug_hooks_validate():
+    h = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=2, seq=128, hidden=256, heads=4, ffn=1024, attn_dropout=0.1))
+    try:
+        off, n, sv = B.tel_debug_buffer(h, "attn_keep_bits")
+        assert sv and n == 2 * 4 * 128 * 128 // 8
+        for name in ("drop1_in", "drop1_out", "drop2_out"):
+            off, n, sv = B.tel_debug_buffer(h, name)
+            assert not sv and n == 2 * 128 * 256 * (4 if name == "drop1_in" else 2)
+        with pytest.raises(B.TelError) as e:     # Pre-LN: site 2's backward input is dy itself
+            B.tel_debug_buffer(h, "drop2_in")
+        assert e.value.status == B.TEL_ERR_UNSUPPORTED
+        with pytest.raises(B.TelError) as e:
+            B.tel_debug_buffer(h, 9)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        B.tel_debug_attn_keep_bits(h, None)       # disarm is always accepted
+        with pytest.raises(B.TelError) as e:       # misaligned buffer
+            B.tel_debug_attn_keep_bits(h, 4100)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+    finally:
+        B.tel_layer_destroy(h)
+    h = B.tel_layer_create(cfg(attn_dropout=0.1))  # fp32, head width 16: no keep bits anywhere
+    try:
+        with pytest.raises(B.TelError) as e:
+            B.tel_debug_attn_keep_bits(h, 4096)
+        assert e.value.status == B.TEL_ERR_UNSUPPORTED
+        with pytest.raises(B.TelError) as e:
+            B.tel_debug_buffer(h, "attn_keep_bits")
+        assert e.value.status == B.TEL_ERR_UNSUPPORTED
+    finally:
+        B.tel_layer_destroy(h)
+
+
+def test_key_length_check_host():
+    B.tel_check_key_lengths([1, 16, 7], 3, 16)
+    for bad in ([0, 16, 7], [1, 17, 7], [1, 16, -3]):
+        with pytest.raises(B.TelError) as e:
+            B.tel_check_key_lengths(bad, 3, 16)
+        assert e.value.status == B.TEL_ERR_INVALID_ARG
+        assert "key_lengths" in B.tel_last_error()
+
+
+def test_debug_library_builds_with_checks():
+    # the debug build differs only by the device key-length check
+    assert os.path.exists(B.DEBUG_LIB_PATH)
+    D = B.lib(B.DEBUG_LIB_PATH)
+    assert B.tel_debug_checks_enabled(D) and not B.tel_debug_checks_enabled()
+    out = subprocess.run(["nm", "-D", "--defined-only", B.DEBUG_LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    assert set(header_functions()) <= syms
+    with pytest.raises(B.TelError) as e:
+        B.tel_check_key_lengths([3, 0], 2, 16, D)
+    assert e.value.status == B.TEL_ERR_INVALID_ARG

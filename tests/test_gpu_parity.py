@@ -2,15 +2,19 @@
 
 Tolerances: fp32 max-abs 1e-5 on y, dx and every gradient; fp16/bf16
 max-abs 2e-2 on y and relative-norm 5e-2 on dx and each gradient; dropout
-masks bit-exact.  Small cases run every sequence through the oracle; the
-full-size workloads run the GPU at their real shape and compare sampled
-sequences (dy is zero on the others, so every weight gradient is exactly
-the sum over the sampled sequences, which the oracle computes)."""
+masks bit-exact (test_gpu_masks.py).  Small cases run every sequence
+through the oracle.  The Post-LN BERT-Base and long-sequence workloads are
+compared in full (whole batch, full upstream gradient); the BERT-Large and
+memory-saving stacks in full, layer by layer, in test_gpu_stack.py.  The
+remaining full-size cases here compare sampled sequences (dy is zero on the
+others, so every weight gradient is exactly the sum over the sampled
+sequences, which the oracle computes)."""
 import numpy as np
 import pytest
 
 import oracle
-from _harness import NAMES, compare, compare_packed, gpu_layer, oracle_layer, prepare, rel_norm, zero_padding_grad
+from _harness import (NAMES, compare, compare_full, compare_packed, gpu_layer, oracle_full, oracle_layer, prepare,
+                      rel_norm, zero_padding_grad)
 from transformer_encoder_layer_amd import synthetic as syn
 
 pytestmark = pytest.mark.gpu
@@ -262,13 +266,74 @@ def test_profiling_hook_keeps_results():
             assert np.array_equal(a[k], b[k]), k
 
 
+def _full(name, layer_id=0, step=0, random_affine=False):
+    # the whole batch with the full upstream gradient: every element of y,
+    # dx and the twelve parameter gradients against the oracle
+    w = syn.WORKLOADS[name]
+    data = prepare(w, layer=layer_id, random_affine=random_affine)
+    g = gpu_layer(w, data, step=step, layer_id=layer_id)
+    o_y, o_dx, o_g = oracle_full(w, data["params_r"], data["x_r"], data["dy_r"], data["lengths"], step=step,
+                                 layer_id=layer_id, invertible=w.normalize_invertible)
+    compare_full(w, g["y"], g["dx"], {n: g["g_" + n] for n in NAMES}, o_y, o_dx, o_g, tag=name)
+
+
+@pytest.mark.timeout(600)
 def test_full_bert_base_postln():
-    _sampled("bert_base_postln", [0, 31])
+    _full("bert_base_postln", layer_id=2, step=1)
 
 
+@pytest.mark.timeout(600)
 def test_full_long_seq():
-    _sampled("long_seq", [7])
+    _full("long_seq", step=3)
 
 
 def test_full_memsave_layer():
     _sampled("memsave_stack", [0, 127])
+
+
+def test_debug_build_checks_key_lengths():
+    # libtel_debug.so reads the device key lengths back before launching
+    # anything: valid lengths give the release library's results bit for
+    # bit; a length outside [1, S] is refused on the host, before any kernel
+    import ctypes
+    import torch
+    from transformer_encoder_layer_amd import binding as B
+    from transformer_encoder_layer_amd.layer import LayerConfig
+    D = B.lib(B.DEBUG_LIB_PATH)
+    assert B.tel_debug_checks_enabled(D)
+    w = syn.Workload("dbg", 3, 64, 256, 4, 1024, True, "f16", 0.1, 0.1, 31, lengths=(5, 64))
+    data = prepare(w, random_affine=True)
+    ref = gpu_layer(w, data, step=2)
+    cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, float(np.float32(0.1)), float(np.float32(0.1)),
+                      True, w.seed, 0, torch.float16).to_c()
+    h = ctypes.c_void_p()
+    assert D.tel_layer_create(ctypes.byref(cfg), ctypes.byref(h)) == 0
+    try:
+        sv, sc = ctypes.c_size_t(), ctypes.c_size_t()
+        assert D.tel_layer_workspace_bytes(h, ctypes.byref(sv), ctypes.byref(sc)) == 0
+        P = {n: data["params_t"][n].cuda() for n in NAMES}
+        x = data["x_t"].cuda()
+        y = torch.empty_like(x)
+        dx = torch.empty_like(x)
+        G = {n: torch.empty_like(P[n]) for n in NAMES}
+        saved = torch.empty(sv.value, dtype=torch.uint8, device="cuda")
+        scratch = torch.empty(sc.value, dtype=torch.uint8, device="cuda")
+        st = torch.cuda.current_stream().cuda_stream
+        good = torch.from_numpy(data["lengths"]).cuda()
+        params = B.make_params(P)
+        assert D.tel_layer_forward(h, ctypes.byref(params), x.data_ptr(), good.data_ptr(), 1, 2, y.data_ptr(),
+                                   saved.data_ptr(), scratch.data_ptr(), st) == 0
+        grads = B.make_grads(G)
+        assert D.tel_layer_backward(h, ctypes.byref(params), x.data_ptr(), good.data_ptr(), 1, 2,
+                                    data["dy_t"].cuda().data_ptr(), saved.data_ptr(), scratch.data_ptr(),
+                                    dx.data_ptr(), ctypes.byref(grads), st) == 0
+        torch.cuda.synchronize()
+        assert np.array_equal(y.double().cpu().numpy(), ref["y"])
+        assert np.array_equal(dx.double().cpu().numpy(), ref["dx"])
+        for bad in ([0, 10, 20], [64, 65, 3]):
+            lens = torch.tensor(bad, dtype=torch.int32, device="cuda")
+            rc = D.tel_layer_forward(h, ctypes.byref(params), x.data_ptr(), lens.data_ptr(), 1, 2, y.data_ptr(),
+                                     saved.data_ptr(), scratch.data_ptr(), st)
+            assert rc == B.TEL_ERR_INVALID_ARG and b"key_lengths" in D.tel_last_error()
+    finally:
+        D.tel_layer_destroy(h)

@@ -40,6 +40,38 @@ def test_drop_threshold_exact():
     assert oracle.drop_threshold(float(np.float32(0.1))) == 6553
 
 
+def test_realised_drop_probability():
+    # The drop probability a 16-bit draw realises is q = floor(p * 2^16) / 2^16
+    # (q <= p < q + 2^-16).  At p = 1.9 * 2^-16 (threshold 1) q is about half
+    # of p, so the oracle's masks over 2^24 elements must match q and be far
+    # from p (about 256 drops against the 486 p would give).
+    n = 1 << 24
+    for p in (1.9 * 2 ** -16, float(np.float32(0.1))):
+        thr = oracle.drop_threshold(p)
+        q = Fraction(thr, 2 ** 16)
+        assert q <= Fraction(p) < q + Fraction(1, 2 ** 16)
+        dropped = n - int(oracle.dropout_mask(99, 3, 2, 11, p, 0, n).sum(dtype=np.int64))
+        sd = math.sqrt(n * float(q) * (1 - float(q)))
+        assert abs(dropped - n * float(q)) < 5 * sd, (p, dropped, n * float(q))
+        if p < 1e-4:
+            assert abs(dropped - n * p) > 5 * sd
+    # p = 0.1f: q = 6553/65536 and the inverted-dropout mean (1-q)/(1-p)
+    p = float(np.float32(0.1))
+    assert oracle.drop_threshold(p) == 6553
+    bias = (1 - 6553 / 65536) / (1 - p) - 1
+    assert 1.0e-5 < bias < 1.1e-5
+
+
+def test_unrealisable_probability_rejected():
+    # 0 < p < 2^-16 would realise no dropout at all; the oracle refuses it
+    cfg = oracle.LayerCfg(1, 16, 64, 4, 256, attn_p=1e-6, hidden_p=0.1)
+    p = {n: np.zeros(s) for n, s in {"w_qkv": (192, 64), "b_qkv": (192,), "w_o": (64, 64), "b_o": (64,),
+                                     "ln1_g": (64,), "ln1_b": (64,), "w_1": (256, 64), "b_1": (256,),
+                                     "w_2": (64, 256), "b_2": (64,), "ln2_g": (64,), "ln2_b": (64,)}.items()}
+    with pytest.raises(ValueError):
+        oracle.layer_forward(cfg, p, np.zeros((16, 64)), np.array([16]))
+
+
 def test_mask_uses_philox_halfwords():
     # element e of a site: 16-bit half (e mod 2) of word (e/2 mod 4) of the
     # Philox4x32-10 block floor(e/8) (counter = (block, 0, site, step),

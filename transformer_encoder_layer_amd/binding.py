@@ -13,6 +13,7 @@ import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtel.so")
+DEBUG_LIB_PATH = os.path.join(_HERE, "libtel_debug.so")
 
 TEL_F32, TEL_F16, TEL_BF16 = 0, 1, 2
 TEL_OK, TEL_ERR_INVALID_ARG, TEL_ERR_UNSUPPORTED, TEL_ERR_STATE, TEL_ERR_HIP = 0, -1, -2, -3, -4
@@ -25,13 +26,17 @@ PARAM_NAMES = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
 # every symbol declared in include/tel.h
 EXPORTS = ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward", "tel_layer_backward",
            "tel_layer_set_valid_tokens", "tel_layer_destroy", "tel_last_error", "tel_debug_dropout_mask",
-           "tel_debug_kernel_events",
-           "tel_pld_theta", "tel_pld_keep")
+           "tel_debug_kernel_events", "tel_debug_attn_keep_bits", "tel_debug_buffer", "tel_check_key_lengths",
+           "tel_debug_checks_enabled", "tel_pld_theta", "tel_pld_keep")
+
+# buffer ids (TEL_BUF_*) of include/tel.h
+BUFFERS = {"drop1_in": 0, "drop1_out": 1, "drop2_in": 2, "drop2_out": 3, "attn_keep_bits": 4}
 
 # kernel ids (TEL_K_*) of include/tel.h
 KERNELS = {"ln1_fwd": 0, "qkv_fwd": 1, "attn_fwd": 2, "out_fwd": 3, "ln2_fwd": 4, "ffn1_fwd": 5, "ffn2_fwd": 6,
            "ffn2_dgrad": 10, "ffn2_wgrad": 11, "ffn1_dgrad": 12, "ffn1_wgrad": 13, "ln2_bwd": 14,
-           "out_dgrad": 15, "out_wgrad": 16, "attn_bwd": 17, "qkv_dgrad": 18, "qkv_wgrad": 19, "ln1_bwd": 20}
+           "out_dgrad": 15, "out_wgrad": 16, "attn_bwd": 17, "qkv_dgrad": 18, "qkv_wgrad": 19, "ln1_bwd": 20,
+           "ffn_wgrad_pair": 21, "attn_wgrad_pair": 22}
 
 
 class TelError(RuntimeError):
@@ -58,17 +63,16 @@ class tel_grads(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in PARAM_NAMES]
 
 
-_lib = None
+_libs = {}
 
 
-def lib():
-    """Load libtel.so (raises if it has not been built)."""
-    global _lib
-    if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+def lib(path: str = LIB_PATH):
+    """Load libtel.so (or the debug build at DEBUG_LIB_PATH); raises if it has not been built."""
+    if path not in _libs:
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with "
                                "`python -m transformer_encoder_layer_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
+        L = ctypes.CDLL(path)
         vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
         L.tel_layer_create.argtypes = [ctypes.POINTER(tel_config), ctypes.POINTER(vp)]
         L.tel_layer_workspace_bytes.argtypes = [vp, ctypes.POINTER(sz), ctypes.POINTER(sz)]
@@ -86,17 +90,24 @@ def lib():
         L.tel_pld_theta.restype = ctypes.c_double
         L.tel_pld_keep.argtypes = [u64, i32, u64, ctypes.c_double]
         L.tel_pld_keep.restype = i32
+        L.tel_debug_attn_keep_bits.argtypes = [vp, vp]
+        L.tel_debug_buffer.argtypes = [vp, ctypes.c_int, ctypes.POINTER(sz), ctypes.POINTER(sz),
+                                       ctypes.POINTER(ctypes.c_int)]
+        L.tel_check_key_lengths.argtypes = [ctypes.POINTER(i32), i32, i32]
+        L.tel_debug_checks_enabled.argtypes = []
+        L.tel_debug_checks_enabled.restype = i32
         for name in ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward",
                      "tel_layer_backward", "tel_layer_set_valid_tokens", "tel_layer_destroy",
-                     "tel_debug_dropout_mask", "tel_debug_kernel_events"):
+                     "tel_debug_dropout_mask", "tel_debug_kernel_events", "tel_debug_attn_keep_bits",
+                     "tel_debug_buffer", "tel_check_key_lengths"):
             getattr(L, name).restype = ctypes.c_int
-        _lib = L
-    return _lib
+        _libs[path] = L
+    return _libs[path]
 
 
-def _check(status: int):
+def _check(status: int, L=None):
     if status != TEL_OK:
-        raise TelError(status, lib().tel_last_error().decode(errors="replace"))
+        raise TelError(status, (L or lib()).tel_last_error().decode(errors="replace"))
 
 
 def ptr(t):
@@ -175,6 +186,30 @@ def tel_debug_kernel_events(handle, kernel_id, start_events, stop_events):
     b = (ctypes.c_void_p * n)(*stop_events)
     _check(lib().tel_debug_kernel_events(handle, int(kernel_id), a, b, n))
     return (a, b)  # caller keeps these alive while the hook is on
+
+
+def tel_debug_attn_keep_bits(handle, out):
+    """Arm the keep-bit capture of the next training forward (out: uint32 device tensor, or None to disarm)."""
+    _check(lib().tel_debug_attn_keep_bits(handle, ptr(out)))
+
+
+def tel_debug_buffer(handle, which):
+    """(offset, bytes, in_saved) of an internal buffer (which: a BUFFERS name or TEL_BUF_* id)."""
+    w = BUFFERS[which] if isinstance(which, str) else int(which)
+    off, n, sv = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_int()
+    _check(lib().tel_debug_buffer(handle, w, ctypes.byref(off), ctypes.byref(n), ctypes.byref(sv)))
+    return off.value, n.value, bool(sv.value)
+
+
+def tel_check_key_lengths(lengths, batch, seq, L=None):
+    """Host check of a key-length array (sequence of ints) against [1, seq]."""
+    L = L or lib()
+    arr = (ctypes.c_int32 * len(lengths))(*[int(v) for v in lengths])
+    _check(L.tel_check_key_lengths(arr, int(batch), int(seq)), L)
+
+
+def tel_debug_checks_enabled(L=None) -> bool:
+    return bool((L or lib()).tel_debug_checks_enabled())
 
 
 def tel_pld_theta(t, theta_bar, gamma) -> float:

@@ -13,8 +13,10 @@ struct AttnArgs {
     const int32_t* len; // [B] valid key counts, or nullptr
     Drop drop;          // site 0; thr == 0: no dropout
     uint32_t* bits;     // optional keep bits [B][NH][S][S/32] (bit j%32 of word j/32 = key j):
-                        // written by the forward, read by the backward; nullptr: the
-                        // backward regenerates them from the counter-based RNG
+                        // written by the MFMA forwards (words of key blocks at or beyond
+                        // len[b] are not visited, so not written); read by the S <= 128
+                        // backward; nullptr there: it regenerates them from the
+                        // counter-based RNG, as the longer-S and generic kernels always do
     // forward
     void* ctx;          // [B*S][H] head-merged output
     float* lse;         // [B][NH][S] log2-sum-exp2 of the scaled scores

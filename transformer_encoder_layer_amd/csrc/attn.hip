@@ -21,10 +21,14 @@
 // Backward: a query-parallel kernel computes D_i = rowsum(dO_i * O_i) and
 // dQ; a key-parallel kernel computes dK and dV (no atomics: every output
 // row is owned by one wave).  Both recompute P from Q, K and the saved
-// log-sum-exp.  The dropout bits come from the 1-bit-per-element mask the
-// forward packed (one 32-bit word per query and 32 keys), or, when the
-// caller chose not to keep it (attention-dropout checkpointing), from the
-// counter-based RNG again -- the same bits either way.
+// log-sum-exp, and regenerate the dropout bits from the counter-based RNG:
+// at these lengths the forward keeps no per-score state at all.  For
+// S <= 128 one workgroup does the whole backward of a (batch, head); its
+// dropout bits come from the 1-bit-per-score mask the forward packed (one
+// 32-bit word per query and 32 keys, B*N*S*S/8 bytes), or, when the caller
+// chose not to keep it (attention-dropout checkpointing), from the RNG
+// again -- the same bits either way.  The forward kernels write their keep
+// words to a.bits whenever it is set (the S <= 128 mask, or a test's copy).
 //
 // SIMT path: one thread per row, any S and d in {16, 32, 64, 128}.
 #include "attn.h"
@@ -409,20 +413,14 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) dq[ct][r] = 0.0f;
     const uint64_t rowbase = ((uint64_t)(b * NH + h) * S + qlc) * (uint64_t)S;
-    const bool stored_bits = a.drop.thr && a.bits;
 
     const int row0 = tid >> 3, row1 = row0 + 32, ch = tid & 7;
     uint4 pk0, pk1, pv0, pv1;
-    uint32_t pb0 = 0xFFFFFFFFu, pb1 = 0xFFFFFFFFu;
     auto fetch = [&](int kb) {
         pk0 = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row0) * D + ch * 8);
         pk1 = *reinterpret_cast<const uint4*>(K + (size_t)(kb * KB + row1) * D + ch * 8);
         pv0 = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row0) * D + ch * 8);
         pv1 = *reinterpret_cast<const uint4*>(V + (size_t)(kb * KB + row1) * D + ch * 8);
-        if (stored_bits) {
-            pb0 = a.bits[(rowbase >> 5) + kb * 2];
-            pb1 = a.bits[(rowbase >> 5) + kb * 2 + 1];
-        }
     };
     if (nkb > 0) fetch(0);
     for (int kb = 0; kb < nkb; ++kb) {
@@ -431,7 +429,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
         *reinterpret_cast<uint4*>(&Ks[buf][kmaj_off(row1, ch * 8)]) = pk1;
         *reinterpret_cast<uint4*>(&Vs[buf][kmaj_off(row0, ch * 8)]) = pv0;
         *reinterpret_cast<uint4*>(&Vs[buf][kmaj_off(row1, ch * 8)]) = pv1;
-        const uint32_t w0 = pb0, w1 = pb1;
         __syncthreads();
         if (kb + 1 < nkb) fetch(kb + 1);
         if (active) {
@@ -452,10 +449,10 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
                     for (int r = 0; r < 16; ++r)
                         if (kb * KB + kt * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3) >= L) sc[r] = -INFINITY;
                 }
+                // keep bits regenerated from the counter-based RNG (the
+                // forward kept none for sequences this long)
                 uint32_t word = 0xFFFFFFFFu;
-                if (a.drop.thr)
-                    word = stored_bits ? (kt ? w1 : w0)
-                                       : keep_word32(a.drop.rng, rowbase + kb * KB + kt * 32, a.drop.thr, lane);
+                if (a.drop.thr) word = keep_word32(a.drop.rng, rowbase + kb * KB + kt * 32, a.drop.thr, lane);
                 const uint32_t kbits = word >> ((lane >> 5) * 4);  // key 8g + 4*(lane>>5) + i -> bit 8g + i
                 const uint32_t scale_bits = __float_as_uint(a.drop.scale);
 #pragma unroll
@@ -507,8 +504,8 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dq_mfma(AttnArgs a) {
 // global loads of block qb+1 (Q, dO, log-sum-exp, D and the keep words) are
 // issued into registers before the MFMAs of block qb, so one barrier per
 // block suffices and the load latency hides behind the compute.  Keep words
-// are always staged: the stored mask, or regenerated per 32 keys with one
-// Philox call per 8 keys, or all ones without dropout.
+// are always staged: regenerated per 32 keys with one Philox call per 8
+// keys, or all ones without dropout.
 template <typename T>
 __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
     constexpr int D = 64, QB = 64;
@@ -554,7 +551,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
     // log-sum-exp / D values, one keep word (query tid/4, key word tid%4)
     uint4 pq0, pq1, po0, po1;
     float pld = 0.0f;
-    uint32_t pw = 0xFFFFFFFFu;
     const int wq = tid >> 2, ww = tid & 3;
     const int kwi = blockIdx.x * 4 + ww;  // 32-key word index of this thread's keep word
     const int row0 = tid >> 3, row1 = (tid + 256) >> 3, ch = tid & 7;
@@ -565,7 +561,6 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
         po1 = *reinterpret_cast<const uint4*>(dO + (size_t)(qb * QB + row1) * D + ch * 8);
         if (tid < QB) pld = lse[qb * QB + tid];
         else if (tid < 2 * QB) pld = Dv[qb * QB + tid - QB];
-        if (a.drop.thr && a.bits && kwi < NW32) pw = a.bits[(bhbase + qb * QB + wq) * NW32 + kwi];
     };
     auto stage = [&](int qb, int buf) {
         *reinterpret_cast<uint4*>(&Qs[buf][kmaj_off(row0, ch * 8)]) = pq0;
@@ -575,15 +570,11 @@ __global__ __launch_bounds__(256, 2) void attn_bwd_dkdv_mfma(AttnArgs a) {
         if (tid < QB) lse_s[buf][tid] = pld;
         else if (tid < 2 * QB) D_s[buf][tid - QB] = pld;
         uint32_t word = 0xFFFFFFFFu;
-        if (a.drop.thr) {
-            if (a.bits) {
-                word = pw;
-            } else if (kwi < NW32) {
-                const uint64_t e0 = (bhbase + qb * QB + wq) * (uint64_t)S + kwi * 32;
-                word = 0;
+        if (a.drop.thr && kwi < NW32) {
+            const uint64_t e0 = (bhbase + qb * QB + wq) * (uint64_t)S + kwi * 32;
+            word = 0;
 #pragma unroll
-                for (int g = 0; g < 4; ++g) word |= keep8_cmp(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
-            }
+            for (int g = 0; g < 4; ++g) word |= keep8_cmp(a.drop.rng, (e0 >> 3) + g, a.drop.thr) << (8 * g);
         }
         bits_s[buf][ww][wq] = word;
     };

@@ -20,6 +20,7 @@
 #include <stdio.h>
 #include <string.h>
 #include <string>
+#include <vector>
 
 #include "../../include/tel.h"
 #include "attn.h"
@@ -92,6 +93,8 @@ struct tel_layer {
     hipEvent_t* prof_stop = nullptr;
     int prof_count = 0;
     long prof_calls = 0;
+    // optional test hook: the next training forward copies its attention keep bits here
+    uint32_t* dbg_bits = nullptr;
 };
 
 // Run one launch; if it is the profiled kernel, bracket it with the next
@@ -124,8 +127,12 @@ static void make_plan(tel_layer* L) {
     const size_t BNS = (size_t)L->B * L->NH * L->S;
     const bool inv = L->cfg.normalize_invertible != 0;
     const bool gck = L->cfg.gelu_checkpoint != 0;
+    // The 1-bit keep mask of the attention probabilities is kept only where
+    // the whole-sequence kernels run (S <= 128: B*N*S*S/8 bytes, 2 MiB per
+    // BERT-Large layer).  Longer sequences always regenerate it in the
+    // backward, so nothing the layer keeps grows with S^2.
     const bool keep_bits = L->cfg.attn_dropout > 0.0f && !L->cfg.attn_dropout_checkpoint &&
-                           L->d == 64 && L->S % 64 == 0 && L->cfg.dtype != TEL_F32;
+                           L->d == 64 && L->S % 64 == 0 && L->S <= 128 && L->cfg.dtype != TEL_F32;
     size_t sv = 0, sc = 0;
     if (keep_bits) place(p.abits, BNS * (size_t)(L->S / 32) * 4, true, sv, sc);
     if (L->cfg.pack_tokens) {
@@ -206,6 +213,9 @@ static void make_plan(tel_layer* L) {
     p.scratch_bytes = sc > fwd_scratch ? sc : fwd_scratch;
 }
 
+// smallest non-zero dropout probability a 16-bit draw realises
+constexpr float kMinDropP = 1.0f / 65536.0f;
+
 static tel_status validate_cfg(const tel_config* c) {
     if (!c) return fail(TEL_ERR_INVALID_ARG, "config is NULL");
     if (c->batch <= 0 || c->seq <= 0 || c->hidden <= 0 || c->heads <= 0)
@@ -219,6 +229,12 @@ static tel_status validate_cfg(const tel_config* c) {
     if (c->hidden > 2048) return fail(TEL_ERR_UNSUPPORTED, "hidden %d > 2048", c->hidden);
     if (!(c->attn_dropout >= 0.0f && c->attn_dropout < 1.0f) || !(c->hidden_dropout >= 0.0f && c->hidden_dropout < 1.0f))
         return fail(TEL_ERR_INVALID_ARG, "dropout probabilities must lie in [0,1)");
+    // Each element draws a 16-bit value, so the drop probability is realised
+    // as floor(p * 2^16) / 2^16: below 2^-16 that is zero, i.e. no dropout at
+    // all, which would silently differ from the p asked for.
+    if ((c->attn_dropout > 0.0f && c->attn_dropout < kMinDropP) ||
+        (c->hidden_dropout > 0.0f && c->hidden_dropout < kMinDropP))
+        return fail(TEL_ERR_UNSUPPORTED, "dropout probabilities in (0, 2^-16) cannot be realised by 16-bit draws");
     if (c->dtype != TEL_F32 && c->dtype != TEL_F16 && c->dtype != TEL_BF16)
         return fail(TEL_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
     if (!(c->ln_eps >= 0.0f)) return fail(TEL_ERR_INVALID_ARG, "ln_eps must be >= 0");
@@ -233,6 +249,34 @@ static tel_status validate_cfg(const tel_config* c) {
 
 static bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+static tel_status check_lengths_host(const int32_t* len, int B, int S) {
+    for (int b = 0; b < B; ++b)
+        if (len[b] < 1 || len[b] > S)
+            return fail(TEL_ERR_INVALID_ARG, "key_lengths[%d] = %d outside [1, %d]", b, (int)len[b], S);
+    return TEL_OK;
+}
+
+#ifdef TEL_DEBUG_CHECKS
+// Debug builds: copy the device key lengths to the host and check them
+// before any kernel reads them (this synchronises the stream).
+static tel_status debug_check_lengths(const tel_layer* L, const int32_t* key_lengths, hipStream_t st) {
+    if (!key_lengths) return TEL_OK;
+    std::vector<int32_t> h(L->B);
+    HIP_TRY(hipMemcpyAsync(h.data(), key_lengths, sizeof(int32_t) * L->B, hipMemcpyDeviceToHost, st));
+    HIP_TRY(hipStreamSynchronize(st));
+    return check_lengths_host(h.data(), L->B, L->S);
+}
+#define DEBUG_CHECK_LENGTHS(L, kl, st)                      \
+    do {                                                    \
+        tel_status ds_ = debug_check_lengths((L), (kl), (st)); \
+        if (ds_ != TEL_OK) return ds_;                      \
+    } while (0)
+#else
+#define DEBUG_CHECK_LENGTHS(L, kl, st) \
+    do {                               \
+    } while (0)
+#endif
+
 static Drop make_drop(const tel_layer* L, float p, uint32_t site, uint64_t step, int training) {
     Drop d;
     d.rng.key0 = (uint32_t)L->cfg.seed;
@@ -242,9 +286,10 @@ static Drop make_drop(const tel_layer* L, float p, uint32_t site, uint64_t step,
     d.thr = 0;
     d.scale = 1.0f;
     if (training && p > 0.0f) {
-        const double t = floor((double)p * 65536.0);
-        d.thr = (uint32_t)t;
-        d.scale = (float)(1.0 / (1.0 - (double)p));
+        // drop iff the element's 16-bit value < floor(p * 2^16) (>= 1 for every
+        // p the config accepts); kept values are scaled by 1/(1-p)
+        d.thr = (uint32_t)floor((double)p * 65536.0);
+        if (d.thr) d.scale = (float)(1.0 / (1.0 - (double)p));
     }
     return d;
 }
@@ -344,6 +389,7 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
     if (x == y) return fail(TEL_ERR_INVALID_ARG, "y must not alias x");
     hipStream_t st = (hipStream_t)stream;
+    DEBUG_CHECK_LENGTHS(L, key_lengths, st);
     const tel_config& c = L->cfg;
     const Plan& p = L->plan;
     const int H = L->H, F = L->F, dt = c.dtype;
@@ -377,9 +423,16 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     aa.ctx = bs.of(p.ctx); aa.lse = (float*)bs.of(p.lse);
     aa.bits = p.abits.used ? (uint32_t*)bs.of(p.abits) : nullptr;
     aa.packed = rinv;
+    // test hook: the keep bits this forward applies go to the caller's buffer
+    // too (written there directly when the layer keeps none of its own)
+    uint32_t* dbg_bits = d0.thr ? L->dbg_bits : nullptr;
+    L->dbg_bits = nullptr;
+    if (dbg_bits && !aa.bits) aa.bits = dbg_bits;
     // attention writes the valid tokens' rows of ctx; filler rows must be finite
     auto attn = [&]() -> hipError_t {
         hipError_t e = attn_forward(aa, st);
+        if (e == hipSuccess && dbg_bits && aa.bits != dbg_bits)
+            e = hipMemcpyAsync(dbg_bits, aa.bits, p.abits.bytes, hipMemcpyDeviceToDevice, st);
         if (e != hipSuccess || !PR) return e;
         return zero_rows(dt, aa.ctx, (int)L->valid_tokens, PR, H, st);
     };
@@ -466,6 +519,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
     if (L->pending_fwd <= 0) return fail(TEL_ERR_STATE, "backward called without a preceding forward with saved state");
     hipStream_t st = (hipStream_t)stream;
+    DEBUG_CHECK_LENGTHS(L, key_lengths, st);
     const Plan& p = L->plan;
     const int H = L->H, F = L->F, dt = c.dtype;
     Bases bs{const_cast<void*>(saved), scratch};
@@ -570,7 +624,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     auto wgrad_pair = [&](int ka, const Wg& a, int kb, const Wg& b, bool with_ln) -> tel_status {
         const GemmDesc ga = wdesc(a), gb = wdesc(b);
         if (grouped(ka, a, kb, b)) {
-            HIP_TRY(gemm_launch_group(ga, gb, st, with_ln ? ln_fin : nullptr, with_ln ? n_ln_fin : 0));
+            const int pair = ka == TEL_K_FFN2_WGRAD ? TEL_K_FFN_WGRAD_PAIR : TEL_K_ATTN_WGRAD_PAIR;
+            TIMED(pair, gemm_launch_group(ga, gb, st, with_ln ? ln_fin : nullptr, with_ln ? n_ln_fin : 0));
             if (with_ln) n_ln_fin = 0;
         } else {
             TIMED(ka, wgrad1(a));
@@ -740,6 +795,59 @@ tel_status tel_debug_dropout_mask(const tel_layer* L, int site, uint64_t step, u
     const size_t n = site == 0 ? (size_t)L->B * L->NH * L->S * L->S : (size_t)L->T * L->H;
     HIP_TRY(dropout_mask_dump(d, out_dev, n, (hipStream_t)stream));
     return TEL_OK;
+}
+
+tel_status tel_debug_attn_keep_bits(tel_layer* L, uint32_t* out_dev) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    if (!out_dev) {
+        L->dbg_bits = nullptr;
+        return TEL_OK;
+    }
+    if (!aligned(out_dev)) return fail(TEL_ERR_INVALID_ARG, "out_dev not 16-byte aligned");
+    if (L->cfg.dtype == TEL_F32 || L->d != 64 || L->S % 64)
+        return fail(TEL_ERR_UNSUPPORTED, "keep bits exist only for the MFMA attention (fp16/bf16, head width 64, "
+                                         "seq a multiple of 64)");
+    L->dbg_bits = out_dev;
+    g_err.clear();
+    return TEL_OK;
+}
+
+tel_status tel_debug_buffer(const tel_layer* L, int which, size_t* offset, size_t* bytes, int* in_saved) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    if (!offset || !bytes || !in_saved) return fail(TEL_ERR_INVALID_ARG, "output pointers must be non-NULL");
+    const Plan& p = L->plan;
+    const Buf* b = nullptr;
+    switch (which) {
+        case TEL_BUF_DROP1_IN: b = &p.dres; break;
+        case TEL_BUF_DROP1_OUT: b = &p.dz; break;
+        case TEL_BUF_DROP2_IN:
+            if (L->cfg.pre_ln) return fail(TEL_ERR_UNSUPPORTED, "Pre-LN: dropout site 2's backward input is dy itself");
+            b = &p.dres2;
+            break;
+        case TEL_BUF_DROP2_OUT: b = &p.df; break;
+        case TEL_BUF_ATTN_KEEP_BITS:
+            if (!p.abits.used) return fail(TEL_ERR_UNSUPPORTED, "this layer keeps no attention keep bits");
+            b = &p.abits;
+            break;
+        default: return fail(TEL_ERR_INVALID_ARG, "unknown buffer id %d", which);
+    }
+    *offset = b->off;
+    *bytes = b->bytes;
+    *in_saved = b->in_saved ? 1 : 0;
+    return TEL_OK;
+}
+
+tel_status tel_check_key_lengths(const int32_t* host_lengths, int32_t batch, int32_t seq) {
+    if (!host_lengths || batch <= 0 || seq <= 0) return fail(TEL_ERR_INVALID_ARG, "bad arguments");
+    return check_lengths_host(host_lengths, batch, seq);
+}
+
+int32_t tel_debug_checks_enabled(void) {
+#ifdef TEL_DEBUG_CHECKS
+    return 1;
+#else
+    return 0;
+#endif
 }
 
 double tel_pld_theta(double t, double theta_bar, double gamma) {

@@ -76,7 +76,9 @@ class _LayerFn(torch.autograd.Function):
         dev = x.device
         if valid is not None:
             B.tel_layer_set_valid_tokens(layer.handle, valid)
-        need_grad = torch.is_grad_enabled() and (x.requires_grad or any(p.requires_grad for p in params))
+        # grad mode is off inside Function.forward; whether autograd will call
+        # backward is what needs_input_grad says
+        need_grad = any(ctx.needs_input_grad)
         x = x.contiguous()
         y = torch.empty_like(x)
         saved = torch.empty(layer.saved_bytes, dtype=torch.uint8, device=dev) if need_grad else None
@@ -153,22 +155,47 @@ def pld_theta(step: int, theta_bar: float = 0.5, gamma: float = 0.001) -> float:
     return B.tel_pld_theta(step, theta_bar, gamma)
 
 
+def pld_gates(seed: int, layers: int, step: int, theta_bar: float, gamma: float):
+    """Keep decision of each of `layers` layers at this step (PLD page, "core
+    mechanism"): every layer is kept with probability theta(step), decided by
+    the counter-based gate of tel_pld_keep keyed by (seed, layer id, step)."""
+    theta = pld_theta(step, theta_bar, gamma)
+    return [B.tel_pld_keep(seed, i, step, theta) for i in range(layers)]
+
+
 class EncoderStack(torch.nn.Module):
-    def __init__(self, cfg: LayerConfig, layers: int, device="cuda", pld: Optional[tuple] = None):
+    def __init__(self, cfg: LayerConfig, layers: int, device="cuda", pld: Optional[tuple] = None,
+                 params: Optional[list] = None, layer_ids: Optional[list] = None):
+        """pld: (theta_bar, gamma) or None.  params: optional list (one per
+        layer) of dicts name -> tensor giving each layer's initial values.
+        layer_ids: the id of each layer (its dropout and PLD key; default
+        0 .. layers-1), e.g. for a stack that holds part of a model."""
         super().__init__()
+        self.layer_ids = list(range(layers)) if layer_ids is None else [int(i) for i in layer_ids]
+        assert len(self.layer_ids) == layers
         self.layers = torch.nn.ModuleList(
-            [EncoderLayer(LayerConfig(**{**cfg.__dict__, "layer_id": i}), device) for i in range(layers)])
-        self.pld = pld  # (theta_bar, gamma) or None
+            [EncoderLayer(LayerConfig(**{**cfg.__dict__, "layer_id": i}), device) for i in self.layer_ids])
+        if params is not None:
+            with torch.no_grad():
+                for layer, vals in zip(self.layers, params):
+                    for n in B.PARAM_NAMES:
+                        getattr(layer, n).copy_(vals[n])
+        self.pld = pld
         self.seed = cfg.seed
 
     def gates(self, step: int):
         if self.pld is None or not self.training:
             return [True] * len(self.layers)
         theta = pld_theta(step, *self.pld)
-        return [B.tel_pld_keep(self.seed, i, step, theta) for i in range(len(self.layers))]
+        return [B.tel_pld_keep(self.seed, i, step, theta) for i in self.layer_ids]
 
-    def forward(self, x, key_lengths=None, step: int = 0):
-        for layer, keep in zip(self.layers, self.gates(step)):
+    def forward(self, x, key_lengths=None, step: int = 0, taps: Optional[list] = None):
+        """A dropped layer is the identity: its input passes on unchanged, in
+        the forward and (through autograd) in the backward.  taps: optional
+        list that receives (layer index, input tensor) of every layer run."""
+        for i, (layer, keep) in enumerate(zip(self.layers, self.gates(step))):
             if keep:
+                if taps is not None:
+                    taps.append((i, x))
                 x = layer(x, key_lengths, step)
         return x
