@@ -164,6 +164,25 @@ tel_status tel_layer_backward(tel_layer* layer, const tel_params* params, const 
                               const void* saved, void* scratch, void* dx, const tel_grads* grads,
                               tel_stream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * inference forward (training = 0, nothing kept for a backward) of
+ * tel_layer_forward, with its workspace in a static device array of the
+ * library instead of a caller-owned scratch.  The array holds
+ * TEL_NOALLOC_MAX_BYTES (64 MiB) per device, reserved by the library on each
+ * device it runs on until the process ends; a layer whose inference forward
+ * needs more (its forward temporaries plus saved_bytes, e.g. BERT-Large
+ * shapes beyond about 1900 tokens) gets TEL_ERR_UNSUPPORTED before any GPU
+ * work.  Calls no hipMalloc / hipFree.  No kernel of that forward needs the
+ * workspace zeroed; it keeps the last call's contents.  Every call on one
+ * device shares its array: calls that overlap on one device (other streams,
+ * other threads) race and must be serialised by the caller.  x, key_lengths
+ * and y as in tel_layer_forward; y is identical to tel_layer_forward's with
+ * training = 0. */
+#define TEL_NOALLOC_MAX_BYTES (64ull << 20)
+tel_status tel_layer_forward_noalloc(tel_layer* layer, const tel_params* params, const void* x,
+                                     const int32_t* key_lengths, void* y, tel_stream_t stream);
+
 /* Token packing (pack_tokens = 1): work on padding tokens is skipped, the
  * cost the AI-infra blog describes for padded batches (sections 2.1 and 4.2,
  * dynamic padding and length bucketing).  Declares that the next forward

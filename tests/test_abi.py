@@ -263,3 +263,16 @@ def test_debug_library_builds_with_checks():
     with pytest.raises(B.TelError) as e:
         B.tel_check_key_lengths([3, 0], 2, 16, D)
     assert e.value.status == B.TEL_ERR_INVALID_ARG
+
+
+def test_noalloc_rejects_layers_beyond_its_buffer():
+    # the BERT-Large inference forward at batch 64 needs far more than the
+    # 64 MiB static workspace: refused before any HIP call
+    h = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=64, seq=128, hidden=1024, heads=16, ffn=4096))
+    try:
+        with pytest.raises(B.TelError) as e:
+            B.tel_layer_forward_noalloc(h, B.tel_params(*([4096] * 12)), 4096, None, 8192, 0)
+        assert e.value.status == B.TEL_ERR_UNSUPPORTED
+        assert "static buffer" in B.tel_last_error()
+    finally:
+        B.tel_layer_destroy(h)

@@ -24,7 +24,8 @@ PARAM_NAMES = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
                "w_1", "b_1", "w_2", "b_2", "ln2_g", "ln2_b")
 
 # every symbol declared in include/tel.h
-EXPORTS = ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward", "tel_layer_backward",
+EXPORTS = ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward", "tel_layer_forward_noalloc",
+           "tel_layer_backward",
            "tel_layer_set_valid_tokens", "tel_layer_destroy", "tel_last_error", "tel_debug_dropout_mask",
            "tel_debug_kernel_events", "tel_debug_attn_keep_bits", "tel_debug_buffer", "tel_check_key_lengths",
            "tel_debug_checks_enabled", "tel_pld_theta", "tel_pld_keep")
@@ -79,6 +80,7 @@ def lib(path: str = LIB_PATH):
         L.tel_layer_forward.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp, vp, vp]
         L.tel_layer_backward.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp, vp,
                                          vp, ctypes.POINTER(tel_grads), vp]
+        L.tel_layer_forward_noalloc.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, vp, vp]
         L.tel_layer_set_valid_tokens.argtypes = [vp, ctypes.c_int64]
         L.tel_layer_destroy.argtypes = [vp]
         L.tel_last_error.argtypes = []
@@ -96,7 +98,7 @@ def lib(path: str = LIB_PATH):
         L.tel_check_key_lengths.argtypes = [ctypes.POINTER(i32), i32, i32]
         L.tel_debug_checks_enabled.argtypes = []
         L.tel_debug_checks_enabled.restype = i32
-        for name in ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward",
+        for name in ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward", "tel_layer_forward_noalloc",
                      "tel_layer_backward", "tel_layer_set_valid_tokens", "tel_layer_destroy",
                      "tel_debug_dropout_mask", "tel_debug_kernel_events", "tel_debug_attn_keep_bits",
                      "tel_debug_buffer", "tel_check_key_lengths"):
@@ -155,6 +157,11 @@ def tel_layer_set_valid_tokens(handle: int, valid_tokens: int):
 def tel_layer_forward(handle, params: tel_params, x, key_lengths, training, step, y, saved, scratch, stream=None):
     _check(lib().tel_layer_forward(handle, ctypes.byref(params), ptr(x), ptr(key_lengths), int(training),
                                    int(step), ptr(y), ptr(saved), ptr(scratch), stream_handle(stream)))
+
+
+def tel_layer_forward_noalloc(handle, params: tel_params, x, key_lengths, y, stream=None):
+    _check(lib().tel_layer_forward_noalloc(handle, ctypes.byref(params), ptr(x), ptr(key_lengths), ptr(y),
+                                           stream_handle(stream)))
 
 
 def tel_layer_backward(handle, params: tel_params, x, key_lengths, training, step, dy, saved, scratch, dx,

@@ -19,6 +19,7 @@
 #include <new>
 #include <stdio.h>
 #include <string.h>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -73,6 +74,7 @@ struct Plan {
     // token packing: row maps and x packed (saved); y, dy, dx packed (scratch)
     Buf rmap, rinv, xp, yp, dyp, dxp;
     size_t saved_bytes = 0, scratch_bytes = 0;
+    size_t fwd_scratch_bytes = 0;  // the forward's own temporaries (a prefix of scratch)
 };
 
 constexpr size_t kAlign = 256;
@@ -211,6 +213,7 @@ static void make_plan(tel_layer* L) {
     if (sk) place(p.splitk, sk * f4, false, sv, sc);
     p.saved_bytes = sv;
     p.scratch_bytes = sc > fwd_scratch ? sc : fwd_scratch;
+    p.fwd_scratch_bytes = fwd_scratch;
 }
 
 // smallest non-zero dropout probability a 16-bit draw realises
@@ -248,6 +251,42 @@ static tel_status validate_cfg(const tel_config* c) {
 }
 
 static bool aligned(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// ------------------------------------------------------------------ static workspace
+// For callers that cannot allocate (code under graph capture, tight serving
+// loops): tel_layer_forward_noalloc runs the inference forward in this
+// file-scope device array.  Each device the library runs on holds its own
+// copy until the process ends.  In host code `scratch` is only a stand-in
+// for the symbol; its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in g_noalloc_ptr.
+constexpr size_t kNoAllocBytes = (size_t)64 << 20;
+namespace noalloc {
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+}
+constexpr int kMaxDevices = 64;
+static std::mutex g_noalloc_mu;
+static void* g_noalloc_ptr[kMaxDevices];
+
+// Bytes the inference forward (saved = NULL) uses of its scratch: the
+// forward's temporaries, then the region that holds the kept tensors.
+static size_t noalloc_need(const tel_layer* L) {
+    return align_up(L->plan.fwd_scratch_bytes) + L->plan.saved_bytes;
+}
+
+static tel_status noalloc_base(void** out) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (dev < 0 || dev >= kMaxDevices) return fail(TEL_ERR_UNSUPPORTED, "device %d beyond %d", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    if (!g_noalloc_ptr[dev]) {
+        void* p = nullptr;
+        HIP_TRY(hipGetSymbolAddress(&p, HIP_SYMBOL(noalloc::scratch)));
+        if (!p) return fail(TEL_ERR_HIP, "hipGetSymbolAddress returned NULL for the static workspace");
+        g_noalloc_ptr[dev] = p;
+    }
+    *out = g_noalloc_ptr[dev];
+    return TEL_OK;
+}
 
 static tel_status check_lengths_host(const int32_t* len, int B, int S) {
     for (int b = 0; b < B; ++b)
@@ -393,10 +432,10 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     const tel_config& c = L->cfg;
     const Plan& p = L->plan;
     const int H = L->H, F = L->F, dt = c.dtype;
-    // without a saved buffer every "saved" tensor lives in a private region of scratch
-    // placed after the scratch plan: callers that pass saved = NULL must size scratch
-    // as saved_bytes + scratch_bytes.
-    void* sv = saved ? saved : (char*)scratch + align_up(p.scratch_bytes);
+    // without a saved buffer every "saved" tensor lives in a private region of
+    // scratch placed after the forward's own temporaries; callers that pass
+    // saved = NULL size scratch as saved_bytes + scratch_bytes (at least that)
+    void* sv = saved ? saved : (char*)scratch + align_up(p.fwd_scratch_bytes);
     Bases bs{sv, scratch};
     // token packing: the layer runs on PR packed rows (x gathered, y scattered back)
     const int PR = packed_rows(L, key_lengths);
@@ -795,6 +834,21 @@ tel_status tel_debug_dropout_mask(const tel_layer* L, int site, uint64_t step, u
     const size_t n = site == 0 ? (size_t)L->B * L->NH * L->S * L->S : (size_t)L->T * L->H;
     HIP_TRY(dropout_mask_dump(d, out_dev, n, (hipStream_t)stream));
     return TEL_OK;
+}
+
+tel_status tel_layer_forward_noalloc(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
+                                     void* y, tel_stream_t stream) {
+    if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
+    const size_t need = noalloc_need(L);
+    if (need > kNoAllocBytes)
+        return fail(TEL_ERR_UNSUPPORTED,
+                    "this layer's inference forward needs %zu bytes of workspace; the static buffer holds %zu "
+                    "(use tel_layer_forward with a caller-owned scratch)",
+                    need, kNoAllocBytes);
+    void* base = nullptr;
+    tel_status s = noalloc_base(&base);
+    if (s != TEL_OK) return s;
+    return tel_layer_forward(L, P, x, key_lengths, 0, 0, y, nullptr, base, stream);
 }
 
 tel_status tel_debug_attn_keep_bits(tel_layer* L, uint32_t* out_dev) {
