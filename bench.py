@@ -306,7 +306,7 @@ def main():
     roof = roofline(sites[0])
     others = [roofline(k) for k in sites[1:]]
     shape = (f"{'BERT-Large' if w.name == 'bert_large' else w.name} layer B{w.batch} S{w.seq} H{w.hidden} "
-             f"{w.dtype.replace('f16', 'fp16')}{', token packing' if pack else ''}")
+             f"{ {'f16': 'fp16', 'bf16': 'bf16', 'f32': 'fp32'}[w.dtype]}{', token packing' if pack else ''}")
 
     out = {
         "metric": f"fwd+bwd tokens/sec and TFLOP/s (% MFMA peak), {shape}",

@@ -351,17 +351,24 @@ static hipError_t ln_backward_t(const LnBwdArgs& a, hipStream_t st) {
     switch (mode) {
 #define TEL_LNB(M) case (M): return ln_backward_m<T, (M)>(a, st);
         // Pre-LN, LN2: dx1 = dy + LN2'(da2) in fp32, drop(dx1) for the attention branch
+        // (source: the fp32 or, for fp16 layers, fp16 residual x1; or the LN output)
         TEL_LNB(LNB_SRC_F32 | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
         // Pre-LN, LN1: dx = dx1 + LN1'(da1)
         TEL_LNB(LNB_RES_F32)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_F32)
         // Post-LN, LN2: dz2 = LN2'(dy) in fp32, drop(dz2) for the FFN branch
+        // (source z2 in fp32 or fp16, or the output y)
         TEL_LNB(LNB_SRC_F32 | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_OUT_F32 | LNB_DROP)
         TEL_LNB(LNB_FROM_OUT | LNB_OUT_F32 | LNB_DROP)
         // Post-LN, LN1: dz1 = LN1'(da1 + dz2) in fp32, drop(dz1) for the attention branch
+        // (source z1 or the output x1, in fp32 or, for fp16 layers, fp16)
         TEL_LNB(LNB_SRC_F32 | LNB_ADD | LNB_OUT_F32 | LNB_DROP)
         TEL_LNB(LNB_SRC_F32 | LNB_FROM_OUT | LNB_ADD | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_ADD | LNB_OUT_F32 | LNB_DROP)
+        TEL_LNB(LNB_FROM_OUT | LNB_ADD | LNB_OUT_F32 | LNB_DROP)
 #undef TEL_LNB
     }
     return hipErrorNotSupported;

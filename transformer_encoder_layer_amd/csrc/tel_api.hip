@@ -11,8 +11,9 @@
 //                    input-gradient GEMM (with the GELU' / head-split / residual
 //                    epilogue) and a weight-gradient GEMM; bias, gamma and beta
 //                    gradients are deterministic two-stage column sums.
-// The residual stream (x1, and z1/z2 for Post-LN) is kept in fp32 so that
-// the output carries a single rounding to the storage dtype.
+// The residual stream (x1, and z1/z2 for Post-LN) is kept in fp32 for bf16
+// layers, so that their output carries a single rounding to bf16 (whose 8-bit
+// significand would otherwise round twice); fp16 layers keep it in fp16.
 #include <algorithm>
 #include <math.h>
 #include <stdarg.h>
@@ -62,10 +63,10 @@ struct Plan {
     // saved (forward -> backward)
     Buf ln1_out, mu1, rs1, qkvh, ctx, lse, mu2, rs2, ln2_out, u, g;
     Buf abits;    // attention keep bits, 1 per score (not kept under attention-dropout checkpointing)
-    Buf res1;     // Pre-LN x1 (fp32) | Post-LN z1 (fp32)
+    Buf res1;     // Pre-LN x1 | Post-LN z1 (fp32; the storage dtype for fp16 layers)
     Buf x1e;      // Post-LN LN1 output, dtype
-    Buf x1f;      // Post-LN LN1 output, fp32 (residual of the FFN branch)
-    Buf res2;     // Post-LN z2 (fp32)
+    Buf x1f;      // Post-LN LN1 output, fp32 (residual of the FFN branch; bf16 and fp32 layers)
+    Buf res2;     // Post-LN z2 (fp32; the storage dtype for fp16 layers)
     Buf ycopy;    // Post-LN output copy (invertible LN2 backward)
     // scratch (backward)
     Buf df, du, dgemm, dres, dz, dout, dvec, dqkv, dres2;
@@ -122,6 +123,9 @@ static void place(Buf& b, size_t bytes, bool saved, size_t& sv, size_t& sc) {
     top = align_up(top + bytes);
 }
 
+// Residual stream in fp32 (bf16 and fp32 layers) or in the storage dtype (fp16).
+static bool residual_f32(const tel_layer* L) { return L->cfg.dtype != TEL_F16; }
+
 static void make_plan(tel_layer* L) {
     Plan& p = L->plan;
     p = Plan();
@@ -129,6 +133,7 @@ static void make_plan(tel_layer* L) {
     const size_t BNS = (size_t)L->B * L->NH * L->S;
     const bool inv = L->cfg.normalize_invertible != 0;
     const bool gck = L->cfg.gelu_checkpoint != 0;
+    const size_t rs = residual_f32(L) ? f4 : e;  // residual stream element size
     // The 1-bit keep mask of the attention probabilities is kept only where
     // the whole-sequence kernels run (S <= 128: B*N*S*S/8 bytes, 2 MiB per
     // BERT-Large layer).  Longer sequences always regenerate it in the
@@ -150,7 +155,7 @@ static void make_plan(tel_layer* L) {
         place(p.qkvh, 3 * T * H * e, true, sv, sc);
         place(p.ctx, T * H * e, true, sv, sc);
         place(p.lse, BNS * f4, true, sv, sc);
-        place(p.res1, T * H * f4, !inv, sv, sc);
+        place(p.res1, T * H * rs, !inv, sv, sc);
         place(p.mu2, T * f4, true, sv, sc);
         place(p.rs2, T * f4, true, sv, sc);
         place(p.ln2_out, T * H * e, true, sv, sc);
@@ -160,14 +165,14 @@ static void make_plan(tel_layer* L) {
         place(p.qkvh, 3 * T * H * e, true, sv, sc);
         place(p.ctx, T * H * e, true, sv, sc);
         place(p.lse, BNS * f4, true, sv, sc);
-        place(p.res1, T * H * f4, !inv, sv, sc);
+        place(p.res1, T * H * rs, !inv, sv, sc);
         place(p.mu1, T * f4, true, sv, sc);
         place(p.rs1, T * f4, true, sv, sc);
         place(p.x1e, T * H * e, true, sv, sc);
-        place(p.x1f, T * H * f4, inv, sv, sc);
+        if (rs == f4) place(p.x1f, T * H * f4, inv, sv, sc);  // fp32 copy of x1 (FFN-branch residual)
         place(p.u, T * F * e, true, sv, sc);
         place(p.g, T * F * e, !gck, sv, sc);
-        place(p.res2, T * H * f4, !inv, sv, sc);
+        place(p.res2, T * H * rs, !inv, sv, sc);
         place(p.mu2, T * f4, true, sv, sc);
         place(p.rs2, T * f4, true, sv, sc);
         if (inv) place(p.ycopy, T * H * e, true, sv, sc);
@@ -455,6 +460,7 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     const Drop d0 = make_drop(L, c.attn_dropout, 0, step, training);
     const Drop d1 = make_drop(L, c.hidden_dropout, 1, step, training);
     const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
+    const int r32 = residual_f32(L) ? 1 : 0;
 
     AttnArgs aa{};
     aa.dtype = dt; aa.B = L->B; aa.S = L->S; aa.NH = L->NH; aa.d = L->d;
@@ -496,10 +502,10 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         TIMED(TEL_K_QKV_FWD, gemm_launch(g, st));
         TIMED(TEL_K_ATTN_FWD, attn());
         g = proj(bs.of(p.ctx), P->w_o, H, H, EPI_BIAS_DROP_RES);
-        g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_o;
+        g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = r32; g.ea.bias = P->b_o;
         g.ea.res = xin; g.ea.res_f32 = 0; g.ea.drop = d1;
         TIMED(TEL_K_OUT_FWD, gemm_launch(g, st));
-        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res1), 1, P->ln2_g, P->ln2_b, bs.of(p.ln2_out), nullptr, nullptr,
+        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res1), r32, P->ln2_g, P->ln2_b, bs.of(p.ln2_out), nullptr, nullptr,
                      (float*)bs.of(p.mu2), (float*)bs.of(p.rs2)};
         TIMED(TEL_K_LN2_FWD, ln_forward(l2, st));
         g = proj(bs.of(p.ln2_out), P->w_1, F, H, EPI_BIAS_GELU);
@@ -508,7 +514,7 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
         g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
         g.ea.out = yout; g.ea.ldo = H; g.ea.out_f32 = 0; g.ea.bias = P->b_2;
-        g.ea.res = bs.of(p.res1); g.ea.res_f32 = 1; g.ea.drop = d2;
+        g.ea.res = bs.of(p.res1); g.ea.res_f32 = r32; g.ea.drop = d2;
         TIMED(TEL_K_FFN2_FWD, gemm_launch(g, st));
     } else {
         GemmDesc g = proj(xin, P->w_qkv, 3 * H, H, EPI_QKV);
@@ -517,21 +523,21 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
         TIMED(TEL_K_QKV_FWD, gemm_launch(g, st));
         TIMED(TEL_K_ATTN_FWD, attn());
         g = proj(bs.of(p.ctx), P->w_o, H, H, EPI_BIAS_DROP_RES);
-        g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_o;
+        g.ea.out = bs.of(p.res1); g.ea.ldo = H; g.ea.out_f32 = r32; g.ea.bias = P->b_o;
         g.ea.res = xin; g.ea.res_f32 = 0; g.ea.drop = d1;
         TIMED(TEL_K_OUT_FWD, gemm_launch(g, st));
-        LnFwdArgs l1{dt, T, H, c.ln_eps, bs.of(p.res1), 1, P->ln1_g, P->ln1_b, bs.of(p.x1e),
-                     (float*)bs.of(p.x1f), nullptr, (float*)bs.of(p.mu1), (float*)bs.of(p.rs1)};
+        LnFwdArgs l1{dt, T, H, c.ln_eps, bs.of(p.res1), r32, P->ln1_g, P->ln1_b, bs.of(p.x1e),
+                     p.x1f.used ? (float*)bs.of(p.x1f) : nullptr, nullptr, (float*)bs.of(p.mu1), (float*)bs.of(p.rs1)};
         TIMED(TEL_K_LN1_FWD, ln_forward(l1, st));
         g = proj(bs.of(p.x1e), P->w_1, F, H, EPI_BIAS_GELU);
         g.ea.out = bs.of(p.u); g.ea.ldo = F; g.ea.bias = P->b_1; g.ea.out2 = bs.of(p.g);
         g.ea.gelu_grad_out = !c.gelu_checkpoint;
         TIMED(TEL_K_FFN1_FWD, gemm_launch(g, st));
         g = proj(bs.of(p.g), P->w_2, H, F, EPI_BIAS_DROP_RES);
-        g.ea.out = bs.of(p.res2); g.ea.ldo = H; g.ea.out_f32 = 1; g.ea.bias = P->b_2;
-        g.ea.res = bs.of(p.x1f); g.ea.res_f32 = 1; g.ea.drop = d2;
+        g.ea.out = bs.of(p.res2); g.ea.ldo = H; g.ea.out_f32 = r32; g.ea.bias = P->b_2;
+        g.ea.res = r32 ? bs.of(p.x1f) : bs.of(p.x1e); g.ea.res_f32 = r32; g.ea.drop = d2;
         TIMED(TEL_K_FFN2_FWD, gemm_launch(g, st));
-        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res2), 1, P->ln2_g, P->ln2_b, yout, nullptr,
+        LnFwdArgs l2{dt, T, H, c.ln_eps, bs.of(p.res2), r32, P->ln2_g, P->ln2_b, yout, nullptr,
                      p.ycopy.used ? bs.of(p.ycopy) : nullptr, (float*)bs.of(p.mu2), (float*)bs.of(p.rs2)};
         TIMED(TEL_K_LN2_FWD, ln_forward(l2, st));
     }
@@ -580,6 +586,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     const Drop d2 = make_drop(L, c.hidden_dropout, 2, step, training);
     const bool inv = c.normalize_invertible != 0;
     const bool gck = c.gelu_checkpoint != 0;
+    const int r32 = residual_f32(L) ? 1 : 0;
     // LN1's and LN2's gamma/beta partial rows (separate buffers: both are
     // finalized at the end, with the last weight-gradient pair when it runs)
     const int lnP = ln_backward_parts(T);
@@ -718,7 +725,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         LnBwdArgs lb{};
         lb.dtype = dt; lb.T = T; lb.H = H;
         lb.dout = bs.of(p.dgemm);
-        lb.src = inv ? bs.of(p.ln2_out) : bs.of(p.res1); lb.src_f32 = inv ? 0 : 1; lb.from_output = inv;
+        lb.src = inv ? bs.of(p.ln2_out) : bs.of(p.res1); lb.src_f32 = inv ? 0 : r32; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
         lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
         lb.res = dyin; lb.res_f32 = 0;
@@ -759,7 +766,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         LnBwdArgs lb{};
         lb.dtype = dt; lb.T = T; lb.H = H;
         lb.dout = dyin;
-        lb.src = inv ? bs.of(p.ycopy) : bs.of(p.res2); lb.src_f32 = inv ? 0 : 1; lb.from_output = inv;
+        lb.src = inv ? bs.of(p.ycopy) : bs.of(p.res2); lb.src_f32 = inv ? 0 : r32; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
         lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
         lb.out = bs.of(p.dres2); lb.out_f32 = 1;
@@ -781,7 +788,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb = LnBwdArgs{};
         lb.dtype = dt; lb.T = T; lb.H = H;
         lb.dout = bs.of(p.dgemm); lb.dout_add = (const float*)bs.of(p.dres2);
-        lb.src = inv ? bs.of(p.x1f) : bs.of(p.res1); lb.src_f32 = 1; lb.from_output = inv;
+        lb.src = inv ? (r32 ? bs.of(p.x1f) : bs.of(p.x1e)) : bs.of(p.res1); lb.src_f32 = r32; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu1); lb.rstd = (const float*)bs.of(p.rs1);
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
         lb.out = bs.of(p.dres); lb.out_f32 = 1;
