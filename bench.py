@@ -153,6 +153,8 @@ def main():
                     help="further call sites timed (comma-separated), each on its own share of the layers")
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle sample (BERT-Large: the whole batch, about 10 s on 16 host threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stochastic", action="store_true",
+                    help="relaxed-determinism mode (the weight-gradient pairs add their k-splits atomically)")
     ap.add_argument("--pack", action="store_true",
                     help="token packing: run the layers on the valid tokens of a padded workload")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -185,7 +187,8 @@ def main():
     for l in range(n_layers):
         cfg = LayerConfig(w.batch, w.seq, w.hidden, w.heads, w.ffn, float(np.float32(w.attn_p)),
                           float(np.float32(w.hidden_p)), w.pre_ln, w.seed, l, dt, 1e-12,
-                          w.attn_dropout_checkpoint, w.normalize_invertible, w.gelu_checkpoint, pack_tokens=pack)
+                          w.attn_dropout_checkpoint, w.normalize_invertible, w.gelu_checkpoint, pack_tokens=pack,
+                          stochastic_mode=args.stochastic)
         h = B.tel_layer_create(cfg.to_c())
         if pack:
             B.tel_layer_set_valid_tokens(h, valid)
@@ -325,7 +328,8 @@ def main():
                                f"ffn {w.ffn}, {'Pre' if w.pre_ln else 'Post'}-LN, {w.dtype}, dropout "
                                f"{w.attn_p}/{w.hidden_p}, {n_layers}-layer stack"
                                + (f", PLD theta={theta:.5f} keeps {n_run}" if w.pld else "")
-                               + (f", token packing ({valid} valid of {T} tokens)" if pack else ""),
+                               + (f", token packing ({valid} valid of {T} tokens)" if pack else "")
+                               + (", stochastic mode" if args.stochastic else ""),
                    "batch": w.batch, "seq_len": w.seq, "hidden": w.hidden, "heads": w.heads, "ffn": w.ffn,
                    "layers": n_layers, "layers_run": n_run, "parallelism": "single GPU"},
         "tflops": round(tflops, 1),

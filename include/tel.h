@@ -114,6 +114,15 @@ typedef struct {
     int32_t gelu_checkpoint;       /* keep the GELU input only; recompute GELU in backward */
     int32_t pack_tokens;           /* run the layer on the valid tokens only (see
                                       tel_layer_set_valid_tokens) */
+    int32_t stochastic_mode;       /* relaxed determinism for speed (the DeepSpeed guide's
+                                      stochastic_mode switch): the grouped weight-gradient
+                                      launches add their k-splits into the zeroed gradients
+                                      with packed fp16/bf16 atomics instead of reducing fp32
+                                      partials in fixed order.  Those weight and bias
+                                      gradients then carry one dtype rounding per split, and
+                                      with more than two splits their last bits may differ
+                                      from run to run; every other output keeps its bits.
+                                      0 (default): every output is bitwise reproducible. */
 } tel_config;
 
 /* The twelve parameters, nn.Linear layout, dtype cfg.dtype, device memory:

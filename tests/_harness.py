@@ -61,7 +61,8 @@ def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=
                       float(np.float32(w.hidden_p)), w.pre_ln, w.seed, layer_id, syn.torch_dtype(w.dtype),
                       1e-12, bool(sw.get("attn_dropout_checkpoint", w.attn_dropout_checkpoint)),
                       bool(sw.get("normalize_invertible", w.normalize_invertible)),
-                      bool(sw.get("gelu_checkpoint", w.gelu_checkpoint)), pack_tokens=pack)
+                      bool(sw.get("gelu_checkpoint", w.gelu_checkpoint)), pack_tokens=pack,
+                      stochastic_mode=bool(sw.get("stochastic_mode", False)))
     h = B.tel_layer_create(cfg.to_c())
     try:
         saved_b, scratch_b = B.tel_layer_workspace_bytes(h)

@@ -38,7 +38,7 @@ def test_library_exports_every_symbol():
 def cfg(**kw):
     base = dict(batch=2, seq=16, hidden=64, heads=4, ffn=256, attn_dropout=0.0, hidden_dropout=0.0, pre_ln=1,
                 seed=1234, layer_id=0, dtype=B.TEL_F32, ln_eps=1e-12, attn_dropout_checkpoint=0,
-                normalize_invertible=0, gelu_checkpoint=0, pack_tokens=0)
+                normalize_invertible=0, gelu_checkpoint=0, pack_tokens=0, stochastic_mode=0)
     base.update(kw)
     return B.tel_config(*[base[f] for f, _ in B.tel_config._fields_])
 
@@ -276,3 +276,14 @@ def test_noalloc_rejects_layers_beyond_its_buffer():
         assert "static buffer" in B.tel_last_error()
     finally:
         B.tel_layer_destroy(h)
+
+
+def test_stochastic_mode_is_a_plain_switch():
+    # relaxed determinism changes no shape or workspace
+    a = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=64, seq=128, hidden=1024, heads=16, ffn=4096))
+    b = B.tel_layer_create(cfg(dtype=B.TEL_F16, batch=64, seq=128, hidden=1024, heads=16, ffn=4096, stochastic_mode=1))
+    try:
+        assert B.tel_layer_workspace_bytes(a) == B.tel_layer_workspace_bytes(b)
+    finally:
+        B.tel_layer_destroy(a)
+        B.tel_layer_destroy(b)

@@ -53,7 +53,8 @@ class tel_config(ctypes.Structure):
                 ("pre_ln", ctypes.c_int32), ("seed", ctypes.c_uint64), ("layer_id", ctypes.c_int32),
                 ("dtype", ctypes.c_int32), ("ln_eps", ctypes.c_float),
                 ("attn_dropout_checkpoint", ctypes.c_int32), ("normalize_invertible", ctypes.c_int32),
-                ("gelu_checkpoint", ctypes.c_int32), ("pack_tokens", ctypes.c_int32)]
+                ("gelu_checkpoint", ctypes.c_int32), ("pack_tokens", ctypes.c_int32),
+                ("stochastic_mode", ctypes.c_int32)]
 
 
 class tel_params(ctypes.Structure):

@@ -22,6 +22,7 @@ enum EpiKind {
     EPI_HEADSPLIT = 5,     // v scattered to [B][N][S][d]
     EPI_ADD_RES = 6,       // out = v + res(f32)
     EPI_MUL_AUX = 7,       // out = v * aux                         (aux T)
+    EPI_ATOMIC_ADD = 8,    // out += v with packed dtype atomics (k-splits of a relaxed-determinism launch)
 };
 
 struct EpiArgs {
@@ -57,6 +58,10 @@ struct GemmDesc {
     EpiArgs ea;
     float* splitk_ws = nullptr;  // fp32 [splits][M][N] partials (+ [splits][M] row sums)
     size_t splitk_ws_elems = 0;
+    // Grouped weight gradients only: the k-splits add their partials (and row
+    // sums) into the zeroed outputs with packed dtype atomics -- no workspace,
+    // no reduction launch, but a summation order that follows arrival.
+    bool splitk_atomic = false;
     // Optional row sums of A over k (sum_k A(m,k), dtype, M values): for a
     // weight gradient dW = dY^T X these are the bias gradients sum_t dY[t][m].
     // Only computed when gemm_rowsum_fused() is true; the caller sums

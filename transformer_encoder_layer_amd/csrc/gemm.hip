@@ -22,6 +22,23 @@
 namespace tel {
 
 // ------------------------------------------------------------------ epilogue
+// out[0..1] += (v0, v1) rounded to T, as one packed atomic add (the pair
+// must be 4-byte aligned).
+__device__ __forceinline__ void atomic_add2(float* out, float v0, float v1) {
+    atomicAdd(out, v0);
+    atomicAdd(out + 1, v1);
+}
+__device__ __forceinline__ void atomic_add2(f16* out, float v0, float v1) {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    __builtin_amdgcn_global_atomic_fadd_v2f16((h2 __attribute__((address_space(1)))*)out, (h2){(f16)v0, (f16)v1});
+}
+__device__ __forceinline__ void atomic_add2(bf16* out, float v0, float v1) {
+    typedef short s2 __attribute__((ext_vector_type(2)));
+    const bf16 a = (bf16)v0, b = (bf16)v1;
+    __builtin_amdgcn_global_atomic_fadd_v2bf16((s2 __attribute__((address_space(1)))*)out,
+                                               (s2){__builtin_bit_cast(short, a), __builtin_bit_cast(short, b)});
+}
+
 // Each epilogue works on 4 consecutive columns n..n+3 of row m.  It is split
 // into loads (per-column bias, per-element residual / GELU input) and the
 // compute-and-store, so that a kernel can issue every load of a block of
@@ -166,6 +183,9 @@ struct Epi {
 #pragma unroll
             for (int i = 0; i < 4; ++i) v[i] += r[i];
             Vec4<T>::store((T*)e.out + off, v);
+        } else if constexpr (EPI == EPI_ATOMIC_ADD) {
+            atomic_add2((T*)e.out + off, v[0], v[1]);
+            atomic_add2((T*)e.out + off + 2, v[2], v[3]);
         }
     }
 };
@@ -188,6 +208,7 @@ struct GemmParams {
     EpiArgs ea;
     float* ws;        // split-K partials, [splits][M][N]
     void* rsum;       // row sums of A: dtype [M] (one split) or fp32 [splits][M] after ws
+    void* rsum_out = nullptr;  // dtype [M] row sums, for splits that add into it atomically
 };
 
 // One or two GEMMs of the same tile shape run by one persistent launch: the
@@ -197,6 +218,10 @@ struct GemmGroup {
     int splits[2];
     int units0;  // units of problem 0 (its tiles x splits)
     int units;   // all units
+    // Relaxed-determinism weight gradients: every k-split adds its partial
+    // tile (and row sums) to the zeroed outputs with packed dtype atomics
+    // instead of writing fp32 partials for a separate reduction.
+    int atomic;
 };
 
 // ------------------------------------------------------------------ MFMA path
@@ -1054,6 +1079,7 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
 #undef TEL_DL4_BLOCK
         __syncthreads();
 
+        const bool atomic = !AK && EPI == EPI_STORE && nsplit > 1 && G.atomic;
         if constexpr (!AK) {
             if (p.rsum != nullptr && in_ == 0) {
                 // lanes l and l + 32 hold the two k halves of row l; waves with
@@ -1061,12 +1087,27 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
 #pragma unroll
                 for (int i = 0; i < MI; ++i) {
                     const float t = rsa[i] + __shfl_xor(rsa[i], 32, 64);
+                    const float t1 = __shfl_down(t, 1, 64);  // row l + 1's sum, for the packed add
                     if (wn == 0 && lane < 32) {
                         const int mrow = m0 + wm * WM + i * 32 + lane;
-                        if (nsplit > 1) reinterpret_cast<float*>(p.rsum)[(size_t)split * p.M + mrow] = t;
-                        else reinterpret_cast<T*>(p.rsum)[mrow] = from_f<T>(t);
+                        if (atomic) {
+                            if (!(lane & 1)) atomic_add2(reinterpret_cast<T*>(p.rsum_out) + mrow, t, t1);
+                        } else if (nsplit > 1) {
+                            reinterpret_cast<float*>(p.rsum)[(size_t)split * p.M + mrow] = t;
+                        } else {
+                            reinterpret_cast<T*>(p.rsum)[mrow] = from_f<T>(t);
+                        }
                     }
                 }
+            }
+        }
+        if constexpr (!AK && EPI == EPI_STORE) {
+            if (atomic) {
+                // staged through LDS like a plain store, so that each packed
+                // atomic instruction covers contiguous row segments
+                gemm_epilogue_impl<T, EPI_ATOMIC_ADD, BM, BN, 2, 2, false>(p, acc, smem_raw, m0, n0, wm, wn, wave,
+                                                                          lane, 0, 1);
+                continue;
             }
         }
         gemm_epilogue<T, EPI, BM, BN, 2, 2>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, split, nsplit);
@@ -1141,6 +1182,32 @@ __global__ __launch_bounds__(256) void splitk_reduce_pair_kernel(ReduceJob a, Re
     const ReduceJob& j = second ? b : a;
     const size_t i4 = ((size_t)(bid - (second ? blocks0 : 0u)) * blockDim.x + threadIdx.x) * 4;
     splitk_reduce_body<T>(i4, j.ws, splits, j.M, j.N, j.ea, j.rs_part, reinterpret_cast<T*>(j.rs_out));
+}
+
+// Relaxed-determinism pairs: zero the outputs the k-splits add into (regions
+// of 16-byte multiples), then the column sums riding along, in one launch
+// before the grouped weight-gradient launch.
+struct ZeroJobs {
+    void* p[4];
+    size_t n16[4];  // 16-byte units
+    int n;
+};
+template <typename T>
+__global__ __launch_bounds__(256) void zero_colsum_kernel(ZeroJobs z, unsigned zero_blocks, ColsumJobs cs) {
+    if (blockIdx.x < zero_blocks) {
+        const size_t stride = (size_t)zero_blocks * 256;
+        for (int r = 0; r < z.n; ++r) {
+            uint4* q = reinterpret_cast<uint4*>(z.p[r]);
+            for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < z.n16[r]; i += stride)
+                q[i] = make_uint4(0u, 0u, 0u, 0u);
+        }
+        return;
+    }
+    __shared__ float red[32][9];
+    const unsigned bid = blockIdx.x - zero_blocks;
+    const int job = (int)(bid / (unsigned)cs.blocks), n0 = (int)(bid % (unsigned)cs.blocks) * 8;
+    const ColsumJob& c = cs.j[job];
+    if (n0 < c.N) colsum8_block<T>(c.part, c.P, c.N, reinterpret_cast<T*>(c.out), n0, red);  // block-uniform
 }
 
 // ------------------------------------------------------------------ SIMT path
@@ -1435,6 +1502,15 @@ size_t gemm_splitk_group_elems(const GemmDesc& a, const GemmDesc& b) {
 bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b) {
     const int s = group_splits(a, b);
     if (s == 0) return false;
+    if (a.splitk_atomic != b.splitk_atomic) return false;
+    if (a.splitk_atomic) {
+        // packed adds need 4-byte aligned pairs and whole 16-byte outputs to zero
+        auto ok = [](const GemmDesc& g) {
+            return g.ea.ldo == g.N && ((uintptr_t)g.ea.out & 15) == 0 && (g.rowsum_out == nullptr ||
+                   (((uintptr_t)g.rowsum_out & 15) == 0 && (g.M * 2) % 16 == 0));
+        };
+        return ok(a) && ok(b);
+    }
     if (s > 1 && (a.splitk_ws == nullptr || gemm_splitk_group_elems(a, b) > a.splitk_ws_elems)) return false;
     return true;
 }
@@ -1456,6 +1532,29 @@ static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStre
     G.units0 = (a.M / BM) * (a.N / BN) * splits;
     G.units = G.units0 + (b.M / BM) * (b.N / BN) * splits;
     const int gx = std::min(G.units, std::max(8, slots / 8 * 8));
+    if (splits > 1 && a.splitk_atomic) {
+        // the k-splits add into the zeroed outputs; the column sums ride with the zeroing
+        G.atomic = 1;
+        G.p[0].rsum_out = a.rowsum_out;
+        G.p[1].rsum_out = b.rowsum_out;
+        ZeroJobs z{};
+        auto add = [&](void* ptr, size_t bytes) {
+            if (ptr) {
+                z.p[z.n] = ptr;
+                z.n16[z.n++] = bytes / 16;
+            }
+        };
+        add(a.ea.out, (size_t)a.M * a.N * sizeof(T));
+        add(b.ea.out, (size_t)b.M * b.N * sizeof(T));
+        add(a.rowsum_out, (size_t)a.M * sizeof(T));
+        add(b.rowsum_out, (size_t)b.M * sizeof(T));
+        const unsigned zb = 512;
+        hipLaunchKernelGGL(zero_colsum_kernel<T>, dim3(zb + (unsigned)(cs.n * cs.blocks)), dim3(256), 0, st, z, zb, cs);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || (splits == 1 && cs.n == 0)) return e;

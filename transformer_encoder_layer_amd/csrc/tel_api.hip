@@ -631,6 +631,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g.epi = EPI_STORE;
         g.ea.out = w.dW; g.ea.ldo = w.in;
         g.splitk_ws = skws; g.splitk_ws_elems = skn;
+        g.splitk_atomic = c.stochastic_mode != 0;  // honoured by grouped launches only
         if (gemm_rowsum_fused(g)) g.rowsum_out = w.db;
         return g;
     };

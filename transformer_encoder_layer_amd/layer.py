@@ -44,13 +44,14 @@ class LayerConfig:
     normalize_invertible: bool = False
     gelu_checkpoint: bool = False
     pack_tokens: bool = False
+    stochastic_mode: bool = False
 
     def to_c(self) -> B.tel_config:
         return B.tel_config(self.batch, self.seq, self.hidden, self.heads, self.ffn, self.attn_dropout,
                             self.hidden_dropout, int(self.pre_ln), self.seed, self.layer_id,
                             _DTYPES[self.dtype], self.ln_eps, int(self.attn_dropout_checkpoint),
                             int(self.normalize_invertible), int(self.gelu_checkpoint),
-                            int(self.pack_tokens))
+                            int(self.pack_tokens), int(self.stochastic_mode))
 
 
 _scratch = {}
