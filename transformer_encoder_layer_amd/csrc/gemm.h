@@ -53,7 +53,6 @@ struct GemmDesc {
     const void* B = nullptr;
     int ldb = 0;
     bool b_kmajor = true;
-    bool b_gelu = false;  // B elements pass through GELU on load
     int epi = EPI_STORE;
     EpiArgs ea;
     float* splitk_ws = nullptr;  // fp32 [splits][M][N] partials (+ [splits][M] row sums)
@@ -72,7 +71,7 @@ struct GemmDesc {
 // True if gemm_launch computes rowsum_out for this GEMM inside its kernel.
 bool gemm_rowsum_fused(const GemmDesc& g);
 
-// Two weight gradients (A and B m/n-major, EPI_STORE, no GELU on load, M
+// Two weight gradients (A and B m/n-major, EPI_STORE, M
 // and N multiples of 256) in one persistent launch, so that the tiles of
 // both fill the chip with fewer k-splits than either alone; a's workspace
 // (splitk_ws, splitk_ws_elems) holds the partials of both.  Row sums are

@@ -149,8 +149,8 @@ struct Epi {
                 const float u = round_through<T>(v[i] + b[i]);
                 float cdf, pdf;
                 normal_cdf_pdf(u, cdf, pdf);
-                g[i] = __fmul_rn(u, cdf);               // gelu_f(u)
-                d[i] = e.gelu_grad_out ? __fmaf_rn(u, pdf, cdf) : u;  // gelu_grad_f(u) or u
+                g[i] = __fmul_rn(u, cdf);               // GELU(u)
+                d[i] = e.gelu_grad_out ? __fmaf_rn(u, pdf, cdf) : u;  // GELU'(u) or u
             }
             Vec4<T>::store((T*)e.out + off, d);
             if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
@@ -158,14 +158,14 @@ struct Epi {
             // GELU'(u) rounded to the storage type, exactly as the forward
             // stores it when GELU is not checkpointed (EPI_MUL_AUX path); with
             // out2, also GELU(u) (the W2 weight gradient's operand), the same
-            // bits as gelu_f and as the forward's stored GELU(u)
+            // bits as the forward's stored GELU(u)
             float g[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 float cdf, pdf;
                 normal_cdf_pdf(r[i], cdf, pdf);
-                v[i] *= round_through<T>(__fmaf_rn(r[i], pdf, cdf));  // gelu_grad_f(u)
-                g[i] = __fmul_rn(r[i], cdf);                          // gelu_f(u)
+                v[i] *= round_through<T>(__fmaf_rn(r[i], pdf, cdf));  // GELU'(u)
+                g[i] = __fmul_rn(r[i], cdf);                          // GELU(u)
             }
             Vec4<T>::store((T*)e.out + off, v);
             if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
@@ -225,94 +225,7 @@ struct GemmGroup {
 };
 
 // ------------------------------------------------------------------ MFMA path
-constexpr int KT = 64;        // k tile (elements)
-// Padding (elements) of m/n-major LDS rows: rows of 128 or 256 elements
-// then start 64 bytes apart modulo 256, so the four rows of a transposing
-// read of two 16-lane groups (32 bytes each) land in distinct banks.
-constexpr int MN_PAD = 32;
-
-template <bool KMAJ, int R>
-struct TileGeom {
-    static constexpr int ELEMS = KMAJ ? R * KT : KT * (R + MN_PAD);
-    static constexpr int CHUNKS = R * KT / 8;  // 16-byte chunks per tile
-};
-
-// Fragment for a 32x32x16 MFMA operand: lane l gets rows rb + (l & 31),
-// k = ks*16 + 8*(l >> 5) .. +7.
-template <typename T, bool KMAJ, int R>
-__device__ __forceinline__ typename MfmaOp<T>::v8 frag_load(const T* lds, int rb, int ks, int lane) {
-    if constexpr (KMAJ) {
-        return frag_kmaj<T>(lds, rb, ks, lane);
-    } else {
-        const int kb = ks * 16 + (lane >> 5) * 8;
-        return frag_tr<T>(lds, R + MN_PAD, rb, kb, kb + 4, lane);
-    }
-}
-
-// Load one operand tile (R rows of the m or n dimension, KT of k) from global
-// into registers: CPT chunks of 8 elements per thread.
-template <typename T, bool KMAJ, int R, int NT>
-__device__ __forceinline__ void tile_load(uint4* reg, const T* base, int ld,
-                                          int row0, int k0, int tid) {
-    constexpr int CPT = TileGeom<KMAJ, R>::CHUNKS / NT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int c = tid + i * NT;
-        if constexpr (KMAJ) {
-            const int row = c >> 3, ch = c & 7;
-            reg[i] = *reinterpret_cast<const uint4*>(base + (size_t)(row0 + row) * ld + k0 + ch * 8);
-        } else {
-            constexpr int CPR = R / 8;  // chunks per k row
-            const int kr = c / CPR, ch = c - kr * CPR;
-            reg[i] = *reinterpret_cast<const uint4*>(base + (size_t)(k0 + kr) * ld + row0 + ch * 8);
-        }
-    }
-}
-
-template <typename T>
-__device__ __forceinline__ uint4 gelu_chunk(uint4 u) {
-    typedef T v8 __attribute__((ext_vector_type(8)));
-    v8 x = *reinterpret_cast<v8*>(&u);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) x[i] = from_f<T>(gelu_f(to_f(x[i])));
-    return *reinterpret_cast<uint4*>(&x);
-}
-
-template <typename T, bool KMAJ, int R, int NT, bool GELU>
-__device__ __forceinline__ void tile_store(T* lds, const uint4* reg, int tid) {
-    constexpr int CPT = TileGeom<KMAJ, R>::CHUNKS / NT;
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const int c = tid + i * NT;
-        uint4 val = reg[i];
-        if constexpr (GELU) val = gelu_chunk<T>(val);
-        if constexpr (KMAJ) {
-            const int row = c >> 3, ch = c & 7;
-            *reinterpret_cast<uint4*>(lds + kmaj_off(row, ch * 8)) = val;
-        } else {
-            constexpr int CPR = R / 8;
-            const int kr = c / CPR, ch = c - kr * CPR;
-            *reinterpret_cast<uint4*>(lds + kr * (R + MN_PAD) + ch * 8) = val;
-        }
-    }
-}
-
-// Per-thread partial row sums of an m-major A tile: with R/8 chunks per k row
-// and NT a multiple of R/8, thread tid always loads the chunk of rows
-// 8*(tid % (R/8)) .. +7, so it can add up the 8 values of every chunk it
-// loads over the whole k range (fixed order).
-template <typename T, int R, int NT>
-__device__ __forceinline__ void rowsum_acc(float (&rs)[8], const uint4* reg) {
-    constexpr int CPT = TileGeom<false, R>::CHUNKS / NT;
-    typedef T v8 __attribute__((ext_vector_type(8)));
-#pragma unroll
-    for (int i = 0; i < CPT; ++i) {
-        const uint4 u = reg[i];
-        const v8 x = *reinterpret_cast<const v8*>(&u);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) rs[e] += to_f(x[e]);
-    }
-}
+constexpr int KT = 64;  // k granularity the MFMA kernels need of K
 
 // Map the linear workgroup id to an output tile.  Consecutive ids are
 // dispatched round-robin over the 8 XCDs; the remap gives each XCD one
@@ -468,121 +381,6 @@ __device__ __forceinline__ void gemm_epilogue(const GemmParams& p, f32x16 (&acc)
         }
     }
     gemm_epilogue_impl<T, EPI, BM, BN, WGM, WGN, false>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, split, nsplit);
-}
-
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
-__global__ __launch_bounds__(WGM* WGN * 64) void gemm_mfma_kernel(GemmParams p) {
-    constexpr int NT = WGM * WGN * 64;
-    constexpr int WM = BM / WGM, WN = BN / WGN;
-    constexpr int MI = WM / 32, NI = WN / 32;
-    typedef TileGeom<AK, BM> GA;
-    typedef TileGeom<BKM, BN> GB;
-    constexpr int STAGE = GA::ELEMS + GB::ELEMS;
-    static_assert(GA::CHUNKS % NT == 0 && GB::CHUNKS % NT == 0, "tile/thread mismatch");
-    typedef typename MfmaOp<T>::v8 v8;
-
-    extern __shared__ __align__(16) unsigned char smem_raw[];
-    T* smem = reinterpret_cast<T*>(smem_raw);
-
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave / WGN, wn = wave % WGN;
-    const int tm = p.M / BM, tn = p.N / BN;
-    int im, in_;
-    tile_of(blockIdx.x, tm, tn, im, in_);
-    const int m0 = im * BM, n0 = in_ * BN;
-    const int kbeg = blockIdx.z * p.k_per_split;
-    const int kend = min(p.K, kbeg + p.k_per_split);
-    const int nk = (kend - kbeg) / KT;
-
-    const T* A = (const T*)p.A;
-    const T* B = (const T*)p.B;
-
-    f32x16 acc[MI][NI];
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NI; ++j)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-    // bias gradient fused into a weight gradient: the workgroups of tile
-    // column 0 also sum their A rows (uniform branch per workgroup)
-    const bool do_rsum = !AK && p.rsum != nullptr && in_ == 0;
-    float rs[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-
-    uint4 ra[GA::CHUNKS / NT], rb[GB::CHUNKS / NT];
-    tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg, tid);
-    tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg, tid);
-    if constexpr (!AK) {
-        if (do_rsum) rowsum_acc<T, BM, NT>(rs, ra);
-    }
-    tile_store<T, AK, BM, NT, false>(smem, ra, tid);
-    tile_store<T, BKM, BN, NT, BGELU>(smem + GA::ELEMS, rb, tid);
-    __syncthreads();
-
-    // Double-buffered LDS: the global loads of k-tile kt+1 are issued before
-    // the MFMAs of tile kt and written to the other buffer after them.
-    for (int kt = 0; kt < nk; ++kt) {
-        const T* sa = smem + (kt & 1) * STAGE;
-        const T* sb = sa + GA::ELEMS;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            tile_load<T, AK, BM, NT>(ra, A, p.lda, m0, kbeg + (kt + 1) * KT, tid);
-            tile_load<T, BKM, BN, NT>(rb, B, p.ldb, n0, kbeg + (kt + 1) * KT, tid);
-        }
-#pragma unroll
-        for (int ks = 0; ks < KT / 16; ++ks) {
-            v8 fa[MI], fb[NI];
-#pragma unroll
-            for (int i = 0; i < MI; ++i) fa[i] = frag_load<T, AK, BM>(sa, wm * WM + i * 32, ks, lane);
-#pragma unroll
-            for (int j = 0; j < NI; ++j) fb[j] = frag_load<T, BKM, BN>(sb, wn * WN + j * 32, ks, lane);
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
-        }
-        if (more) {
-            if constexpr (!AK) {
-                if (do_rsum) rowsum_acc<T, BM, NT>(rs, ra);
-            }
-            T* da = smem + ((kt + 1) & 1) * STAGE;
-            tile_store<T, AK, BM, NT, false>(da, ra, tid);
-            tile_store<T, BKM, BN, NT, BGELU>(da + GA::ELEMS, rb, tid);
-        }
-        __syncthreads();
-    }
-
-    if constexpr (!AK) {
-        if (do_rsum) {
-            // threads tid, tid + R/8, tid + 2R/8, ... hold the same 8 rows:
-            // add them in that order through LDS (free after the main loop)
-            constexpr int CPR = BM / 8;
-            float* red = reinterpret_cast<float*>(smem_raw);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) red[tid * 8 + e] = rs[e];
-            __syncthreads();
-            if (tid < CPR) {
-                float t[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-                for (int q = tid; q < NT; q += CPR)
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) t[e] += red[q * 8 + e];
-                const int mrow = m0 + tid * 8;
-                if (gridDim.z > 1) {
-                    float* out = reinterpret_cast<float*>(p.rsum) + (size_t)blockIdx.z * p.M + mrow;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) out[e] = t[e];
-                } else {
-                    T* out = reinterpret_cast<T*>(p.rsum) + mrow;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) out[e] = from_f<T>(t[e]);
-                }
-            }
-            __syncthreads();
-        }
-    }
-
-    gemm_epilogue<T, EPI, BM, BN, WGM, WGN>(p, acc, smem_raw, m0, n0, wm, wn, wave, lane, blockIdx.z, gridDim.z);
 }
 
 // ------------------------------------------------------------------ direct-load path
@@ -1211,7 +1009,7 @@ __global__ __launch_bounds__(256) void zero_colsum_kernel(ZeroJobs z, unsigned z
 }
 
 // ------------------------------------------------------------------ SIMT path
-template <typename T, int EPI, bool BGELU>
+template <typename T, int EPI>
 __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmParams p, int a_kmajor, int b_kmajor) {
     constexpr int TB = 64, TK = 16;
     __shared__ float As[TK][TB + 1];
@@ -1227,10 +1025,7 @@ __global__ __launch_bounds__(256) void gemm_simt_kernel(GemmParams p, int a_kmaj
             const int m = m0 + r, n = n0 + r, k = k0 + kk;
             float av = 0.f, bv = 0.f;
             if (m < p.M && k < p.K) av = to_f(a_kmajor ? A[(size_t)m * p.lda + k] : A[(size_t)k * p.lda + m]);
-            if (n < p.N && k < p.K) {
-                bv = to_f(b_kmajor ? B[(size_t)n * p.ldb + k] : B[(size_t)k * p.ldb + n]);
-                if constexpr (BGELU) bv = to_f(from_f<T>(gelu_f(bv)));
-            }
+            if (n < p.N && k < p.K) bv = to_f(b_kmajor ? B[(size_t)n * p.ldb + k] : B[(size_t)k * p.ldb + n]);
             As[kk][r] = av;
             Bs[kk][r] = bv;
         }
@@ -1325,33 +1120,6 @@ template <int BM, int BN, int WGM, int WGN>
 constexpr size_t epilogue_lds_bytes() {
     return (size_t)(WGM * WGN) * 32 * (BN / WGN + 4) * 4;  // every wave: 32 rows x (WN + 4) floats
 }
-
-template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI, bool BGELU>
-static hipError_t launch_mfma(const GemmDesc& g, hipStream_t st, int splits) {
-    float* rs_part = splits > 1 ? g.splitk_ws + (size_t)splits * g.M * g.N : nullptr;
-    void* rsum = g.rowsum_out == nullptr || AK ? nullptr : (splits > 1 ? (void*)rs_part : g.rowsum_out);
-    GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K / splits, g.ea, g.splitk_ws, rsum};
-    auto kern = gemm_mfma_kernel<T, BM, BN, WGM, WGN, AK, BKM, EPI, BGELU>;
-    size_t lds = 2 * (TileGeom<AK, BM>::ELEMS + TileGeom<BKM, BN>::ELEMS) * sizeof(T);
-    lds = std::max(lds, epilogue_lds_bytes<BM, BN, WGM, WGN>());
-    lds = std::max(lds, (size_t)WGM * WGN * 64 * 8 * 4);  // row-sum reduction
-    static bool attr_done = false;
-    if (!attr_done) {
-        hipError_t e = set_lds(kern, lds);
-        if (e != hipSuccess) return e;
-        attr_done = true;
-    }
-    dim3 grid((g.M / BM) * (g.N / BN), 1, splits);
-    hipLaunchKernelGGL(kern, grid, dim3(WGM * WGN * 64), lds, st, p);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || splits == 1) return e;
-    const size_t n4 = (size_t)g.M * g.N / 4;
-    hipLaunchKernelGGL(splitk_reduce_kernel<T>, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st,
-                       (const float*)g.splitk_ws, splits, g.M, g.N, g.ea, rs_part,
-                       rsum ? reinterpret_cast<T*>(g.rowsum_out) : (T*)nullptr);
-    return hipGetLastError();
-}
-
 
 template <typename T, int BM, int BN, int WGM, int WGN, bool AK, bool BKM, int EPI>
 static hipError_t launch_dl(const GemmDesc& g, hipStream_t st, int splits) {
@@ -1466,7 +1234,7 @@ static hipError_t launch_dl4(const GemmDesc& g, hipStream_t st, int splits) {
 // keeps at least 8 k tiles.  0: the pair does not fit.
 static int group_splits(const GemmDesc& a, const GemmDesc& b) {
     auto ok = [](const GemmDesc& g) {
-        return g.dtype != 0 && !g.a_kmajor && !g.b_kmajor && !g.b_gelu && g.epi == EPI_STORE &&
+        return g.dtype != 0 && !g.a_kmajor && !g.b_kmajor && g.epi == EPI_STORE &&
                g.M % 256 == 0 && g.N % 256 == 0 && g.K % QKT == 0 && g.lda % 8 == 0 && g.ldb % 8 == 0;
     };
     if (!ok(a) || !ok(b) || a.dtype != b.dtype) return 0;
@@ -1606,52 +1374,37 @@ hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t s
 #endif
 constexpr int W256N = GEMM_W256N;
 constexpr int W128M = 4;
-template <typename T, int EPI, bool BGELU, bool AK, bool BKM>
+template <typename T, int EPI, bool AK, bool BKM>
 static hipError_t dispatch_tiles(const GemmDesc& g, hipStream_t st, TileCfg c) {
-    if constexpr (!BGELU) {
-        // operands stream straight into LDS; only the GELU-on-load variant
-        // (weight gradient under GELU checkpointing) uses the register-staged
-        // kernel, which can transform B on its way to LDS
-        if (c.BM == 256 && c.BN == 256) {
-            // the GELU epilogue's VALU work runs better with two waves per SIMD
-            if constexpr (W256N == 2 && EPI != EPI_BIAS_GELU)
-                return launch_dl4<T, 256, 256, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
-            else
-                return launch_dl<T, 256, 256, 2, 4, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
-        }
-        if (c.BM == 256 && c.BN == 192) {
-            if constexpr ((EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES) && AK && BKM)
-                return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
-            if constexpr ((EPI == EPI_STORE || EPI == EPI_HEADSPLIT || EPI == EPI_ADD_RES) && AK && !BKM)
-                return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
-            return hipErrorNotSupported;
-        }
-        if (c.BM == 256 && c.BN == 128) {
-            // the dropout epilogue's Philox work, like GELU's, favours two waves
-            // per SIMD unless the k loop is long enough to dominate
-            if constexpr (EPI != EPI_BIAS_GELU) {
-                if (EPI != EPI_BIAS_DROP_RES || g.K >= 2048)
-                    return launch_dl4<T, 256, 128, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
-            }
-            return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
-        }
+    // operands stream straight from global memory into LDS
+    if (c.BM == 256 && c.BN == 256) {
+        // the GELU epilogue's VALU work runs better with two waves per SIMD
+        if constexpr (W256N == 2 && EPI != EPI_BIAS_GELU)
+            return launch_dl4<T, 256, 256, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+        else
+            return launch_dl<T, 256, 256, 2, 4, AK, BKM, EPI>(g, st, splitk_for(g, 256, 256));
+    }
+    if (c.BM == 256 && c.BN == 192) {
+        if constexpr ((EPI == EPI_QKV || EPI == EPI_BIAS_DROP_RES) && AK && BKM)
+            return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
+        if constexpr ((EPI == EPI_STORE || EPI == EPI_HEADSPLIT || EPI == EPI_ADD_RES) && AK && !BKM)
+            return launch_dl4<T, 256, 192, AK, BKM, EPI>(g, st, 1);
+        return hipErrorNotSupported;
+    }
+    if (c.BM == 256 && c.BN == 128) {
+        // the dropout epilogue's Philox work, like GELU's, favours two waves
+        // per SIMD unless the k loop is long enough to dominate
         if constexpr (EPI != EPI_BIAS_GELU) {
             if (EPI != EPI_BIAS_DROP_RES || g.K >= 2048)
-                return launch_dl4<T, 128, 128, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
+                return launch_dl4<T, 256, 128, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
         }
-        return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
-    } else {
-        if (c.BM == 256 && c.BN == 256) {
-            int s = splitk_for(g, 256, 256);
-            return launch_mfma<T, 256, 256, 2, 4, AK, BKM, EPI, BGELU>(g, st, s);
-        }
-        if (c.BM == 256 && c.BN == 128) {
-            int s = splitk_for(g, 256, 128);
-            return launch_mfma<T, 256, 128, W128M, 2, AK, BKM, EPI, BGELU>(g, st, s);
-        }
-        int s = splitk_for(g, 128, 128);
-        return launch_mfma<T, 128, 128, 2, 2, AK, BKM, EPI, BGELU>(g, st, s);
+        return launch_dl<T, 256, 128, W128M, 2, AK, BKM, EPI>(g, st, splitk_for(g, 256, 128));
     }
+    if constexpr (EPI != EPI_BIAS_GELU) {
+        if (EPI != EPI_BIAS_DROP_RES || g.K >= 2048)
+            return launch_dl4<T, 128, 128, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
+    }
+    return launch_dl<T, 128, 128, 2, 2, AK, BKM, EPI>(g, st, splitk_for(g, 128, 128));
 }
 
 // Operand layouts the layer uses with each epilogue: projections (A, B
@@ -1668,24 +1421,23 @@ constexpr bool mfma_combo() {
     return false;
 }
 
-template <typename T, int EPI, bool BGELU>
+template <typename T, int EPI>
 static hipError_t dispatch_mfma(const GemmDesc& g, hipStream_t st, TileCfg c) {
     if (g.a_kmajor && g.b_kmajor) {
-        if constexpr (mfma_combo<EPI, true, true>() && !BGELU) return dispatch_tiles<T, EPI, BGELU, true, true>(g, st, c);
+        if constexpr (mfma_combo<EPI, true, true>()) return dispatch_tiles<T, EPI, true, true>(g, st, c);
     } else if (g.a_kmajor && !g.b_kmajor) {
-        if constexpr (mfma_combo<EPI, true, false>() && !BGELU) return dispatch_tiles<T, EPI, BGELU, true, false>(g, st, c);
+        if constexpr (mfma_combo<EPI, true, false>()) return dispatch_tiles<T, EPI, true, false>(g, st, c);
     } else if (!g.a_kmajor && !g.b_kmajor) {
-        if constexpr (mfma_combo<EPI, false, false>()) return dispatch_tiles<T, EPI, BGELU, false, false>(g, st, c);
+        if constexpr (mfma_combo<EPI, false, false>()) return dispatch_tiles<T, EPI, false, false>(g, st, c);
     }
     return hipErrorNotSupported;
 }
 
-template <typename T, int EPI, bool BGELU>
+template <typename T, int EPI>
 static hipError_t launch_simt(const GemmDesc& g, hipStream_t st) {
     GemmParams p{g.A, g.B, g.lda, g.ldb, g.M, g.N, g.K, g.K, g.ea, nullptr, nullptr};
     dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
-    hipLaunchKernelGGL((gemm_simt_kernel<T, EPI, BGELU>), grid, dim3(256), 0, st, p, (int)g.a_kmajor,
-                       (int)g.b_kmajor);
+    hipLaunchKernelGGL((gemm_simt_kernel<T, EPI>), grid, dim3(256), 0, st, p, (int)g.a_kmajor, (int)g.b_kmajor);
     return hipGetLastError();
 }
 
@@ -1696,21 +1448,12 @@ static hipError_t dispatch_epi(const GemmDesc& g, hipStream_t st, bool force_sim
         if (!force_simt) {
             TileCfg c = pick_tiles(g);
             if (c.BM) {
-                hipError_t e = hipErrorNotSupported;
-                if (g.b_gelu) {
-                    if constexpr (EPI == EPI_STORE) e = dispatch_mfma<T, EPI, true>(g, st, c);
-                } else {
-                    e = dispatch_mfma<T, EPI, false>(g, st, c);
-                }
+                const hipError_t e = dispatch_mfma<T, EPI>(g, st, c);
                 if (e != hipErrorNotSupported) return e;
             }
         }
     }
-    if (g.b_gelu) {
-        if constexpr (EPI == EPI_STORE) return launch_simt<T, EPI, true>(g, st);
-        return hipErrorInvalidValue;
-    }
-    return launch_simt<T, EPI, false>(g, st);
+    return launch_simt<T, EPI>(g, st);
 }
 
 template <typename T>

@@ -620,14 +620,12 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         const void *dY, *X;
         int out, in;
         void *dW, *db;
-        bool gelu;
     };
     auto wdesc = [&](const Wg& w) {
         GemmDesc g;
         g.dtype = dt; g.M = w.out; g.N = w.in; g.K = T;
         g.A = w.dY; g.lda = w.out; g.a_kmajor = false;
         g.B = w.X; g.ldb = w.in; g.b_kmajor = false;
-        g.b_gelu = w.gelu;
         g.epi = EPI_STORE;
         g.ea.out = w.dW; g.ea.ldo = w.in;
         g.splitk_ws = skws; g.splitk_ws_elems = skn;
@@ -641,9 +639,6 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         if (e != hipSuccess || g.rowsum_out) return e;
         return bias_grad(w.dY, w.out, w.db);
     };
-    // Two weight gradients: one grouped launch when both qualify (the tiles
-    // of both fill the chip with fewer k-splits), else one after the other.
-    // A profiled kernel id always runs alone, so its events cover only it.
     // Two weight gradients run as one grouped launch when both qualify (the
     // tiles of both fill the chip with fewer k-splits), else one after the
     // other.  A profiled kernel id always runs alone, so its events cover
@@ -657,8 +652,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     // partial rows): when the last pair (W_o with W_qkv, the end of the
     // backward) runs grouped, they wait for it and ride with its reduction
     // launch; otherwise each runs right after its LayerNorm backward.
-    const bool fold_ln = grouped(TEL_K_OUT_WGRAD, Wg{nullptr, nullptr, H, H, G->w_o, G->b_o, false},
-                                 TEL_K_QKV_WGRAD, Wg{nullptr, nullptr, 3 * H, H, G->w_qkv, G->b_qkv, false});
+    const bool fold_ln = grouped(TEL_K_OUT_WGRAD, Wg{nullptr, nullptr, H, H, G->w_o, G->b_o},
+                                 TEL_K_QKV_WGRAD, Wg{nullptr, nullptr, 3 * H, H, G->w_qkv, G->b_qkv});
     ColsumJob ln_fin[kMaxColsumJobs];
     int n_ln_fin = 0;
     auto ln_grads = [&](const float* pg, const float* pb, void* gg, void* gb) -> hipError_t {
@@ -719,8 +714,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, false},
-                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, G->b_1, false}, false);
+        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2},
+                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, G->b_1}, false);
         if (s != TEL_OK) return s;
         // x1 -> LN2: dx1 = dy + LN2'(da2); dz = drop1(dx1)
         LnBwdArgs lb{};
@@ -758,8 +753,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.part_g = part_ln1_g; lb.part_b = part_ln1_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(part_ln1_g, part_ln1_b, G->ln1_g, G->ln1_b));
-        s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o, false},
-                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, G->b_qkv, false},
+        s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o},
+                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), bs.of(p.ln1_out), 3 * H, H, G->w_qkv, G->b_qkv},
                        true);
         if (s != TEL_OK) return s;
     } else {
@@ -782,8 +777,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2, false},
-                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, G->b_1, false}, false);
+        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2},
+                       TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.x1e), F, H, G->w_1, G->b_1}, false);
         if (s != TEL_OK) return s;
         // x1 = LN1(z1): dz1 = LN1'(dgemm + dz2); dz = drop1(dz1)
         lb = LnBwdArgs{};
@@ -806,8 +801,8 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         g = dgrad(bs.of(p.dqkv), P->w_qkv, 3 * H, H, EPI_ADD_RES);
         g.ea.out = dxout; g.ea.ldo = H; g.ea.res = bs.of(p.dres);
         TIMED(TEL_K_QKV_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o, false},
-                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), xin, 3 * H, H, G->w_qkv, G->b_qkv, false}, true);
+        s = wgrad_pair(TEL_K_OUT_WGRAD, Wg{bs.of(p.dz), bs.of(p.ctx), H, H, G->w_o, G->b_o},
+                       TEL_K_QKV_WGRAD, Wg{bs.of(p.dqkv), xin, 3 * H, H, G->w_qkv, G->b_qkv}, true);
         if (s != TEL_OK) return s;
     }
     if (PR) HIP_TRY(scatter_rows(dt, dxout, dx, rinv, L->T, H, st));

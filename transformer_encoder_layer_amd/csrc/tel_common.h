@@ -203,8 +203,9 @@ __device__ __forceinline__ void colsum8_block(const float* part, int P, int N, T
 // Stegun, Handbook of Mathematical Functions, formula 7.1.26
 // (|error| <= 1.5e-7 in erf), evaluated on |u|/sqrt(2) so that the left
 // tail has no cancellation; phi shares the same exponential.  Every
-// operation is explicitly rounded so that each kernel that recomputes the
-// GELU (forward epilogue, weight-gradient operand load) gets the same bits.
+// operation is explicitly rounded so that every epilogue that evaluates it
+// (the FFN1 forward, the FFN2 input gradient under GELU checkpointing) gets
+// the same bits: GELU(u) = u * cdf, GELU'(u) = cdf + u * pdf.
 __device__ __forceinline__ void normal_cdf_pdf(float u, float& cdf, float& pdf) {
     const float x = __fmul_rn(fabsf(u), 0.70710678118654752f);
     const float t = __builtin_amdgcn_rcpf(__fmaf_rn(0.3275911f, x, 1.0f));
@@ -217,16 +218,6 @@ __device__ __forceinline__ void normal_cdf_pdf(float u, float& cdf, float& pdf) 
     const float half_erfc = __fmul_rn(__fmul_rn(0.5f, poly), e);
     cdf = u >= 0.0f ? __fadd_rn(1.0f, -half_erfc) : half_erfc;
     pdf = __fmul_rn(e, 0.39894228040143268f);
-}
-__device__ __forceinline__ float gelu_f(float u) {
-    float cdf, pdf;
-    normal_cdf_pdf(u, cdf, pdf);
-    return __fmul_rn(u, cdf);
-}
-__device__ __forceinline__ float gelu_grad_f(float u) {
-    float cdf, pdf;
-    normal_cdf_pdf(u, cdf, pdf);
-    return __fmaf_rn(u, pdf, cdf);
 }
 
 // ---------------------------------------------------------------- wave ops
