@@ -136,8 +136,12 @@ def kernel_sources_digest() -> str:
 # the BERT-Large layer, scaled by the copy calibration; keyed by the digest of
 # the kernel sources they were taken on (a changed kernel reports null).
 MEASURED_TRAFFIC = {
-    # FFN1 forward: FETCH_SIZE 49377 KiB + WRITE_SIZE 131072 KiB, scaled by the copy calibration
-    ("ffn1_fwd", "bert_large"): ("8278780ea09c9622", 235339119),
+    # W2 + W1 weight-gradient pair: the grouped GEMM launch (570.7 MB) and its split-K reduce (84.0 MB)
+    ("ffn_wgrad_pair", "bert_large"): ("3511d0a0ca7be768", 654705433),
+    # W_o + W_qkv pair: GEMM launch (407.3 MB) and its reduce with the LayerNorm gamma/beta sums (109.2 MB)
+    ("attn_wgrad_pair", "bert_large"): ("3511d0a0ca7be768", 516470713),
+    # FFN1 forward (GELU epilogue)
+    ("ffn1_fwd", "bert_large"): ("3511d0a0ca7be768", 235331670),
 }
 
 
