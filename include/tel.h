@@ -265,8 +265,9 @@ tel_status tel_debug_attn_keep_bits(tel_layer* layer, uint32_t* out_dev);
  * the next call that uses the same saved / scratch buffer).  Rows are the
  * layer's rows: tokens, or packed rows under token packing. */
 enum {
-    TEL_BUF_DROP1_IN = 0,   /* scratch, fp32 [T,H]: gradient reaching dropout site 1 in the backward
-                               (Pre-LN dx1, Post-LN dz1) */
+    TEL_BUF_DROP1_IN = 0,   /* scratch, fp32 [T,H] (the storage dtype for Pre-LN fp16 layers):
+                               gradient reaching dropout site 1 in the backward (Pre-LN dx1,
+                               Post-LN dz1) */
     TEL_BUF_DROP1_OUT = 1,  /* scratch, dtype [T,H]: the same after site 1's mask and 1/(1-p) */
     TEL_BUF_DROP2_IN = 2,   /* scratch, fp32 [T,H]: Post-LN dz2 reaching site 2 (Pre-LN: it is dy,
                                TEL_ERR_UNSUPPORTED) */

@@ -84,7 +84,7 @@ def test_masks_in_situ_bert_large():
         m1 = _oracle_mask(w, 1, step, lid, 0, n)
         df = run.buffer("drop2_out", torch.float16).double().numpy()[:n]
         k2 = _check_hidden_mask(data["dy_r"], df, m2, "site 2 backward")
-        dx1 = run.buffer("drop1_in", torch.float32).double().numpy()[:n]
+        dx1 = run.buffer("drop1_in", torch.float16).double().numpy()[:n]  # fp16 layer: dx1 in fp16
         dz = run.buffer("drop1_out", torch.float16).double().numpy()[:n]
         k1 = _check_hidden_mask(dx1, dz, m1, "site 1 backward")
         print("bits compared:", w.batch * w.heads * w.seq * w.seq, k2, k1)

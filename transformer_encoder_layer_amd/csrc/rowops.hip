@@ -350,14 +350,17 @@ static hipError_t ln_backward_t(const LnBwdArgs& a, hipStream_t st) {
                      (a.out_f32 ? LNB_OUT_F32 : 0) | (a.drop_out ? LNB_DROP : 0);
     switch (mode) {
 #define TEL_LNB(M) case (M): return ln_backward_m<T, (M)>(a, st);
-        // Pre-LN, LN2: dx1 = dy + LN2'(da2) in fp32, drop(dx1) for the attention branch
-        // (source: the fp32 or, for fp16 layers, fp16 residual x1; or the LN output)
+        // Pre-LN, LN2: dx1 = dy + LN2'(da2), drop(dx1) for the attention branch; x1
+        // and dx1 in fp32 (bf16 and fp32 layers) or fp16 (fp16 layers); or the LN output
         TEL_LNB(LNB_SRC_F32 | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
-        TEL_LNB(LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
-        // Pre-LN, LN1: dx = dx1 + LN1'(da1)
+        TEL_LNB(LNB_RES_LOWP | LNB_DROP)
+        TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP | LNB_DROP)
+        // Pre-LN, LN1: dx = dx1 + LN1'(da1), dx1 in fp32 or fp16 as above
         TEL_LNB(LNB_RES_F32)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_F32)
+        TEL_LNB(LNB_RES_LOWP)
+        TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP)
         // Post-LN, LN2: dz2 = LN2'(dy) in fp32, drop(dz2) for the FFN branch
         // (source z2 in fp32 or fp16, or the output y)
         TEL_LNB(LNB_SRC_F32 | LNB_OUT_F32 | LNB_DROP)

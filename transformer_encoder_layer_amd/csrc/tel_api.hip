@@ -184,7 +184,9 @@ static void make_plan(tel_layer* L) {
     place(p.du, T * F * e, false, sv, sc);
     if (gck) place(p.gck_g, T * F * e, false, sv, sc);
     place(p.dgemm, T * H * e, false, sv, sc);
-    place(p.dres, T * H * f4, false, sv, sc);
+    // gradient of the residual stream between the two LayerNorm backwards:
+    // Pre-LN keeps it in the residual's type (fp16 for fp16 layers)
+    place(p.dres, T * H * (L->cfg.pre_ln ? rs : f4), false, sv, sc);
     place(p.dres2, T * H * f4, false, sv, sc);
     place(p.dz, T * H * e, false, sv, sc);
     place(p.dout, T * H * e, false, sv, sc);
@@ -725,7 +727,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.mu = (const float*)bs.of(p.mu2); lb.rstd = (const float*)bs.of(p.rs2);
         lb.gamma = P->ln2_g; lb.beta = P->ln2_b;
         lb.res = dyin; lb.res_f32 = 0;
-        lb.out = bs.of(p.dres); lb.out_f32 = 1;
+        lb.out = bs.of(p.dres); lb.out_f32 = r32;
         lb.drop_out = bs.of(p.dz); lb.drop = d1;
         lb.part_g = part_ln2_g; lb.part_b = part_ln2_b; lb.row_map = rmap;
         TIMED(TEL_K_LN2_BWD, ln_backward(lb, st));
@@ -748,7 +750,7 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.src = inv ? bs.of(p.ln1_out) : xin; lb.src_f32 = 0; lb.from_output = inv;
         lb.mu = (const float*)bs.of(p.mu1); lb.rstd = (const float*)bs.of(p.rs1);
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
-        lb.res = bs.of(p.dres); lb.res_f32 = 1;
+        lb.res = bs.of(p.dres); lb.res_f32 = r32;
         lb.out = dxout; lb.out_f32 = 0;
         lb.part_g = part_ln1_g; lb.part_b = part_ln1_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
