@@ -237,9 +237,12 @@ constexpr int KT = 64;  // k granularity the MFMA kernels need of K
 #ifndef GEMM_GM
 #define GEMM_GM 8
 #endif
+__device__ __forceinline__ int xcd_range(int u, int total) {
+    return (GEMM_XCD_REMAP && (total & 7) == 0) ? (u & 7) * (total >> 3) + (u >> 3) : u;
+}
+template <bool REMAP = true>
 __device__ __forceinline__ void tile_of(int pid, int tm, int tn, int& im, int& in_) {
-    const int total = tm * tn;
-    if (GEMM_XCD_REMAP && (total & 7) == 0) pid = (pid & 7) * (total >> 3) + (pid >> 3);
+    if (REMAP) pid = xcd_range(pid, tm * tn);
     constexpr int GM = GEMM_GM;
     const int group = pid / (GM * tn);
     const int first = group * GM;
@@ -761,16 +764,20 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
     const uint32_t lds0 = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)smem_raw;
     for (int u = blockIdx.x; u < G.units; u += gridDim.x) {
         if (u != (int)blockIdx.x) __syncthreads();  // the last epilogue is done with LDS
-        const int g = u >= G.units0 ? 1 : 0;
+        // each XCD takes one contiguous range of the units (whole k-splits
+        // of one problem where they divide evenly), so the A and B panels
+        // its L2 fetches serve every tile of that range
+        const int v = xcd_range(u, G.units);
+        const int g = v >= G.units0 ? 1 : 0;
         const GemmParams& p = g ? G.p[1] : G.p[0];
         const int nsplit = g ? G.splits[1] : G.splits[0];
         const int tm = p.M / BM, tn = p.N / BN;
-        const int lu = u - (g ? G.units0 : 0);
+        const int lu = v - (g ? G.units0 : 0);
         const int split = lu / (tm * tn), pid = lu - split * (tm * tn);
         const Dl4Plan<T, AK, BM> pa(p.lda, wave_s, lane);
         const Dl4Plan<T, BKM, BN> pb(p.ldb, wave_s, lane);
         int im, in_;
-        tile_of(pid, tm, tn, im, in_);
+        tile_of<false>(pid, tm, tn, im, in_);
         const int m0 = im * BM, n0 = in_ * BN;
         const int kbeg = split * p.k_per_split;
         const int kend = min(p.K, kbeg + p.k_per_split);
