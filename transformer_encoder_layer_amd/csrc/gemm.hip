@@ -667,8 +667,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------- 256x256 tiles, one wave per SIMD
-// Four waves in a 2 x 2 grid of 128x128 wave tiles; k tiles 64 deep in two
-// LDS stages of 64 KB.  Compared with two waves per SIMD on 128x64 wave
+// Four waves in a 2 x 2 grid of 128x128 wave tiles; k tiles 64 deep in as
+// many LDS stages as fit (two of 64 KB at 256x256, three of 48 KB at
+// 256x128, so that loads run two k tiles ahead where the k tile is short).  Compared with two waves per SIMD on 128x64 wave
 // tiles: 8 fragment reads feed 16 MFMAs (a third fewer LDS bytes per MFMA,
 // and LDS traffic is what bounds the loop), k-major rows are 128 bytes so
 // every direct load fetches whole cache lines, and there is one barrier per
@@ -677,7 +678,8 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
 // memory instructions (a fragment read for the next k-step, a direct load of
 // the tile after next), fenced so that the pairing survives scheduling.
 constexpr int QKT = 64;  // k per stage
-constexpr int QNS = 2;   // stages
+// LDS stages of a BM x BN tile: three where they fit in the 160 KB, else two
+constexpr int dl4_stages(int BM, int BN, int esz) { return 3 * (BM + BN) * QKT * esz <= 160 * 1024 ? 3 : 2; }
 
 // k-major rows of 64 k (128 bytes): 16-byte chunk c of row r is stored at
 // chunk c ^ ((r >> 1) & 7), so the 16 rows read by each quarter of a wave's
@@ -749,6 +751,8 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
     constexpr int LA = BM * QKT * (int)sizeof(T) / 1024 / 4;  // direct loads per wave per stage: A
     constexpr int LPW = LA + BN * QKT * (int)sizeof(T) / 1024 / 4;  // A and B
     constexpr int AEL = BM * QKT, STAGE = (BM + BN) * QKT;
+    constexpr int NS = dl4_stages(BM, BN, (int)sizeof(T));
+    static_assert(NS == 2 || NS == 3, "stage count");
     typedef typename MfmaOp<T>::v8 v8;
 
     extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -828,58 +832,64 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
         __builtin_amdgcn_sched_barrier(0);                                                               \
     }
 
+        // prologue: tiles 0 .. NS-1 into stages 0 .. NS-1, then wait for tile 0
 #pragma unroll
-        for (int q = 0; q < LPW; ++q) load_q(0, q);
-        oa += sta;
-        ob += stb;
-        if (nk > 1) {
+        for (int t = 0; t < NS; ++t) {
+            if (t < nk) {
 #pragma unroll
-            for (int q = 0; q < LPW; ++q) load_q(1, q);
-            oa += sta;
-            ob += stb;
-            wait_vmcnt<LPW>();  // tile 0 landed, tile 1 may be in flight
-        } else {
-            wait_vmcnt<0>();
+                for (int q = 0; q < LPW; ++q) load_q(t, q);
+                oa += sta;
+                ob += stb;
+            }
         }
+        if (NS == 3 && nk >= 3) wait_vmcnt<(NS - 1) * LPW>();  // tiles 1, 2 may be in flight
+        else if (nk >= 2) wait_vmcnt<LPW>();
+        else wait_vmcnt<0>();
         __syncthreads();
 #pragma unroll
         for (int q = 0; q < NF; ++q) fr[0][q] = frag(smem, 0, q);
-        // Per k tile kt (stage kt & 1; k-step 0 fragments already in set 0):
+        // Per k tile kt (stage kt % NS; k-step 0 fragments already in set 0):
         // k-steps 0..2 each read the next k-step of the stage; then tile kt+1
         // is made visible (its loads landed on every wave, and every wave has
-        // read all of tile kt, whose stage tile kt+2 now overwrites), and
+        // read all of tile kt, whose stage tile kt+NS now overwrites), and
         // k-step 3 reads tile kt+1's first k-step.  The steady state (a tile
-        // still to load) is one branch-free block; the last two tiles are
+        // still to load) is one branch-free block; the last NS tiles are
         // peeled.
-        int kt = 0;
-        for (; kt < nk - 2; ++kt) {
-            const T* cur = smem + (kt & 1) * STAGE;
-            const T* nxt = smem + ((kt + 1) & 1) * STAGE;
+        int kt = 0, sc = 0;  // sc = kt % NS
+        for (; kt < nk - NS; ++kt) {
+            const int sn = sc + 1 == NS ? 0 : sc + 1;
+            const T* cur = smem + sc * STAGE;
+            const T* nxt = smem + sn * STAGE;
             __builtin_amdgcn_sched_barrier(0);
             TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0)
             TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0)
             TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0)
-            wait_vmcnt<0>();
+            wait_vmcnt<(NS - 2) * LPW>();  // tile kt+1 landed; kt+2 .. kt+NS-1 may be in flight
             __syncthreads();
-            TEL_DL4_BLOCK(1, 1, nxt, 0, 1, (kt & 1))
+            TEL_DL4_BLOCK(1, 1, nxt, 0, 1, sc)
             oa += sta;
             ob += stb;
+            sc = sn;
         }
         for (; kt < nk; ++kt) {
-            const T* cur = smem + (kt & 1) * STAGE;
-            const T* nxt = smem + ((kt + 1) & 1) * STAGE;
+            const int sn = sc + 1 == NS ? 0 : sc + 1;
+            const T* cur = smem + sc * STAGE;
+            const T* nxt = smem + sn * STAGE;
             __builtin_amdgcn_sched_barrier(0);
             TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0)
             TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0)
             TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0)
             if (kt + 1 < nk) {
-                wait_vmcnt<0>();
+                // tiles kt+1 .. nk-1 are the ones in flight
+                if (NS == 3 && kt + 2 < nk) wait_vmcnt<LPW>();
+                else wait_vmcnt<0>();
                 __syncthreads();
 #pragma unroll
                 for (int q = 0; q < NF; ++q) fr[0][q] = frag(nxt, 0, q);
             }
             __builtin_amdgcn_sched_barrier(0);
             TEL_DL4_BLOCK(1, 0, cur, 0, 0, 0)
+            sc = sn;
         }
 #undef TEL_DL4_BLOCK
         __syncthreads();
@@ -1194,7 +1204,8 @@ static int dl4_slots(size_t lds) {
 
 template <int BM, int BN>
 constexpr size_t dl4_lds_bytes(size_t esz) {
-    return std::max(std::max((size_t)QNS * (BM + BN) * QKT * esz, epilogue_lds_bytes<BM, BN, 2, 2>()),
+    return std::max(std::max((size_t)dl4_stages(BM, BN, (int)esz) * (BM + BN) * QKT * esz,
+                             epilogue_lds_bytes<BM, BN, 2, 2>()),
                     (size_t)256 * 8 * 4);
 }
 
