@@ -679,7 +679,10 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
 // the tile after next), fenced so that the pairing survives scheduling.
 constexpr int QKT = 64;  // k per stage
 // LDS stages of a BM x BN tile: three where they fit in the 160 KB, else two
-constexpr int dl4_stages(int BM, int BN, int esz) { return 3 * (BM + BN) * QKT * esz <= 160 * 1024 ? 3 : 2; }
+// (128x128 keeps two, so that two workgroups share a CU)
+constexpr int dl4_stages(int BM, int BN, int esz) {
+    return BM + BN >= 384 && 3 * (BM + BN) * QKT * esz <= 160 * 1024 ? 3 : 2;
+}
 
 // k-major rows of 64 k (128 bytes): 16-byte chunk c of row r is stored at
 // chunk c ^ ((r >> 1) & 7), so the 16 rows read by each quarter of a wave's
@@ -819,79 +822,147 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
         };
         v8 fr[2][NF];  // fragment sets: [0..MI-1] A, [MI..] B
         // NQ MFMAs on fragment set S, paired with reads of k-step RKS of stage
-        // RST into set S^1 (if RD) and the LPW direct loads into stage LST (if
-        // LD), spread over the MFMAs; RD and LD are literal 0 or 1
-#define TEL_DL4_BLOCK(S, RD, RST, RKS, LD, LST)                                                          \
+        // RST into set S^1 (if RD) and the direct loads L0 .. L1-1 of the
+        // current origins into stage LST (if the wave-uniform LOK holds),
+        // spread over the MFMAs; RD, L0 and L1 are literals
+#define TEL_DL4_BLOCK_IF(S, RD, RST, RKS, LST, L0, L1, LOK)                                              \
     _Pragma("unroll") for (int q = 0; q < NQ; ++q) {                                                     \
         acc[q / NI][q % NI] = MfmaOp<T>::mma(fr[S][MI + q % NI], fr[S][q / NI], acc[q / NI][q % NI]);    \
         if (!AK && q < MI) rsa[q] = frag_sum8(fr[S][q], rsa[q]);                                         \
         if (RD && q < NF) fr[(S) ^ 1][q] = frag((RST), (RKS), q);                                         \
-        if (LD) {                                                                                        \
-            _Pragma("unroll") for (int l = q * LPW / NQ; l < (q + 1) * LPW / NQ; ++l) load_q((LST), l);  \
-        }                                                                                                \
+        _Pragma("unroll") for (int l = (L0) + q * ((L1) - (L0)) / NQ; l < (L0) + (q + 1) * ((L1) - (L0)) / NQ; \
+                               ++l) if (LOK) load_q((LST), l);                                           \
         __builtin_amdgcn_sched_barrier(0);                                                               \
     }
+#define TEL_DL4_BLOCK(S, RD, RST, RKS, LST, L0, L1) TEL_DL4_BLOCK_IF(S, RD, RST, RKS, LST, L0, L1, true)
 
-        // prologue: tiles 0 .. NS-1 into stages 0 .. NS-1, then wait for tile 0
+        int kt = 0, sc = 0;  // sc = kt % NS
+        if constexpr (NS == 3) {
+            // Loads of tile kt+2 are spread over the whole of k tile kt-1's
+            // last k-step (the first L4, into the stage tile kt-1 just freed)
+            // and k tile kt's first three (the rest), so that no k-step issues
+            // more than a quarter of a tile's loads: bunched together they
+            // back up the load path and stall the MFMA issue behind them.
+            constexpr int LQ = LPW / 4, L4 = LPW - 3 * LQ;
+            // prologue: tiles 0 and 1 whole, the first L4 loads of tile 2
 #pragma unroll
-        for (int t = 0; t < NS; ++t) {
-            if (t < nk) {
+            for (int t = 0; t < 2; ++t) {
+                if (t < nk) {
 #pragma unroll
-                for (int q = 0; q < LPW; ++q) load_q(t, q);
+                    for (int q = 0; q < LPW; ++q) load_q(t, q);
+                    oa += sta;
+                    ob += stb;
+                }
+            }
+            if (nk > 2) {
+#pragma unroll
+                for (int q = 0; q < L4; ++q) load_q(2, q);
+                wait_vmcnt<LPW + L4>();  // tile 0 landed
+            } else if (nk == 2) {
+                wait_vmcnt<LPW>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < NF; ++q) fr[0][q] = frag(smem, 0, q);
+            // steady state: tile kt+2 is completed, tile kt+3 begun
+            for (; kt < nk - 3; ++kt) {
+                const int sn = sc == 2 ? 0 : sc + 1, sp = sn == 2 ? 0 : sn + 1;  // stages of kt+1, kt+2
+                const T* cur = smem + sc * STAGE;
+                const T* nxt = smem + sn * STAGE;
+                __builtin_amdgcn_sched_barrier(0);
+                TEL_DL4_BLOCK(0, 1, cur, 1, sp, L4, L4 + LQ)
+                TEL_DL4_BLOCK(1, 1, cur, 2, sp, L4 + LQ, L4 + 2 * LQ)
+                TEL_DL4_BLOCK(0, 1, cur, 3, sp, L4 + 2 * LQ, LPW)
                 oa += sta;
                 ob += stb;
-            }
-        }
-        if (NS == 3 && nk >= 3) wait_vmcnt<(NS - 1) * LPW>();  // tiles 1, 2 may be in flight
-        else if (nk >= 2) wait_vmcnt<LPW>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < NF; ++q) fr[0][q] = frag(smem, 0, q);
-        // Per k tile kt (stage kt % NS; k-step 0 fragments already in set 0):
-        // k-steps 0..2 each read the next k-step of the stage; then tile kt+1
-        // is made visible (its loads landed on every wave, and every wave has
-        // read all of tile kt, whose stage tile kt+NS now overwrites), and
-        // k-step 3 reads tile kt+1's first k-step.  The steady state (a tile
-        // still to load) is one branch-free block; the last NS tiles are
-        // peeled.
-        int kt = 0, sc = 0;  // sc = kt % NS
-        for (; kt < nk - NS; ++kt) {
-            const int sn = sc + 1 == NS ? 0 : sc + 1;
-            const T* cur = smem + sc * STAGE;
-            const T* nxt = smem + sn * STAGE;
-            __builtin_amdgcn_sched_barrier(0);
-            TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0)
-            TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0)
-            TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0)
-            wait_vmcnt<(NS - 2) * LPW>();  // tile kt+1 landed; kt+2 .. kt+NS-1 may be in flight
-            __syncthreads();
-            TEL_DL4_BLOCK(1, 1, nxt, 0, 1, sc)
-            oa += sta;
-            ob += stb;
-            sc = sn;
-        }
-        for (; kt < nk; ++kt) {
-            const int sn = sc + 1 == NS ? 0 : sc + 1;
-            const T* cur = smem + sc * STAGE;
-            const T* nxt = smem + sn * STAGE;
-            __builtin_amdgcn_sched_barrier(0);
-            TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0)
-            TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0)
-            TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0)
-            if (kt + 1 < nk) {
-                // tiles kt+1 .. nk-1 are the ones in flight
-                if (NS == 3 && kt + 2 < nk) wait_vmcnt<LPW>();
-                else wait_vmcnt<0>();
+                wait_vmcnt<LPW>();  // tile kt+1 landed; tile kt+2 may be in flight
                 __syncthreads();
-#pragma unroll
-                for (int q = 0; q < NF; ++q) fr[0][q] = frag(nxt, 0, q);
+                TEL_DL4_BLOCK(1, 1, nxt, 0, sc, 0, L4)
+                sc = sn;
             }
-            __builtin_amdgcn_sched_barrier(0);
-            TEL_DL4_BLOCK(1, 0, cur, 0, 0, 0)
-            sc = sn;
+            for (; kt < nk; ++kt) {
+                const int sn = sc == 2 ? 0 : sc + 1, sp = sn == 2 ? 0 : sn + 1;
+                const T* cur = smem + sc * STAGE;
+                const T* nxt = smem + sn * STAGE;
+                // tile kt+2, when it exists, is the last one: complete it
+                const bool more = kt + 2 < nk;
+                __builtin_amdgcn_sched_barrier(0);
+                TEL_DL4_BLOCK_IF(0, 1, cur, 1, sp, L4, L4 + LQ, more)
+                TEL_DL4_BLOCK_IF(1, 1, cur, 2, sp, L4 + LQ, L4 + 2 * LQ, more)
+                TEL_DL4_BLOCK_IF(0, 1, cur, 3, sp, L4 + 2 * LQ, LPW, more)
+                if (more) wait_vmcnt<LPW>();
+                else wait_vmcnt<0>();
+                if (kt + 1 < nk) {
+                    __syncthreads();
+#pragma unroll
+                    for (int q = 0; q < NF; ++q) fr[0][q] = frag(nxt, 0, q);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                TEL_DL4_BLOCK(1, 0, cur, 0, 0, 0, 0)
+                sc = sn;
+            }
+        } else {
+            // prologue: tiles 0 and 1 into stages 0 and 1, then wait for tile 0
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                if (t < nk) {
+#pragma unroll
+                    for (int q = 0; q < LPW; ++q) load_q(t, q);
+                    oa += sta;
+                    ob += stb;
+                }
+            }
+            if (nk >= 2) wait_vmcnt<LPW>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+#pragma unroll
+            for (int q = 0; q < NF; ++q) fr[0][q] = frag(smem, 0, q);
+            // Per k tile kt (stage kt & 1; k-step 0 fragments already in set
+            // 0): k-steps 0..2 each read the next k-step of the stage; then
+            // tile kt+1 is made visible (its loads landed on every wave, and
+            // every wave has read all of tile kt, whose stage tile kt+2 now
+            // overwrites), and k-step 3 reads tile kt+1's first k-step while
+            // the loads of tile kt+2 go out.  The steady state (a tile still
+            // to load) is one branch-free block; the last two tiles are
+            // peeled.
+            for (; kt < nk - 2; ++kt) {
+                const int sn = sc ^ 1;
+                const T* cur = smem + sc * STAGE;
+                const T* nxt = smem + sn * STAGE;
+                __builtin_amdgcn_sched_barrier(0);
+                TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0, 0)
+                TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0, 0)
+                TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0, 0)
+                wait_vmcnt<0>();
+                __syncthreads();
+                TEL_DL4_BLOCK(1, 1, nxt, 0, sc, 0, LPW)
+                oa += sta;
+                ob += stb;
+                sc = sn;
+            }
+            for (; kt < nk; ++kt) {
+                const int sn = sc ^ 1;
+                const T* cur = smem + sc * STAGE;
+                const T* nxt = smem + sn * STAGE;
+                __builtin_amdgcn_sched_barrier(0);
+                TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0, 0)
+                TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0, 0)
+                TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0, 0)
+                if (kt + 1 < nk) {
+                    wait_vmcnt<0>();
+                    __syncthreads();
+#pragma unroll
+                    for (int q = 0; q < NF; ++q) fr[0][q] = frag(nxt, 0, q);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+                TEL_DL4_BLOCK(1, 0, cur, 0, 0, 0, 0)
+                sc = sn;
+            }
         }
 #undef TEL_DL4_BLOCK
+#undef TEL_DL4_BLOCK_IF
         __syncthreads();
 
         const bool atomic = !AK && EPI == EPI_STORE && nsplit > 1 && G.atomic;
