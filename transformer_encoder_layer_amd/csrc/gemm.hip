@@ -904,53 +904,58 @@ __global__ __launch_bounds__(256) void gemm_dl4_kernel(GemmGroup G) {
                 sc = sn;
             }
         } else {
-            // prologue: tiles 0 and 1 into stages 0 and 1, then wait for tile 0
+            // Two stages: the loads of tile kt+1 go out half in k tile
+            // kt-1's last k-step (into the stage tile kt-1 just freed) and
+            // half in k tile kt's first, two k-steps before the wait for them.
+            constexpr int H1 = LPW / 2;
+            // prologue: tile 0 whole, the first H1 loads of tile 1
 #pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                if (t < nk) {
+            for (int q = 0; q < LPW; ++q) load_q(0, q);
+            oa += sta;
+            ob += stb;
+            if (nk > 1) {
 #pragma unroll
-                    for (int q = 0; q < LPW; ++q) load_q(t, q);
-                    oa += sta;
-                    ob += stb;
-                }
+                for (int q = 0; q < H1; ++q) load_q(1, q);
+                wait_vmcnt<H1>();  // tile 0 landed
+            } else {
+                wait_vmcnt<0>();
             }
-            if (nk >= 2) wait_vmcnt<LPW>();
-            else wait_vmcnt<0>();
             __syncthreads();
 #pragma unroll
             for (int q = 0; q < NF; ++q) fr[0][q] = frag(smem, 0, q);
             // Per k tile kt (stage kt & 1; k-step 0 fragments already in set
-            // 0): k-steps 0..2 each read the next k-step of the stage; then
-            // tile kt+1 is made visible (its loads landed on every wave, and
-            // every wave has read all of tile kt, whose stage tile kt+2 now
-            // overwrites), and k-step 3 reads tile kt+1's first k-step while
-            // the loads of tile kt+2 go out.  The steady state (a tile still
-            // to load) is one branch-free block; the last two tiles are
-            // peeled.
+            // 0): k-steps 0..2 each read the next k-step of the stage (the
+            // first also completes tile kt+1's loads); then tile kt+1 is made
+            // visible (its loads landed on every wave, and every wave has read
+            // all of tile kt, whose stage tile kt+2 now takes), and k-step 3
+            // reads tile kt+1's first k-step while tile kt+2's first loads go
+            // out.  The steady state is one branch-free block; the last two
+            // tiles are peeled.
             for (; kt < nk - 2; ++kt) {
                 const int sn = sc ^ 1;
                 const T* cur = smem + sc * STAGE;
                 const T* nxt = smem + sn * STAGE;
                 __builtin_amdgcn_sched_barrier(0);
-                TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0, 0)
+                TEL_DL4_BLOCK(0, 1, cur, 1, sn, H1, LPW)
+                oa += sta;
+                ob += stb;
                 TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0, 0)
                 TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0, 0)
                 wait_vmcnt<0>();
                 __syncthreads();
-                TEL_DL4_BLOCK(1, 1, nxt, 0, sc, 0, LPW)
-                oa += sta;
-                ob += stb;
+                TEL_DL4_BLOCK(1, 1, nxt, 0, sc, 0, H1)
                 sc = sn;
             }
             for (; kt < nk; ++kt) {
                 const int sn = sc ^ 1;
                 const T* cur = smem + sc * STAGE;
                 const T* nxt = smem + sn * STAGE;
+                const bool more = kt + 1 < nk;  // tile kt+1 (begun) is the last one: complete it
                 __builtin_amdgcn_sched_barrier(0);
-                TEL_DL4_BLOCK(0, 1, cur, 1, 0, 0, 0)
+                TEL_DL4_BLOCK_IF(0, 1, cur, 1, sn, H1, LPW, more)
                 TEL_DL4_BLOCK(1, 1, cur, 2, 0, 0, 0)
                 TEL_DL4_BLOCK(0, 1, cur, 3, 0, 0, 0)
-                if (kt + 1 < nk) {
+                if (more) {
                     wait_vmcnt<0>();
                     __syncthreads();
 #pragma unroll
