@@ -10,6 +10,7 @@
 #include <stdint.h>
 #include <hip/hip_runtime.h>
 #include "tel_common.h"
+#include "fastdiv.h"
 
 namespace tel {
 
@@ -36,6 +37,7 @@ struct EpiArgs {
     int gelu_grad_out = 0;  // EPI_BIAS_GELU: out receives GELU'(u) instead of u
     const void* aux = nullptr;
     int B = 0, S = 0, H = 0, NH = 0, d = 0;  // head-split geometry
+    FastDiv fS, fH, fd;                       // dividers by S, H and d (set by the launch)
     Drop drop{};                              // thr == 0: no dropout
     // Packed rows: row m of the GEMM holds token row_map[m] (b*S + s) of the
     // padded batch, or no token (-1, a filler row).  The head-split scatters

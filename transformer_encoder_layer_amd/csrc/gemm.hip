@@ -132,8 +132,9 @@ struct Epi {
             for (int i = 0; i < 4; ++i) v[i] += b[i];
             const int t = PK ? e.row_map[m] : m;
             if (PK && t < 0) return;
-            const int which = n / e.H, rem = n - which * e.H, h = rem / e.d, c = rem - h * e.d;
-            const int bb = t / e.S, s = t - bb * e.S;
+            const int which = (int)e.fH.div(n), rem = n - which * e.H;
+            const int h = (int)e.fd.div(rem), c = rem - h * e.d;
+            const int bb = (int)e.fS.div(t), s = t - bb * e.S;
             const size_t o = ((((size_t)which * e.B + bb) * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
         } else if constexpr (EPI == EPI_BIAS_DROP_RES) {
@@ -176,7 +177,7 @@ struct Epi {
         } else if constexpr (EPI == EPI_HEADSPLIT) {
             const int t = PK ? e.row_map[m] : m;
             if (PK && t < 0) return;
-            const int bb = t / e.S, s = t - bb * e.S, h = n / e.d, c = n - h * e.d;
+            const int bb = (int)e.fS.div(t), s = t - bb * e.S, h = (int)e.fd.div(n), c = n - h * e.d;
             const size_t o = (((size_t)bb * e.NH + h) * e.S + s) * e.d + c;
             Vec4<T>::store((T*)e.out + o, v);
         } else if constexpr (EPI == EPI_ADD_RES) {
@@ -1565,8 +1566,16 @@ static hipError_t dispatch_type(const GemmDesc& g, hipStream_t st, bool force_si
     return hipErrorInvalidValue;
 }
 
-hipError_t gemm_launch(const GemmDesc& g, hipStream_t st, bool force_simt) {
-    if (g.M <= 0 || g.N <= 0 || g.K <= 0) return hipSuccess;
+hipError_t gemm_launch(const GemmDesc& g_in, hipStream_t st, bool force_simt) {
+    if (g_in.M <= 0 || g_in.N <= 0 || g_in.K <= 0) return hipSuccess;
+    GemmDesc g = g_in;
+    if (g.epi == EPI_QKV || g.epi == EPI_HEADSPLIT) {
+        // the scatters divide row and column indices (< 2^31) by S, H and d
+        if (g.ea.S < 1 || g.ea.H < 1 || g.ea.d < 1) return hipErrorInvalidValue;
+        g.ea.fS = FastDiv((uint32_t)g.ea.S);
+        g.ea.fH = FastDiv((uint32_t)g.ea.H);
+        g.ea.fd = FastDiv((uint32_t)g.ea.d);
+    }
     switch (g.dtype) {
         case 0: return dispatch_type<float>(g, st, true);
         case 1: return dispatch_type<f16>(g, st, force_simt);
