@@ -136,10 +136,10 @@ def kernel_sources_digest() -> str:
 # the BERT-Large layer, scaled by the copy calibration; keyed by the digest of
 # the kernel sources they were taken on (a changed kernel reports null).
 MEASURED_TRAFFIC = {
-    # W2 + W1 weight-gradient pair: the grouped GEMM launch (268.7 MB) and its split-K reduce (84.0 MB)
-    ("ffn_wgrad_pair", "bert_large"): ("c78c450e0521d228", 352721145),
-    # W_o + W_qkv pair: GEMM launch (197.4 MB) and its reduce with the LayerNorm gamma/beta sums (109.2 MB)
-    ("attn_wgrad_pair", "bert_large"): ("c78c450e0521d228", 306649140),
+    # W2 + W1 weight-gradient pair: the grouped GEMM launch (its split-K reduce launch, 84.0 MB, apart)
+    ("ffn_wgrad_pair", "bert_large"): ("c78c450e0521d228", 268722875),
+    # W_o + W_qkv pair: the grouped GEMM launch (its reduce with the LayerNorm gamma/beta sums, 109.2 MB, apart)
+    ("attn_wgrad_pair", "bert_large"): ("c78c450e0521d228", 197445847),
     # FFN1 forward (GELU epilogue)
     ("ffn1_fwd", "bert_large"): ("c78c450e0521d228", 235324886),
 }
@@ -153,7 +153,7 @@ def main():
     ap.add_argument("--workload", default="bert_large")
     ap.add_argument("--layers", type=int, default=0, help="override the stack depth")
     ap.add_argument("--kernel", default="ffn_wgrad_pair", help="call site whose roofline is reported")
-    ap.add_argument("--also", default="ffn1_fwd,attn_wgrad_pair",
+    ap.add_argument("--also", default="ffn_wgrad_reduce,ffn1_fwd,attn_wgrad_pair",
                     help="further call sites timed (comma-separated), each on its own share of the layers")
     ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle sample (BERT-Large: the whole batch, about 10 s on 16 host threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -295,6 +295,15 @@ def main():
         if not ms:
             return {"kernel": site, "launches": 0}
         avg_ms = float(np.mean(ms))
+        if site.endswith("_wgrad_reduce"):  # the launch after a pair: its time, and the pair's rate with it
+            pair = site.replace("_reduce", "_pair")
+            out_r = {"kernel": site, "avg_launch_us": round(avg_ms * 1e3, 2), "launches": len(ms)}
+            if site_ms.get(pair):
+                both = float(np.mean(site_ms[pair])) + avg_ms
+                ach = gemm_flops[pair] / (both / 1e3) / 1e12
+                out_r["pair_with_reduce"] = {"achieved": round(ach, 1), "unit": "TFLOP/s", "frac": round(ach / peak, 4),
+                                             "avg_us": round(both * 1e3, 2)}
+            return out_r
         if site in gemm_flops:
             ach = gemm_flops[site] / (avg_ms / 1e3) / 1e12
             meas = MEASURED_TRAFFIC.get((site, w.name))
@@ -312,6 +321,9 @@ def main():
 
     roof = roofline(sites[0])
     others = [roofline(k) for k in sites[1:]]
+    for o in others:  # the dominant pair's rate including the launch after it
+        if o.get("kernel") == sites[0].replace("_pair", "_reduce") and "pair_with_reduce" in o:
+            roof["with_reduce"] = dict(o["pair_with_reduce"], reduce_avg_us=o["avg_launch_us"])
     shape = (f"{'BERT-Large' if w.name == 'bert_large' else w.name} layer B{w.batch} S{w.seq} H{w.hidden} "
              f"{ {'f16': 'fp16', 'bf16': 'bf16', 'f32': 'fp32'}[w.dtype]}{', token packing' if pack else ''}")
 

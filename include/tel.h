@@ -231,10 +231,12 @@ enum {
     TEL_K_FFN2_DGRAD = 10, TEL_K_FFN2_WGRAD = 11, TEL_K_FFN1_DGRAD = 12, TEL_K_FFN1_WGRAD = 13,
     TEL_K_LN2_BWD = 14, TEL_K_OUT_DGRAD = 15, TEL_K_OUT_WGRAD = 16, TEL_K_ATTN_BWD = 17,
     TEL_K_QKV_DGRAD = 18, TEL_K_QKV_WGRAD = 19, TEL_K_LN1_BWD = 20,
-    /* the grouped weight-gradient launches (W_2 with W_1, W_o with W_qkv),
-       each with its split-K reduction and, for the last, the LayerNorm
-       gamma/beta sums; only where the pair runs grouped */
-    TEL_K_FFN_WGRAD_PAIR = 21, TEL_K_ATTN_WGRAD_PAIR = 22
+    /* the grouped weight-gradient kernel launches (W_2 with W_1, W_o with
+       W_qkv), and the launch after each: its split-K reduction and, for the
+       last, the LayerNorm gamma/beta sums (events back to back where the
+       pair needs no such launch); only where the pair runs grouped */
+    TEL_K_FFN_WGRAD_PAIR = 21, TEL_K_ATTN_WGRAD_PAIR = 22,
+    TEL_K_FFN_WGRAD_REDUCE = 23, TEL_K_ATTN_WGRAD_REDUCE = 24
 };
 
 /* Benchmark hook: from now on, every launch of kernel kernel_id (a TEL_K_*
@@ -246,7 +248,8 @@ enum {
  * grouped launch runs as two launches while one of its single ids
  * (TEL_K_*_WGRAD) is profiled: those two weight gradients and their bias
  * gradients may then take another k-split and round differently (every other
- * output keeps its bits).  The pair ids time the grouped launch as it runs. */
+ * output keeps its bits).  The pair ids time the grouped GEMM kernel alone,
+ * the reduce ids the launch that follows it. */
 tel_status tel_debug_kernel_events(tel_layer* layer, int kernel_id, void** start_events, void** stop_events,
                                    int count);
 

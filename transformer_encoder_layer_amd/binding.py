@@ -37,7 +37,7 @@ BUFFERS = {"drop1_in": 0, "drop1_out": 1, "drop2_in": 2, "drop2_out": 3, "attn_k
 KERNELS = {"ln1_fwd": 0, "qkv_fwd": 1, "attn_fwd": 2, "out_fwd": 3, "ln2_fwd": 4, "ffn1_fwd": 5, "ffn2_fwd": 6,
            "ffn2_dgrad": 10, "ffn2_wgrad": 11, "ffn1_dgrad": 12, "ffn1_wgrad": 13, "ln2_bwd": 14,
            "out_dgrad": 15, "out_wgrad": 16, "attn_bwd": 17, "qkv_dgrad": 18, "qkv_wgrad": 19, "ln1_bwd": 20,
-           "ffn_wgrad_pair": 21, "attn_wgrad_pair": 22}
+           "ffn_wgrad_pair": 21, "attn_wgrad_pair": 22, "ffn_wgrad_reduce": 23, "attn_wgrad_reduce": 24}
 
 
 class TelError(RuntimeError):

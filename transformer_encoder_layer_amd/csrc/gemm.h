@@ -93,9 +93,17 @@ struct ColsumJob {
     void* out;
 };
 constexpr int kMaxColsumJobs = 4;
+// Optional timing events (any may be null), recorded on the stream right
+// around the grouped GEMM kernel and around the launch after it (the split-K
+// reduction with the column sums; back to back when there is none).
+struct GroupEvents {
+    hipEvent_t gemm_start = nullptr, gemm_stop = nullptr;
+    hipEvent_t red_start = nullptr, red_stop = nullptr;
+};
 bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b);
 hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t stream,
-                             const ColsumJob* colsums = nullptr, int n_colsums = 0);
+                             const ColsumJob* colsums = nullptr, int n_colsums = 0,
+                             const GroupEvents* events = nullptr);
 // Workspace elements gemm_launch_group needs for the pair (0: none).
 size_t gemm_splitk_group_elems(const GemmDesc& a, const GemmDesc& b);
 

@@ -1379,7 +1379,12 @@ bool gemm_group_ok(const GemmDesc& a, const GemmDesc& b) {
 }
 
 template <typename T>
-static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJobs& cs) {
+static hipError_t launch_group_tail(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJobs& cs,
+                                    int splits, float* ws_a, float* ws_b);
+template <typename T>
+static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJobs& cs,
+                                   const GroupEvents& ev) {
+    auto mark = [&](hipEvent_t e) { return e ? hipEventRecord(e, st) : hipSuccess; };
     constexpr int BM = 256, BN = 256;
     const int splits = group_splits(a, b);
     auto kern = gemm_dl4_kernel<T, BM, BN, false, false, EPI_STORE>;
@@ -1415,12 +1420,28 @@ static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStre
         hipLaunchKernelGGL(zero_colsum_kernel<T>, dim3(zb + (unsigned)(cs.n * cs.blocks)), dim3(256), 0, st, z, zb, cs);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        if ((e = mark(ev.gemm_start)) != hipSuccess) return e;
         hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
-        return hipGetLastError();
+        if ((e = hipGetLastError()) != hipSuccess || (e = mark(ev.gemm_stop)) != hipSuccess) return e;
+        if ((e = mark(ev.red_start)) != hipSuccess) return e;
+        return mark(ev.red_stop);
     }
+    hipError_t e = mark(ev.gemm_start);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(gx), dim3(256), lds, st, G);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || (splits == 1 && cs.n == 0)) return e;
+    if ((e = hipGetLastError()) != hipSuccess || (e = mark(ev.gemm_stop)) != hipSuccess) return e;
+    if ((e = mark(ev.red_start)) != hipSuccess) return e;
+    e = launch_group_tail<T>(a, b, st, cs, splits, ws_a, ws_b);
+    if (e != hipSuccess) return e;
+    return mark(ev.red_stop);
+}
+
+// The launch after a grouped GEMM: the split-K reduction of both problems
+// with the column sums riding along, the column sums alone, or nothing.
+template <typename T>
+static hipError_t launch_group_tail(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJobs& cs,
+                                    int splits, float* ws_a, float* ws_b) {
+    if (splits == 1 && cs.n == 0) return hipSuccess;
     const unsigned extra = (unsigned)(cs.n * cs.blocks);
     if (splits == 1) {  // no partials to reduce: the column sums alone
         hipLaunchKernelGGL(splitk_reduce_pair_kernel<T>, dim3(extra), dim3(256), 0, st, ReduceJob{}, ReduceJob{}, 1,
@@ -1440,7 +1461,8 @@ static hipError_t launch_dl4_group(const GemmDesc& a, const GemmDesc& b, hipStre
 }
 
 hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t st, const ColsumJob* colsums,
-                             int n_colsums) {
+                             int n_colsums, const GroupEvents* events) {
+    const GroupEvents ev = events ? *events : GroupEvents{};
     if (!gemm_group_ok(a, b) || n_colsums < 0 || n_colsums > kMaxColsumJobs || (n_colsums && !colsums))
         return hipErrorInvalidValue;
     ColsumJobs cs{};
@@ -1452,8 +1474,8 @@ hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t s
         cs.blocks = std::max(cs.blocks, (c.N + 7) / 8);
     }
     switch (a.dtype) {
-        case 1: return launch_dl4_group<f16>(a, b, st, cs);
-        case 2: return launch_dl4_group<bf16>(a, b, st, cs);
+        case 1: return launch_dl4_group<f16>(a, b, st, cs, ev);
+        case 2: return launch_dl4_group<bf16>(a, b, st, cs, ev);
     }
     return hipErrorInvalidValue;
 }

@@ -668,8 +668,22 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     auto wgrad_pair = [&](int ka, const Wg& a, int kb, const Wg& b, bool with_ln) -> tel_status {
         const GemmDesc ga = wdesc(a), gb = wdesc(b);
         if (grouped(ka, a, kb, b)) {
-            const int pair = ka == TEL_K_FFN2_WGRAD ? TEL_K_FFN_WGRAD_PAIR : TEL_K_ATTN_WGRAD_PAIR;
-            TIMED(pair, gemm_launch_group(ga, gb, st, with_ln ? ln_fin : nullptr, with_ln ? n_ln_fin : 0));
+            const bool ffn = ka == TEL_K_FFN2_WGRAD;
+            const int pair = ffn ? TEL_K_FFN_WGRAD_PAIR : TEL_K_ATTN_WGRAD_PAIR;
+            const int red = ffn ? TEL_K_FFN_WGRAD_REDUCE : TEL_K_ATTN_WGRAD_REDUCE;
+            // profiled: events around the GEMM kernel, or around the launch after it
+            GroupEvents ev{};
+            if (L->prof_count > 0 && (L->prof_kernel == pair || L->prof_kernel == red)) {
+                const int pi = (int)(L->prof_calls++ % L->prof_count);
+                if (L->prof_kernel == pair) {
+                    ev.gemm_start = L->prof_start[pi];
+                    ev.gemm_stop = L->prof_stop[pi];
+                } else {
+                    ev.red_start = L->prof_start[pi];
+                    ev.red_stop = L->prof_stop[pi];
+                }
+            }
+            HIP_TRY(gemm_launch_group(ga, gb, st, with_ln ? ln_fin : nullptr, with_ln ? n_ln_fin : 0, &ev));
             if (with_ln) n_ln_fin = 0;
         } else {
             TIMED(ka, wgrad1(a));
