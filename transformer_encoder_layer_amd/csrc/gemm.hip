@@ -585,6 +585,26 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
 #pragma unroll
                 for (int j = 0; j < NI; ++j) acc[i][j] = MfmaOp<T>::mma(fb[j], fa[i], acc[i][j]);
         };
+        // the same MFMAs with the next tile's direct loads spread over them
+        // (one after every NQ/LPW-th MFMA) rather than issued together
+        constexpr int NQ = MI * NI;
+        static_assert(LPW <= NQ, "loads per MFMA block");
+        auto mfmas_issue = [&](const v8 (&fa)[MI], const v8 (&fb)[NI]) {
+            const uint32_t st = lds0 + (uint32_t)((issued % DNS) * STAGE * (int)sizeof(T));
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) {
+                acc[q / NI][q % NI] = MfmaOp<T>::mma(fb[q % NI], fa[q / NI], acc[q / NI][q % NI]);
+                if (q % (NQ / LPW) == 0 && q / (NQ / LPW) < LPW) {
+                    const int l = q / (NQ / LPW);
+                    if (l < DlPlan<T, AK, BM, NW>::PER) pa.issue_one(oa, st, wave_s, l);
+                    else pb.issue_one(ob, st + AEL * (uint32_t)sizeof(T), wave_s, l - DlPlan<T, AK, BM, NW>::PER);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            oa += sta;
+            ob += stb;
+            ++issued;
+        };
 
 #pragma unroll
         for (int s0 = 0; s0 < DNS - 1; ++s0)
@@ -612,10 +632,9 @@ __global__ __launch_bounds__(WGM* WGN * 64) void gemm_dl_kernel(GemmParams p) {
             __builtin_amdgcn_sched_barrier(0);
             wait_vmcnt<(DNS - 3) * LPW>();
             __syncthreads();
-            issue_next();
             read_ks(kt + 1, 0, fa0, fb0);
             __builtin_amdgcn_sched_barrier(0);
-            mfmas(fa1, fb1);
+            mfmas_issue(fa1, fb1);  // tile kt+3 into the stage tile kt-1 left
             __builtin_amdgcn_sched_barrier(0);
         }
         for (; kt < nk; ++kt) {
