@@ -37,6 +37,7 @@ def _hip_events(n):
     hip = ctypes.CDLL("libamdhip64.so")
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
     hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
     out = []
     for _ in range(n):
         e = ctypes.c_void_p()
@@ -93,7 +94,11 @@ def gpu_layer(w: syn.Workload, data, training=True, step=0, layer_id=0, dy_rows=
                                  B.make_grads(G))
             torch.cuda.synchronize()
             if hook is not None:
+                import ctypes
                 B.tel_debug_kernel_events(h, -1, None, None)
+                ms = ctypes.c_float()
+                assert hip.hipEventElapsedTime(ctypes.byref(ms), ev[0], ev[1]) == 0, "profiled events not recorded"
+                out["prof_ms"] = torch.tensor([ms.value], dtype=torch.float64)
                 for e in ev:
                     hip.hipEventDestroy(e)
             out["dx"] = dx

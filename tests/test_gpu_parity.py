@@ -300,6 +300,21 @@ def test_profiling_hook_keeps_results():
             assert np.array_equal(a[k], b[k]), k
 
 
+def test_profiling_pair_and_reduce_ids():
+    # The grouped weight-gradient ids time the GEMM kernel of the pair and the
+    # launch after it (its split-K reduction) without changing the launches:
+    # every output keeps its bits, and each event pair spans a positive time.
+    from transformer_encoder_layer_amd import binding as B
+    w = syn.WORKLOADS["bert_large"]
+    data = prepare(w, random_affine=True)
+    a = gpu_layer(w, data, step=1, layer_id=2)
+    for site in ("ffn_wgrad_pair", "ffn_wgrad_reduce", "attn_wgrad_pair", "attn_wgrad_reduce"):
+        b = gpu_layer(w, data, step=1, layer_id=2, prof_kernel=B.KERNELS[site])
+        assert float(b.pop("prof_ms")[0]) > 0.0, site
+        for k in a:
+            assert np.array_equal(a[k], b[k]), (site, k)
+
+
 def _full(name, layer_id=0, step=0, random_affine=False):
     # the whole batch with the full upstream gradient: every element of y,
     # dx and the twelve parameter gradients against the oracle
