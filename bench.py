@@ -161,6 +161,9 @@ def main():
                     help="relaxed-determinism mode (the weight-gradient pairs add their k-splits atomically)")
     ap.add_argument("--pack", action="store_true",
                     help="token packing: run the layers on the valid tokens of a padded workload")
+    ap.add_argument("--unchained", action="store_true",
+                    help="Pre-LN stacks: each layer applies its own site-2 dropout to dy, instead of the layer "
+                         "above doing it in its LayerNorm-1 backward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run plain device copies of 1 GiB (scale for the HBM byte counters)")
     args = ap.parse_args()
@@ -222,6 +225,10 @@ def main():
         theta, gates = 1.0, [True] * n_layers
     run = [l for l in range(n_layers) if gates[l]]
     stream = torch.cuda.current_stream().cuda_stream
+    # Pre-LN stacks chain the backward: each layer's LayerNorm-1 backward also
+    # writes the next run layer's site-2 masked gradient (two buffers in turn)
+    chain = w.pre_ln and not pack and not args.unchained
+    dxd = [torch.empty_like(x0), torch.empty_like(x0)] if chain else None
 
     def step():
         # skipped layers are the identity: their input buffer is passed on unchanged
@@ -232,10 +239,18 @@ def main():
             B.tel_layer_forward(handles[l], cparams[l], cur, lengths, 1, step_id, acts[l + 1], saved[l], scratch,
                                 stream)
             cur = acts[l + 1]
-        g = dy_top
-        for l in reversed(run):
-            B.tel_layer_backward(handles[l], cparams[l], inputs[l], lengths, 1, step_id, g, saved[l], scratch,
-                                 dgrads[l], cgrads[l], stream)
+        g, gd = dy_top, None
+        order = run[::-1]
+        for i, l in enumerate(order):
+            if chain:
+                below = handles[order[i + 1]] if i + 1 < len(order) else None
+                out_d = dxd[i % 2] if below is not None else None
+                B.tel_layer_backward_chain(handles[l], cparams[l], inputs[l], lengths, 1, step_id, g, gd, saved[l],
+                                           scratch, dgrads[l], below, out_d, cgrads[l], stream)
+                gd = out_d
+            else:
+                B.tel_layer_backward(handles[l], cparams[l], inputs[l], lengths, 1, step_id, g, saved[l], scratch,
+                                     dgrads[l], cgrads[l], stream)
             g = dgrads[l]
 
     for _ in range(args.warmup):
@@ -354,6 +369,7 @@ def main():
         "ms_per_layer_fwd_bwd": round(ms_per_step / n_run, 4),
         "valid_tokens_per_s": round(valid * n_run / (ms_per_step / 1e3), 1),
         "token_packing": pack,
+        "chained_backward": chain,
         "wall_s_timed": round(wall, 3),
         "step_ms": {"median": round(float(np.median(step_ms)), 4), "p10": round(float(np.percentile(step_ms, 10)), 4),
                     "p90": round(float(np.percentile(step_ms, 90)), 4)},

@@ -173,6 +173,36 @@ tel_status tel_layer_backward(tel_layer* layer, const tel_params* params, const 
                               const void* saved, void* scratch, void* dx, const tel_grads* grads,
                               tel_stream_t stream);
 
+/* Backward through a stack of Pre-LN layers, with the hidden dropout of each
+ * layer's FFN branch (DS guide: the layer's hidden_dropout_ratio; AI-infra
+ * blog section 5.1: mask / (1-p)) applied where the gradient is made.  In a
+ * Pre-LN layer y = x1 + drop2(FFN(LN2(x1))), so the backward needs both dy
+ * and drop2(dy); the layer above produces dy = its dx in its LayerNorm-1
+ * backward, and can apply this layer's mask in the same pass instead of a
+ * separate pass over dy here.  As tel_layer_backward, plus:
+ *   dy_dropped -- drop2(dy) with this layer's site-2 mask and 1/(1-p), as
+ *                 the layer above's call wrote it into its dx_dropped, or
+ *                 NULL (then computed here from dy);
+ *   below      -- the next layer down the stack (the one whose input
+ *                 gradient dx is), or NULL;
+ *   dx_dropped -- [B*S,H] out, required iff below is set: below's site-2
+ *                 mask and 1/(1-p) applied to dx as stored (dx rounded to
+ *                 the dtype), i.e. the dy_dropped of below's backward.  The
+ *                 mask is below's (its seed and layer id) at this call's step
+ *                 and training flag, so below's forward and backward must use
+ *                 the same step and training.
+ * Every output equals tel_layer_backward's bit for bit.  TEL_ERR_INVALID_ARG
+ * for a Post-LN layer (site 2 there follows its own LayerNorm backward and is
+ * fused already), below without dx_dropped or vice versa, or a below that is
+ * not a Pre-LN layer of the same batch, sequence, hidden size, dtype and
+ * hidden dropout; TEL_ERR_UNSUPPORTED under token packing.  dx_dropped may
+ * not alias dy, dy_dropped or dx. */
+tel_status tel_layer_backward_chain(tel_layer* layer, const tel_params* params, const void* x,
+                                    const int32_t* key_lengths, int training, uint64_t step, const void* dy,
+                                    const void* dy_dropped, const void* saved, void* scratch, void* dx,
+                                    const tel_layer* below, void* dx_dropped, const tel_grads* grads,
+                                    tel_stream_t stream);
+
 /* For callers that cannot allocate device memory (code under HIP graph
  * capture, tight serving loops, harnesses that forbid hipMalloc): the
  * inference forward (training = 0, nothing kept for a backward) of

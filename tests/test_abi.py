@@ -287,3 +287,32 @@ def test_stochastic_mode_is_a_plain_switch():
     finally:
         B.tel_layer_destroy(a)
         B.tel_layer_destroy(b)
+
+
+def test_backward_chain_validation_before_gpu():
+    # tel_layer_backward_chain: argument checks run before any GPU work
+    h = B.tel_layer_create(cfg())
+    hp = B.tel_layer_create(cfg(pre_ln=0))
+    hw = B.tel_layer_create(cfg(hidden=128, heads=8))
+    P = B.tel_params(*([4096] * 12))
+    G = B.tel_grads(*([4096] * 12))
+    try:
+        def chain(layer, dyd, below, dxd):
+            return B.tel_layer_backward_chain(layer, P, 4096, None, 1, 0, 4096, dyd, 4096, 4096, 4096, below, dxd, G,
+                                              0)
+        for args in ((hp, None, h, 8192),      # Post-LN layer
+                     (hp, 8192, None, None),
+                     (h, None, h, None),       # below without dx_dropped
+                     (h, None, None, 8192),    # dx_dropped without below
+                     (h, None, hp, 8192),      # below is Post-LN
+                     (h, None, hw, 8192),      # below of another hidden size
+                     (h, 8196, None, None)):   # misaligned dy_dropped
+            with pytest.raises(B.TelError) as e:
+                chain(*args)
+            assert e.value.status == B.TEL_ERR_INVALID_ARG, args
+        with pytest.raises(B.TelError) as e:   # valid chain arguments; no forward yet
+            chain(h, 8192, h, 12288)
+        assert e.value.status == B.TEL_ERR_STATE
+    finally:
+        for x in (h, hp, hw):
+            B.tel_layer_destroy(x)

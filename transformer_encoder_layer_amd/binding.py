@@ -25,7 +25,7 @@ PARAM_NAMES = ("w_qkv", "b_qkv", "w_o", "b_o", "ln1_g", "ln1_b",
 
 # every symbol declared in include/tel.h
 EXPORTS = ("tel_layer_create", "tel_layer_workspace_bytes", "tel_layer_forward", "tel_layer_forward_noalloc",
-           "tel_layer_backward",
+           "tel_layer_backward", "tel_layer_backward_chain",
            "tel_layer_set_valid_tokens", "tel_layer_destroy", "tel_last_error", "tel_debug_dropout_mask",
            "tel_debug_kernel_events", "tel_debug_attn_keep_bits", "tel_debug_buffer", "tel_check_key_lengths",
            "tel_debug_checks_enabled", "tel_pld_theta", "tel_pld_keep")
@@ -81,6 +81,8 @@ def lib(path: str = LIB_PATH):
         L.tel_layer_forward.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp, vp, vp]
         L.tel_layer_backward.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp, vp,
                                          vp, ctypes.POINTER(tel_grads), vp]
+        L.tel_layer_backward_chain.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, ctypes.c_int, u64, vp, vp,
+                                               vp, vp, vp, vp, vp, ctypes.POINTER(tel_grads), vp]
         L.tel_layer_forward_noalloc.argtypes = [vp, ctypes.POINTER(tel_params), vp, vp, vp, vp]
         L.tel_layer_set_valid_tokens.argtypes = [vp, ctypes.c_int64]
         L.tel_layer_destroy.argtypes = [vp]
@@ -170,6 +172,14 @@ def tel_layer_backward(handle, params: tel_params, x, key_lengths, training, ste
     _check(lib().tel_layer_backward(handle, ctypes.byref(params), ptr(x), ptr(key_lengths), int(training),
                                     int(step), ptr(dy), ptr(saved), ptr(scratch), ptr(dx), ctypes.byref(grads),
                                     stream_handle(stream)))
+
+
+def tel_layer_backward_chain(handle, params: tel_params, x, key_lengths, training, step, dy, dy_dropped, saved,
+                             scratch, dx, below, dx_dropped, grads: tel_grads, stream=None):
+    """below: handle of the next layer down, or None (then dx_dropped must be None)."""
+    _check(lib().tel_layer_backward_chain(handle, ctypes.byref(params), ptr(x), ptr(key_lengths), int(training),
+                                          int(step), ptr(dy), ptr(dy_dropped), ptr(saved), ptr(scratch), ptr(dx),
+                                          below, ptr(dx_dropped), ctypes.byref(grads), stream_handle(stream)))
 
 
 def tel_layer_destroy(handle):

@@ -210,10 +210,17 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
                 }
                 store4k<T, OUT_F32>(a.out, base + idx, dx);
                 if constexpr (DROP) {
+                    // the mask applies to dx as stored (rounded to T when
+                    // stored in T), exactly as a separate dropout pass over
+                    // the stored tensor would
+                    if constexpr (!OUT_F32) {
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) dx[i] = round_through<T>(dx[i]);
+                    }
                     if (a.drop.thr) {
                         const uint32_t k = kn[u][c];
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) dx[i] = ((k >> i) & 1u) ? dx[i] * a.drop.scale : 0.0f;
+                        for (int i = 0; i < 4; ++i) dx[i] = ((k >> i) & 1u) ? fp32_barrier(dx[i] * a.drop.scale) : 0.0f;
                     }
                     Vec4<T>::store((T*)a.drop_out + base + idx, dx);
                 }
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(256) void dropout_apply_kernel(const T* in, T* out,
         }
         const uint32_t k = keep8(d.rng, e >> 3, d.thr);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) v[i] = ((k >> i) & 1u) ? v[i] * d.scale : 0.0f;
+        for (int i = 0; i < 8; ++i) v[i] = ((k >> i) & 1u) ? fp32_barrier(v[i] * d.scale) : 0.0f;
     }
     Vec4<T>::store(out + i8, v);
     if (two) Vec4<T>::store(out + i8 + 4, v + 4);
@@ -356,11 +363,15 @@ static hipError_t ln_backward_t(const LnBwdArgs& a, hipStream_t st) {
         TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP | LNB_OUT_F32 | LNB_DROP)
         TEL_LNB(LNB_RES_LOWP | LNB_DROP)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP | LNB_DROP)
-        // Pre-LN, LN1: dx = dx1 + LN1'(da1), dx1 in fp32 or fp16 as above
+        // Pre-LN, LN1: dx = dx1 + LN1'(da1), dx1 in fp32 or fp16 as above;
+        // in a chained stack also the layer below's drop2(dx) (the fp16
+        // forms with the drop are the LN2 ones above)
         TEL_LNB(LNB_RES_F32)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_F32)
         TEL_LNB(LNB_RES_LOWP)
         TEL_LNB(LNB_FROM_OUT | LNB_RES_LOWP)
+        TEL_LNB(LNB_RES_F32 | LNB_DROP)
+        TEL_LNB(LNB_FROM_OUT | LNB_RES_F32 | LNB_DROP)
         // Post-LN, LN2: dz2 = LN2'(dy) in fp32, drop(dz2) for the FFN branch
         // (source z2 in fp32 or fp16, or the output y)
         TEL_LNB(LNB_SRC_F32 | LNB_OUT_F32 | LNB_DROP)

@@ -549,9 +549,14 @@ tel_status tel_layer_forward(tel_layer* L, const tel_params* P, const void* x, c
     return TEL_OK;
 }
 
-tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
-                              int training, uint64_t step, const void* dy, const void* saved, void* scratch,
-                              void* dx, const tel_grads* G, tel_stream_t stream) {
+// The backward, optionally chained through a Pre-LN stack: dy_dropped (if
+// set) is this layer's site-2 masked dy, computed by the layer above; below
+// (if set) is the next layer down, whose site-2 mask the LN1 backward applies
+// to dx into dx_dropped.
+static tel_status backward_impl(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
+                                int training, uint64_t step, const void* dy, const void* dy_dropped,
+                                const void* saved, void* scratch, void* dx, const tel_layer* below,
+                                void* dx_dropped, const tel_grads* G, tel_stream_t stream) {
     if (!L) return fail(TEL_ERR_INVALID_ARG, "layer is NULL");
     tel_status s = check_params(P);
     if (s != TEL_OK) return s;
@@ -564,6 +569,24 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     if (!aligned(dy) || !aligned(saved) || !aligned(scratch) || !aligned(dx) || (x && !aligned(x)) ||
         (key_lengths && !aligned(key_lengths)))
         return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+    const bool chained = dy_dropped || below || dx_dropped;
+    if (chained) {
+        if (!c.pre_ln)
+            return fail(TEL_ERR_INVALID_ARG, "chained backward is for Pre-LN layers (Post-LN applies site 2 "
+                                             "after its own LayerNorm backward)");
+        if (!below != !dx_dropped) return fail(TEL_ERR_INVALID_ARG, "below and dx_dropped go together");
+        if ((dy_dropped && !aligned(dy_dropped)) || (dx_dropped && !aligned(dx_dropped)))
+            return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
+        if (below) {
+            const tel_config& b = below->cfg;
+            if (b.batch != c.batch || b.seq != c.seq || b.hidden != c.hidden || b.dtype != c.dtype || !b.pre_ln ||
+                b.hidden_dropout != c.hidden_dropout)
+                return fail(TEL_ERR_INVALID_ARG, "below must be a Pre-LN layer of the same batch, sequence, hidden "
+                                                 "size, dtype and hidden dropout");
+        }
+        if (packed_rows(L, key_lengths))
+            return fail(TEL_ERR_UNSUPPORTED, "chained backward does not run on packed tokens");
+    }
     if (L->pending_fwd <= 0) return fail(TEL_ERR_STATE, "backward called without a preceding forward with saved state");
     hipStream_t st = (hipStream_t)stream;
     DEBUG_CHECK_LENGTHS(L, key_lengths, st);
@@ -721,16 +744,20 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     const void* g_src = gck ? bs.of(p.gck_g) : bs.of(p.g);
 
     if (c.pre_ln) {
-        // y = x1 + drop2(g W2^T + b2)
-        HIP_TRY(dropout_apply(dt, dyin, bs.of(p.df), (size_t)T * H, d2, st, rmap, H));
-        GemmDesc g = dgrad(bs.of(p.df), P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
+        // y = x1 + drop2(g W2^T + b2); drop2(dy) handed down by the layer above, or made here
+        const void* df = dy_dropped;
+        if (!df) {
+            HIP_TRY(dropout_apply(dt, dyin, bs.of(p.df), (size_t)T * H, d2, st, rmap, H));
+            df = bs.of(p.df);
+        }
+        GemmDesc g = dgrad(df, P->w_2, H, F, gck ? EPI_GELU_BWD : EPI_MUL_AUX);
         g.ea.out = bs.of(p.du); g.ea.ldo = F; g.ea.aux = bs.of(p.u);
         if (gck) g.ea.out2 = bs.of(p.gck_g);
         TIMED(TEL_K_FFN2_DGRAD, gemm_launch(g, st));
         g = dgrad(bs.of(p.du), P->w_1, F, H, EPI_STORE);
         g.ea.out = bs.of(p.dgemm); g.ea.ldo = H;
         TIMED(TEL_K_FFN1_DGRAD, gemm_launch(g, st));
-        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{bs.of(p.df), g_src, H, F, G->w_2, G->b_2},
+        s = wgrad_pair(TEL_K_FFN2_WGRAD, Wg{df, g_src, H, F, G->w_2, G->b_2},
                        TEL_K_FFN1_WGRAD, Wg{bs.of(p.du), bs.of(p.ln2_out), F, H, G->w_1, G->b_1}, false);
         if (s != TEL_OK) return s;
         // x1 -> LN2: dx1 = dy + LN2'(da2); dz = drop1(dx1)
@@ -766,6 +793,10 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
         lb.gamma = P->ln1_g; lb.beta = P->ln1_b;
         lb.res = bs.of(p.dres); lb.res_f32 = r32;
         lb.out = dxout; lb.out_f32 = 0;
+        if (below) {  // the layer below's drop2(dx), from dx as stored
+            lb.drop_out = dx_dropped;
+            lb.drop = make_drop(below, below->cfg.hidden_dropout, 2, step, training);
+        }
         lb.part_g = part_ln1_g; lb.part_b = part_ln1_b; lb.row_map = rmap;
         TIMED(TEL_K_LN1_BWD, ln_backward(lb, st));
         HIP_TRY(ln_grads(part_ln1_g, part_ln1_b, G->ln1_g, G->ln1_b));
@@ -825,6 +856,22 @@ tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, 
     L->pending_fwd--;
     g_err.clear();
     return TEL_OK;
+}
+
+
+tel_status tel_layer_backward(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
+                              int training, uint64_t step, const void* dy, const void* saved, void* scratch,
+                              void* dx, const tel_grads* G, tel_stream_t stream) {
+    return backward_impl(L, P, x, key_lengths, training, step, dy, nullptr, saved, scratch, dx, nullptr, nullptr, G,
+                         stream);
+}
+
+tel_status tel_layer_backward_chain(tel_layer* L, const tel_params* P, const void* x, const int32_t* key_lengths,
+                                    int training, uint64_t step, const void* dy, const void* dy_dropped,
+                                    const void* saved, void* scratch, void* dx, const tel_layer* below,
+                                    void* dx_dropped, const tel_grads* G, tel_stream_t stream) {
+    return backward_impl(L, P, x, key_lengths, training, step, dy, dy_dropped, saved, scratch, dx, below,
+                         dx_dropped, G, stream);
 }
 
 tel_status tel_debug_kernel_events(tel_layer* L, int kernel_id, void** start_events, void** stop_events,

@@ -71,9 +71,21 @@ def _round256(n: int) -> int:
     return (n + 255) // 256 * 256
 
 
+class _Chain:
+    """One forward's hand-down of site-2 masked gradients through a Pre-LN
+    stack (tel_layer_backward_chain): the backward of a layer writes the
+    masked dx of the run layer below it, which that layer's backward takes
+    as its drop2(dy) only while its dy is still that same, unmodified dx
+    tensor (same storage and version counter); otherwise it masks dy
+    itself.  The results are the same bits either way."""
+
+    def __init__(self):
+        self.pending = None  # (layer it is for, dx, dx._version, masked dx)
+
+
 class _LayerFn(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, x, lengths, step, valid, layer, *params):
+    def forward(ctx, x, lengths, step, valid, layer, chain, below, *params):
         dev = x.device
         if valid is not None:
             B.tel_layer_set_valid_tokens(layer.handle, valid)
@@ -95,6 +107,7 @@ class _LayerFn(torch.autograd.Function):
         ctx.save_for_backward(x, *params)
         ctx.lengths = lengths
         ctx.valid = valid
+        ctx.chain, ctx.below = chain, below
         return y
 
     @staticmethod
@@ -107,11 +120,28 @@ class _LayerFn(torch.autograd.Function):
         scratch = scratch_buffer(x.device, layer.scratch_bytes)
         if ctx.valid is not None:
             B.tel_layer_set_valid_tokens(layer.handle, ctx.valid)
-        B.tel_layer_backward(layer.handle, B.make_params(dict(zip(B.PARAM_NAMES, params))), x, ctx.lengths,
-                             ctx.training_flag, ctx.step, dy, ctx.saved_buf, scratch, dx,
-                             B.make_grads(dict(zip(B.PARAM_NAMES, grads))))
+        P = B.make_params(dict(zip(B.PARAM_NAMES, params)))
+        G = B.make_grads(dict(zip(B.PARAM_NAMES, grads)))
+        chain, below = ctx.chain, ctx.below
+        dyd = None
+        if chain is not None:
+            pend, chain.pending = chain.pending, None
+            if (pend is not None and pend[0] is layer and pend[1].data_ptr() == dy.data_ptr()
+                    and pend[1].shape == dy.shape and pend[1].stride() == dy.stride() and dy._version == pend[2]):
+                dyd = pend[3]
+        if dyd is not None or below is not None:
+            dxd = torch.empty_like(x) if below is not None else None
+            B.tel_layer_backward_chain(layer.handle, P, x, ctx.lengths, ctx.training_flag, ctx.step, dy, dyd,
+                                       ctx.saved_buf, scratch, dx, below.handle if below is not None else None,
+                                       dxd, G)
+            if below is not None:
+                chain.pending = (below, dx, dx._version, dxd)
+        else:
+            B.tel_layer_backward(layer.handle, P, x, ctx.lengths, ctx.training_flag, ctx.step, dy, ctx.saved_buf,
+                                 scratch, dx, G)
         ctx.saved_buf = None
-        return (dx, None, None, None, None, *grads)
+        ctx.chain = ctx.below = None
+        return (dx, None, None, None, None, None, None, *grads)
 
 
 class EncoderLayer(torch.nn.Module):
@@ -134,13 +164,16 @@ class EncoderLayer(torch.nn.Module):
         return [getattr(self, n) for n in B.PARAM_NAMES]
 
     def forward(self, x: torch.Tensor, key_lengths: Optional[torch.Tensor] = None, step: int = 0,
-                valid_tokens: Optional[int] = None):
+                valid_tokens: Optional[int] = None, _chain: Optional[_Chain] = None,
+                _below: Optional["EncoderLayer"] = None):
         """valid_tokens: sum of key_lengths (token packing); computed on the
-        host from key_lengths when packing is on and it is not given."""
+        host from key_lengths when packing is on and it is not given.
+        _chain, _below: set by EncoderStack (the stack's hand-down of masked
+        gradients and the run layer below this one)."""
         valid = None
         if self.cfg.pack_tokens and key_lengths is not None:
             valid = int(key_lengths.sum().item()) if valid_tokens is None else int(valid_tokens)
-        return _LayerFn.apply(x, key_lengths, int(step), valid, self, *self.params())
+        return _LayerFn.apply(x, key_lengths, int(step), valid, self, _chain, _below, *self.params())
 
     def __del__(self):
         h = getattr(self, "handle", None)
@@ -194,9 +227,16 @@ class EncoderStack(torch.nn.Module):
         """A dropped layer is the identity: its input passes on unchanged, in
         the forward and (through autograd) in the backward.  taps: optional
         list that receives (layer index, input tensor) of every layer run."""
-        for i, (layer, keep) in enumerate(zip(self.layers, self.gates(step))):
-            if keep:
-                if taps is not None:
-                    taps.append((i, x))
-                x = layer(x, key_lengths, step)
+        run = [(i, layer) for i, (layer, keep) in enumerate(zip(self.layers, self.gates(step))) if keep]
+        # Pre-LN, unpacked: each layer's backward masks the gradient of the
+        # run layer below it (tel_layer_backward_chain)
+        chain = _Chain() if (self.layers[0].cfg.pre_ln and not self.layers[0].cfg.pack_tokens
+                             and torch.is_grad_enabled()) else None
+        for j, (i, layer) in enumerate(run):
+            if taps is not None:
+                taps.append((i, x))
+            below = run[j - 1][1] if chain is not None and j > 0 else None
+            if below is not None and below.training != layer.training:
+                below = None
+            x = layer(x, key_lengths, step, _chain=chain, _below=below)
         return x
