@@ -41,6 +41,14 @@ __device__ __forceinline__ void store4k(void* p, size_t off, const float v[4]) {
     else Vec4<T>::store((T*)p + off, v);
 }
 
+// x passed through an empty register barrier: a product feeding a rounding
+// to fp16/bf16 stays an fp32 product, so two kernels that scale the same
+// stored values round the same way (a mixed-precision fma would round once).
+__device__ __forceinline__ float fp32_barrier(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
 template <typename T, int NC, bool XF32>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const int lane = threadIdx.x & 63;

@@ -220,14 +220,6 @@ __device__ __forceinline__ void normal_cdf_pdf(float u, float& cdf, float& pdf) 
     pdf = __fmul_rn(e, 0.39894228040143268f);
 }
 
-// x passed through an empty register barrier: a product feeding a rounding
-// to fp16/bf16 stays an fp32 product, so two kernels that scale the same
-// stored values round the same way (a mixed-precision fma would round once).
-__device__ __forceinline__ float fp32_barrier(float x) {
-    asm volatile("" : "+v"(x));
-    return x;
-}
-
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
