@@ -153,7 +153,13 @@ struct Epi {
                 g[i] = __fmul_rn(u, cdf);               // GELU(u)
                 d[i] = e.gelu_grad_out ? __fmaf_rn(u, pdf, cdf) : u;  // GELU'(u) or u
             }
-            Vec4<T>::store((T*)e.out + off, d);
+            // GELU'(u) (or u) is next read in the backward: a non-temporal
+            // store; GELU(u) feeds the next GEMM and stays cacheable
+            {
+                typedef T t4 __attribute__((ext_vector_type(4)));
+                const t4 q = {(T)d[0], (T)d[1], (T)d[2], (T)d[3]};
+                __builtin_nontemporal_store(q, reinterpret_cast<t4*>((T*)e.out + off));
+            }
             if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
         } else if constexpr (EPI == EPI_GELU_BWD) {
             // GELU'(u) rounded to the storage type, exactly as the forward
