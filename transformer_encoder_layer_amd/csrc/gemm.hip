@@ -39,6 +39,26 @@ __device__ __forceinline__ void atomic_add2(bf16* out, float v0, float v1) {
                                                (s2){__builtin_bit_cast(short, a), __builtin_bit_cast(short, b)});
 }
 
+// Non-temporal forms, for data whose next reader is far away (the
+// backward, the optimizer) or that is read for the last time: they do not
+// displace cache lines that the kernels in between still use.
+template <typename T>
+__device__ __forceinline__ void store4_nt(T* p, const float v[4]) {
+    typedef T t4 __attribute__((ext_vector_type(4)));
+    const t4 q = {(T)v[0], (T)v[1], (T)v[2], (T)v[3]};
+    __builtin_nontemporal_store(q, reinterpret_cast<t4*>(p));
+}
+__device__ __forceinline__ void load4f_nt(const float* p, float v[4]) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 q = __builtin_nontemporal_load(reinterpret_cast<const f4*>(p));
+    v[0] = q[0]; v[1] = q[1]; v[2] = q[2]; v[3] = q[3];
+}
+__device__ __forceinline__ uint2 load8_nt(const void* p) {
+    typedef unsigned u2 __attribute__((ext_vector_type(2)));
+    const u2 q = __builtin_nontemporal_load(reinterpret_cast<const u2*>(p));
+    return make_uint2(q[0], q[1]);
+}
+
 // Each epilogue works on 4 consecutive columns n..n+3 of row m.  It is split
 // into loads (per-column bias, per-element residual / GELU input) and the
 // compute-and-store, so that a kernel can issue every load of a block of
@@ -82,6 +102,11 @@ struct Epi {
             src = (const float*)e.res + off;
         }
         const uint2* q = reinterpret_cast<const uint2*>(src);
+        if constexpr (EPI == EPI_GELU_BWD || EPI == EPI_MUL_AUX) {
+            // GELU'(u) or u: this is its last read
+            const uint2 lo = load8_nt(q);
+            return make_uint4(lo.x, lo.y, lo.x, lo.y);
+        }
         const uint2 lo = q[0];
         const uint2 hi = q[f32 ? 1 : 0];
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
@@ -155,11 +180,7 @@ struct Epi {
             }
             // GELU'(u) (or u) is next read in the backward: a non-temporal
             // store; GELU(u) feeds the next GEMM and stays cacheable
-            {
-                typedef T t4 __attribute__((ext_vector_type(4)));
-                const t4 q = {(T)d[0], (T)d[1], (T)d[2], (T)d[3]};
-                __builtin_nontemporal_store(q, reinterpret_cast<t4*>((T*)e.out + off));
-            }
+            store4_nt<T>((T*)e.out + off, d);
             if (e.out2) Vec4<T>::store((T*)e.out2 + off, g);
         } else if constexpr (EPI == EPI_GELU_BWD) {
             // GELU'(u) rounded to the storage type, exactly as the forward
@@ -1048,15 +1069,19 @@ __device__ __forceinline__ void splitk_reduce_body(size_t i4, const float* ws, i
         Vec4<T>::store(rs_out + i4, r);
     }
     if (i4 >= MN) return;
+    // the partials are read once and the weight gradient is next read by the
+    // caller's optimizer: non-temporal both ways
     float v[4] = {0, 0, 0, 0};
     for (int z = 0; z < splits; ++z) {
         float t[4];
-        Vec4<float>::load(ws + z * MN + i4, t);
+        load4f_nt(ws + z * MN + i4, t);
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] += t[i];
     }
     const int m = (int)(i4 / N), n = (int)(i4 - (size_t)m * N);
-    epilogue4<T, EPI_STORE>(ea, m, n, v);
+    const size_t off = (size_t)m * ea.ldo + n;
+    if (ea.out_f32) store4_nt<float>((float*)ea.out + off, v);
+    else store4_nt<T>((T*)ea.out + off, v);
 }
 
 template <typename T>
