@@ -323,9 +323,12 @@ def main():
             ach = gemm_flops[site] / (avg_ms / 1e3) / 1e12
             meas = MEASURED_TRAFFIC.get((site, w.name))
             traffic = meas[1] if meas and meas[0] == digest and not pack else None
-            return {"kernel": site, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(ach / peak, 4), "traffic": traffic, "avg_launch_us": round(avg_ms * 1e3, 2),
-                    "launches": len(ms), "algorithmic_per_launch": gemm_flops[site]}
+            out_s = {"kernel": site, "bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(ach / peak, 4), "traffic": traffic, "avg_launch_us": round(avg_ms * 1e3, 2),
+                     "launches": len(ms), "algorithmic_per_launch": gemm_flops[site]}
+            if site.endswith("_wgrad_pair"):  # a grouped launch always runs the four-wave 256x256 kernel
+                out_s["symbol"] = f"gemm_dl4_kernel<{w.dtype},256,256,0,0,0>"
+            return out_s
         e = 2 if w.dtype != "f32" else 4
         ln_bytes = {"ln1_fwd": 2 * Tg * H * e + 8 * Tg, "ln2_fwd": Tg * H * (4 + e) + 8 * Tg}
         byts = ln_bytes.get(site, float("nan"))
