@@ -70,8 +70,8 @@
  * takes x, key_lengths, training and step again (the forward keeps no
  * pointers, and dropout masks are regenerated from them); tel_pld_keep
  * returns int32_t; tel_config orders its fields as below and adds
- * pack_tokens; token packing, the kernel-event hook, the debug buffer hooks
- * and tel_check_key_lengths are additions.
+ * pack_tokens; token packing, the chained Pre-LN backward, the kernel-event
+ * hook, the debug buffer hooks and tel_check_key_lengths are additions.
  */
 #ifndef TEL_H
 #define TEL_H
