@@ -35,6 +35,22 @@ __device__ __forceinline__ void load4k(const void* p, size_t off, float v[4]) {
     if constexpr (F32) Vec4<float>::load((const float*)p + off, v);
     else Vec4<T>::load((const T*)p + off, v);
 }
+// store4k with a non-temporal hint: the LayerNorm backward's gradient output
+// is read next only after several other kernels (the next LayerNorm
+// backward, or the layer below's), so it should not displace the lines the
+// kernels in between read.
+template <typename T, bool F32>
+__device__ __forceinline__ void store4k_nt(void* p, size_t off, const float v[4]) {
+    if constexpr (F32 || sizeof(T) == 4) {
+        typedef float f4 __attribute__((ext_vector_type(4)));
+        const f4 q = {v[0], v[1], v[2], v[3]};
+        __builtin_nontemporal_store(q, reinterpret_cast<f4*>((float*)p + off));
+    } else {
+        typedef T t4 __attribute__((ext_vector_type(4)));
+        const t4 q = {(T)v[0], (T)v[1], (T)v[2], (T)v[3]};
+        __builtin_nontemporal_store(q, reinterpret_cast<t4*>((T*)p + off));
+    }
+}
 template <typename T, bool F32>
 __device__ __forceinline__ void store4k(void* p, size_t off, const float v[4]) {
     if constexpr (F32) Vec4<float>::store((float*)p + off, v);
@@ -216,7 +232,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
                     dx[i] = rsv[u] * (dy[u][c][i] * gam[c][i] - mg - xh[u][c][i] * mgx);
                     if constexpr (RES != 0) dx[i] += r[u][c][i];
                 }
-                store4k<T, OUT_F32>(a.out, base + idx, dx);
+                store4k_nt<T, OUT_F32>(a.out, base + idx, dx);
                 if constexpr (DROP) {
                     // the mask applies to dx as stored (rounded to T when
                     // stored in T), exactly as a separate dropout pass over
