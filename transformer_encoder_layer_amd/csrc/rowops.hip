@@ -65,6 +65,25 @@ __device__ __forceinline__ float fp32_barrier(float x) {
     return x;
 }
 
+// Sum over the 64 lanes of a wave, the same value in every lane: DPP adds
+// within each row of 16 lanes (quad swaps, then rotations by 4 and 8), then
+// the four row sums read from lanes 0, 16, 32 and 48 -- no LDS round trips.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float wave_sum64(float v) {
+    v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_f32<0x124>(v);  // row_ror:4
+    v += dpp_f32<0x128>(v);  // row_ror:8
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
+
 template <typename T, int NC, bool XF32>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const int lane = threadIdx.x & 63;
@@ -86,7 +105,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
         if (!col_ok<NC>(c, lane, H)) v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.0f;
         s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
     }
-    const float mean = wave_sum(s) / (float)H;
+    const float mean = wave_sum64(s) * (1.0f / (float)H);
     float s2 = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -98,7 +117,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
             }
         }
     }
-    const float var = wave_sum(s2) / (float)H;
+    const float var = wave_sum64(s2) * (1.0f / (float)H);
     const float rs = 1.0f / sqrtf(var + a.eps);
     if (row >= a.T) return;
 #pragma unroll
@@ -218,8 +237,8 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int row = row0 + rr + u;
-            const float mg = wave_sum(s1[u]) / (float)H;
-            const float mgx = wave_sum(s2[u]) / (float)H;
+            const float mg = wave_sum64(s1[u]) * (1.0f / (float)H);
+            const float mgx = wave_sum64(s2[u]) * (1.0f / (float)H);
             if (row >= a.T) continue;
             const size_t base = (size_t)row * H;
 #pragma unroll

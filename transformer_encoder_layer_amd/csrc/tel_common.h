@@ -220,11 +220,4 @@ __device__ __forceinline__ void normal_cdf_pdf(float u, float& cdf, float& pdf) 
     pdf = __fmul_rn(e, 0.39894228040143268f);
 }
 
-// ---------------------------------------------------------------- wave ops
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
-}
-
 }  // namespace tel
