@@ -19,8 +19,10 @@ namespace tel {
 // lane l holds the NC groups of 4 consecutive columns c*256 + 4l .. +3
 // (c < NC, NC = ceil(H / 256)), so each load or store of a group is one
 // 8- or 16-byte access and a wave covers 256 contiguous columns per group.
-template <int NC>
-__device__ __forceinline__ bool col_ok(int c, int lane, int H) { return c * 256 + lane * 4 < H; }
+// FULL: H is exactly NC * 256, every group is in range and no mask is
+// needed (the kernels are instantiated both ways and picked at launch).
+template <bool FULL>
+__device__ __forceinline__ bool col_ok(int c, int lane, int H) { return FULL || c * 256 + lane * 4 < H; }
 
 // Every load of a row is issued unconditionally so that they are all in
 // flight together: a lane whose column group lies beyond H (H need not be a
@@ -28,7 +30,10 @@ __device__ __forceinline__ bool col_ok(int c, int lane, int H) { return c * 256 
 // masked to zero; rows past T read row T-1 and store nothing.  (Loads under
 // per-lane or per-flag branches would each be followed by a full memory
 // wait at the branch join.)
-__device__ __forceinline__ int col_clamped(int c, int lane, int H) { return min(c * 256 + lane * 4, H - 4); }
+template <bool FULL>
+__device__ __forceinline__ int col_clamped(int c, int lane, int H) {
+    return FULL ? c * 256 + lane * 4 : min(c * 256 + lane * 4, H - 4);
+}
 
 template <typename T, bool F32>
 __device__ __forceinline__ void load4k(const void* p, size_t off, float v[4]) {
@@ -84,7 +89,7 @@ __device__ __forceinline__ float wave_sum64(float v) {
     return (r0 + r1) + (r2 + r3);
 }
 
-template <typename T, int NC, bool XF32>
+template <typename T, int NC, bool XF32, bool FULL>
 __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     const int lane = threadIdx.x & 63;
     const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -94,7 +99,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     float v[NC][4], g[NC][4], bt[NC][4];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int idx = col_clamped(c, lane, H);
+        const int idx = col_clamped<FULL>(c, lane, H);
         load4k<T, XF32>(a.x, base + idx, v[c]);
         Vec4<T>::load((const T*)a.gamma + idx, g[c]);
         Vec4<T>::load((const T*)a.beta + idx, bt[c]);
@@ -102,14 +107,14 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
     float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (!col_ok<NC>(c, lane, H)) v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.0f;
+        if (!col_ok<FULL>(c, lane, H)) v[c][0] = v[c][1] = v[c][2] = v[c][3] = 0.0f;
         s += (v[c][0] + v[c][1]) + (v[c][2] + v[c][3]);
     }
     const float mean = wave_sum64(s) * (1.0f / (float)H);
     float s2 = 0.0f;
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        if (col_ok<NC>(c, lane, H)) {
+        if (col_ok<FULL>(c, lane, H)) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float dlt = v[c][i] - mean;
@@ -123,7 +128,7 @@ __global__ __launch_bounds__(256) void ln_fwd_kernel(LnFwdArgs a) {
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
         const int idx = c * 256 + lane * 4;
-        if (col_ok<NC>(c, lane, H)) {
+        if (col_ok<FULL>(c, lane, H)) {
             float y[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) y[i] = (v[c][i] - mean) * rs * g[c][i] + bt[c][i];
@@ -153,7 +158,7 @@ enum : int {
     LNB_DROP = 64
 };
 
-template <typename T, int NC, int MODE>
+template <typename T, int NC, int MODE, bool FULL>
 __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
     constexpr bool SRC_F32 = MODE & LNB_SRC_F32, FROM_OUT = MODE & LNB_FROM_OUT, ADD = MODE & LNB_ADD;
     constexpr bool OUT_F32 = MODE & LNB_OUT_F32, DROP = MODE & LNB_DROP;
@@ -164,7 +169,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
     float gam[NC][4], bet[NC][4], pg[NC][4], pb[NC][4];
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
-        const int idx = col_clamped(c, lane, H);
+        const int idx = col_clamped<FULL>(c, lane, H);
         Vec4<T>::load((const T*)a.gamma + idx, gam[c]);
         if constexpr (FROM_OUT) Vec4<T>::load((const T*)a.beta + idx, bet[c]);
 #pragma unroll
@@ -182,7 +187,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
             muv[u] = FROM_OUT ? 0.0f : a.mu[rowc];
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const int idx = col_clamped(c, lane, H);
+                const int idx = col_clamped<FULL>(c, lane, H);
                 Vec4<T>::load((const T*)a.dout + base + idx, dy[u][c]);
                 if constexpr (ADD) {
                     float t[4];
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
             const bool rok = row0 + rr + u < a.T;
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
-                const bool ok = rok && col_ok<NC>(c, lane, H);
+                const bool ok = rok && col_ok<FULL>(c, lane, H);
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float d = ok ? dy[u][c][i] : 0.0f;
@@ -244,7 +249,7 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int idx = c * 256 + lane * 4;
-                if (!col_ok<NC>(c, lane, H)) continue;
+                if (!col_ok<FULL>(c, lane, H)) continue;
                 float dx[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -346,16 +351,21 @@ __global__ __launch_bounds__(256) void mask_dump_kernel(Drop d, uint8_t* out, si
 }
 
 // ------------------------------------------------------------------ launchers
+template <typename T, int NC, bool XF32>
+static void ln_fwd_launch(const LnFwdArgs& a, dim3 grid, dim3 blk, hipStream_t st) {
+    if (a.H == NC * 256) hipLaunchKernelGGL((ln_fwd_kernel<T, NC, XF32, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((ln_fwd_kernel<T, NC, XF32, false>), grid, blk, 0, st, a);
+}
 template <typename T, bool XF32>
 static hipError_t ln_forward_x(const LnFwdArgs& a, hipStream_t st) {
     dim3 grid((a.T + 3) / 4), blk(256);
     switch ((a.H + 255) / 256) {
-        case 1: hipLaunchKernelGGL((ln_fwd_kernel<T, 1, XF32>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((ln_fwd_kernel<T, 2, XF32>), grid, blk, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((ln_fwd_kernel<T, 3, XF32>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((ln_fwd_kernel<T, 4, XF32>), grid, blk, 0, st, a); break;
-        case 5: case 6: hipLaunchKernelGGL((ln_fwd_kernel<T, 6, XF32>), grid, blk, 0, st, a); break;
-        case 7: case 8: hipLaunchKernelGGL((ln_fwd_kernel<T, 8, XF32>), grid, blk, 0, st, a); break;
+        case 1: ln_fwd_launch<T, 1, XF32>(a, grid, blk, st); break;
+        case 2: ln_fwd_launch<T, 2, XF32>(a, grid, blk, st); break;
+        case 3: ln_fwd_launch<T, 3, XF32>(a, grid, blk, st); break;
+        case 4: ln_fwd_launch<T, 4, XF32>(a, grid, blk, st); break;
+        case 5: case 6: ln_fwd_launch<T, 6, XF32>(a, grid, blk, st); break;
+        case 7: case 8: ln_fwd_launch<T, 8, XF32>(a, grid, blk, st); break;
         default: return hipErrorInvalidValue;  // H <= 2048
     }
     return hipGetLastError();
@@ -376,16 +386,21 @@ hipError_t ln_forward(const LnFwdArgs& a, hipStream_t st) {
 
 int ln_backward_parts(int T) { return (T + 4 * LN_RPW - 1) / (4 * LN_RPW); }
 
+template <typename T, int NC, int MODE>
+static void ln_bwd_launch(const LnBwdArgs& a, dim3 grid, dim3 blk, hipStream_t st) {
+    if (a.H == NC * 256) hipLaunchKernelGGL((ln_bwd_kernel<T, NC, MODE, true>), grid, blk, 0, st, a);
+    else hipLaunchKernelGGL((ln_bwd_kernel<T, NC, MODE, false>), grid, blk, 0, st, a);
+}
 template <typename T, int MODE>
 static hipError_t ln_backward_m(const LnBwdArgs& a, hipStream_t st) {
     dim3 grid(ln_backward_parts(a.T)), blk(256);
     switch ((a.H + 255) / 256) {
-        case 1: hipLaunchKernelGGL((ln_bwd_kernel<T, 1, MODE>), grid, blk, 0, st, a); break;
-        case 2: hipLaunchKernelGGL((ln_bwd_kernel<T, 2, MODE>), grid, blk, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((ln_bwd_kernel<T, 3, MODE>), grid, blk, 0, st, a); break;
-        case 4: hipLaunchKernelGGL((ln_bwd_kernel<T, 4, MODE>), grid, blk, 0, st, a); break;
-        case 5: case 6: hipLaunchKernelGGL((ln_bwd_kernel<T, 6, MODE>), grid, blk, 0, st, a); break;
-        case 7: case 8: hipLaunchKernelGGL((ln_bwd_kernel<T, 8, MODE>), grid, blk, 0, st, a); break;
+        case 1: ln_bwd_launch<T, 1, MODE>(a, grid, blk, st); break;
+        case 2: ln_bwd_launch<T, 2, MODE>(a, grid, blk, st); break;
+        case 3: ln_bwd_launch<T, 3, MODE>(a, grid, blk, st); break;
+        case 4: ln_bwd_launch<T, 4, MODE>(a, grid, blk, st); break;
+        case 5: case 6: ln_bwd_launch<T, 6, MODE>(a, grid, blk, st); break;
+        case 7: case 8: ln_bwd_launch<T, 8, MODE>(a, grid, blk, st); break;
         default: return hipErrorInvalidValue;  // H <= 2048 (LDS of the partial reduction)
     }
     return hipGetLastError();
