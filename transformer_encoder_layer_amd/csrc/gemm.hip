@@ -1103,9 +1103,9 @@ struct ReduceJob {
 struct ColsumJobs {
     ColsumJob j[kMaxColsumJobs];
     int n;
-    int blocks;  // workgroups per job: (N + 7) / 8 of the widest job
+    int blocks;  // workgroups per job: N / kColsumCols (rounded up) of the widest job
 };
-// The first cs.n * cs.blocks workgroups each sum 8 columns of one
+// The first cs.n * cs.blocks workgroups each sum kColsumCols columns of one
 // column-sum job (first, so that their latency-bound loads overlap the
 // reduction); then blocks0 workgroups reduce problem a and the rest problem b.
 template <typename T>
@@ -1113,10 +1113,10 @@ __global__ __launch_bounds__(256) void splitk_reduce_pair_kernel(ReduceJob a, Re
                                                                  unsigned blocks0, ColsumJobs cs) {
     const unsigned extra = (unsigned)(cs.n * cs.blocks);
     if (blockIdx.x < extra) {
-        __shared__ float red[32][9];
-        const int job = (int)(blockIdx.x / (unsigned)cs.blocks), n0 = (int)(blockIdx.x % (unsigned)cs.blocks) * 8;
+        __shared__ float red[256 / kColsumCols][kColsumCols + 1];
+        const int job = (int)(blockIdx.x / (unsigned)cs.blocks), n0 = (int)(blockIdx.x % (unsigned)cs.blocks) * kColsumCols;
         const ColsumJob& c = cs.j[job];
-        if (n0 < c.N) colsum8_block<T>(c.part, c.P, c.N, reinterpret_cast<T*>(c.out), n0, red);  // block-uniform
+        if (n0 < c.N) colsum_block<T>(c.part, c.P, c.N, reinterpret_cast<T*>(c.out), n0, red);  // block-uniform
         return;
     }
     const unsigned bid = blockIdx.x - extra;
@@ -1145,11 +1145,11 @@ __global__ __launch_bounds__(256) void zero_colsum_kernel(ZeroJobs z, unsigned z
         }
         return;
     }
-    __shared__ float red[32][9];
+    __shared__ float red[256 / kColsumCols][kColsumCols + 1];
     const unsigned bid = blockIdx.x - zero_blocks;
-    const int job = (int)(bid / (unsigned)cs.blocks), n0 = (int)(bid % (unsigned)cs.blocks) * 8;
+    const int job = (int)(bid / (unsigned)cs.blocks), n0 = (int)(bid % (unsigned)cs.blocks) * kColsumCols;
     const ColsumJob& c = cs.j[job];
-    if (n0 < c.N) colsum8_block<T>(c.part, c.P, c.N, reinterpret_cast<T*>(c.out), n0, red);  // block-uniform
+    if (n0 < c.N) colsum_block<T>(c.part, c.P, c.N, reinterpret_cast<T*>(c.out), n0, red);  // block-uniform
 }
 
 // ------------------------------------------------------------------ SIMT path
@@ -1521,7 +1521,7 @@ hipError_t gemm_launch_group(const GemmDesc& a, const GemmDesc& b, hipStream_t s
         const ColsumJob& c = colsums[i];
         if (!c.part || !c.out || c.P <= 0 || c.N <= 0) return hipErrorInvalidValue;
         cs.j[i] = c;
-        cs.blocks = std::max(cs.blocks, (c.N + 7) / 8);
+        cs.blocks = std::max(cs.blocks, (c.N + kColsumCols - 1) / kColsumCols);
     }
     switch (a.dtype) {
         case 1: return launch_dl4_group<f16>(a, b, st, cs, ev);

@@ -289,13 +289,13 @@ __global__ __launch_bounds__(256) void ln_bwd_kernel(LnBwdArgs a) {
     }
 }
 
-// out_v[n] = sum_p part_v[p][n] for up to two vectors v (blockIdx.y), 8
-// columns per workgroup, in the fixed order of colsum8_block.
+// out_v[n] = sum_p part_v[p][n] for up to two vectors v (blockIdx.y),
+// kColsumCols columns per workgroup, in the fixed order of colsum_block.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_finalize_kernel(const float* part0, const float* part1, int P, int N,
                                                               T* out0, T* out1) {
-    __shared__ float red[32][9];
-    colsum8_block<T>(blockIdx.y ? part1 : part0, P, N, blockIdx.y ? out1 : out0, blockIdx.x * 8, red);
+    __shared__ float red[256 / kColsumCols][kColsumCols + 1];
+    colsum_block<T>(blockIdx.y ? part1 : part0, P, N, blockIdx.y ? out1 : out0, blockIdx.x * kColsumCols, red);
 }
 
 constexpr int CS_ROWS = 64;  // rows per partial in colsum_partial
@@ -461,7 +461,7 @@ hipError_t colsum_finalize(int dtype, const float* part, int P, int N, void* out
 
 hipError_t colsum_finalize2(int dtype, const float* part0, const float* part1, int P, int N, void* out0, void* out1,
                             hipStream_t st) {
-    dim3 grid((N + 7) / 8, part1 ? 2 : 1);
+    dim3 grid((N + kColsumCols - 1) / kColsumCols, part1 ? 2 : 1);
     switch (dtype) {
         case 0: hipLaunchKernelGGL(colsum_finalize_kernel<float>, grid, dim3(256), 0, st, part0, part1, P, N, (float*)out0, (float*)out1); break;
         case 1: hipLaunchKernelGGL(colsum_finalize_kernel<f16>, grid, dim3(256), 0, st, part0, part1, P, N, (f16*)out0, (f16*)out1); break;

@@ -166,32 +166,37 @@ struct Drop {
 };
 
 // ---------------------------------------------------------------- column sums
-// out[n] = sum_p part[p][n] (fp32 [P][N] partial rows) for the 8 columns
-// n0 .. n0+7, by one 256-thread block: thread (phase j = tid / 8, column
-// tid % 8) adds rows j, j+32, ... in order, then the 32 phase sums are added
-// in order -- a fixed summation order, independent of scheduling, with only
-// P/128 dependent load rounds.  red: 32 x 9 floats of LDS; every thread of
-// the block must call it.
+// out[n] = sum_p part[p][n] (fp32 [P][N] partial rows) for the 32 columns
+// n0 .. n0+31, by one 256-thread block: thread (phase j = tid / 32, column
+// tid % 32) adds rows j, j+8, ... in order, then the 8 phase sums are added
+// in order -- a fixed summation order, independent of scheduling.  A wave's
+// load covers two rows of 32 consecutive columns (whole 128-byte lines) and
+// each thread keeps 8 loads in flight.  red: 8 x 33 floats of LDS; every
+// thread of the block must call it.
+constexpr int kColsumCols = 32;
 template <typename T>
-__device__ __forceinline__ void colsum8_block(const float* part, int P, int N, T* out, int n0, float (*red)[9]) {
-    const int cl = threadIdx.x & 7, ph = threadIdx.x >> 3;
+__device__ __forceinline__ void colsum_block(const float* part, int P, int N, T* out, int n0,
+                                             float (*red)[kColsumCols + 1]) {
+    const int cl = threadIdx.x & (kColsumCols - 1), ph = threadIdx.x / kColsumCols;
     const int n = n0 + cl;
     float s = 0.0f;
     if (n < N) {
         int p = ph;
-        for (; p + 96 < P; p += 128) {
-            const float a0 = part[(size_t)p * N + n], a1 = part[(size_t)(p + 32) * N + n];
-            const float a2 = part[(size_t)(p + 64) * N + n], a3 = part[(size_t)(p + 96) * N + n];
-            s += a0; s += a1; s += a2; s += a3;
+        for (; p + 56 < P; p += 64) {
+            float a[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] = part[(size_t)(p + 8 * i) * N + n];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) s += a[i];
         }
-        for (; p < P; p += 32) s += part[(size_t)p * N + n];
+        for (; p < P; p += 8) s += part[(size_t)p * N + n];
     }
     red[ph][cl] = s;
     __syncthreads();
     if (ph == 0 && n < N) {
         float t = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 32; ++j) t += red[j][cl];
+        for (int j = 0; j < 256 / kColsumCols; ++j) t += red[j][cl];
         out[n] = from_f<T>(t);
     }
 }
