@@ -195,8 +195,8 @@ tel_status tel_layer_backward(tel_layer* layer, const tel_params* params, const 
  * for a Post-LN layer (site 2 there follows its own LayerNorm backward and is
  * fused already), below without dx_dropped or vice versa, or a below that is
  * not a Pre-LN layer of the same batch, sequence, hidden size, dtype and
- * hidden dropout; TEL_ERR_UNSUPPORTED under token packing.  dx_dropped may
- * not alias dy, dy_dropped or dx. */
+ * hidden dropout, or a dx_dropped equal to dy, dy_dropped or dx;
+ * TEL_ERR_UNSUPPORTED under token packing. */
 tel_status tel_layer_backward_chain(tel_layer* layer, const tel_params* params, const void* x,
                                     const int32_t* key_lengths, int training, uint64_t step, const void* dy,
                                     const void* dy_dropped, const void* saved, void* scratch, void* dx,

@@ -306,7 +306,9 @@ def test_backward_chain_validation_before_gpu():
                      (h, None, None, 8192),    # dx_dropped without below
                      (h, None, hp, 8192),      # below is Post-LN
                      (h, None, hw, 8192),      # below of another hidden size
-                     (h, 8196, None, None)):   # misaligned dy_dropped
+                     (h, 8196, None, None),    # misaligned dy_dropped
+                     (h, None, h, 4096),       # dx_dropped aliases dx (and dy)
+                     (h, 12288, h, 12288)):    # dx_dropped aliases dy_dropped
             with pytest.raises(B.TelError) as e:
                 chain(*args)
             assert e.value.status == B.TEL_ERR_INVALID_ARG, args

@@ -575,6 +575,8 @@ static tel_status backward_impl(tel_layer* L, const tel_params* P, const void* x
             return fail(TEL_ERR_INVALID_ARG, "chained backward is for Pre-LN layers (Post-LN applies site 2 "
                                              "after its own LayerNorm backward)");
         if (!below != !dx_dropped) return fail(TEL_ERR_INVALID_ARG, "below and dx_dropped go together");
+        if (dx_dropped && (dx_dropped == dx || dx_dropped == dy || dx_dropped == dy_dropped))
+            return fail(TEL_ERR_INVALID_ARG, "dx_dropped may not alias dy, dy_dropped or dx");
         if ((dy_dropped && !aligned(dy_dropped)) || (dx_dropped && !aligned(dx_dropped)))
             return fail(TEL_ERR_INVALID_ARG, "buffers must be 16-byte aligned");
         if (below) {
